@@ -1,0 +1,29 @@
+"""CPU oracle for the layer-streamed QLoRA step -- TEST INFRASTRUCTURE ONLY.
+
+A plain, slow, obviously correct NumPy implementation of what the streamed
+step computes.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` may import it; the product path never
+does.  It shares no code with the HIP library and imports nothing from the
+package.
+
+Streaming is a reordering of when weights reach the device and changes no
+value (page "Soup ... radar note", section "In detail": the streamed result is
+"just a reordering" with zero difference against the resident run), so the
+oracle is simply the un-streamed computation: dequantise, run the decoder,
+back-propagate to the LoRA matrices.
+
+Pins (what the oracle is checked against, in ``tests/test_oracle_*.py``):
+  nf4.codebook      -- normal-CDF spacing of the levels (scipy ndtr), exact
+                       +-1 ends and exact zero; values parity unpinned against
+                       the pages, which print no table.
+  nf4.quantize      -- exact-rational optimality of every chosen code, absmax
+                       element maps to an end code, idempotence, zero blocks.
+  nf4.dequant       -- exact product in float64 + independent integer rounding.
+  model.*           -- fp64 finite differences of the loss (LoRA A/B and the
+                       embedded input), torch autograd on fp64, library
+                       attention / cross-entropy, B = 0 identities, the
+                       adapters-disabled reference pass, the DPO ln 2 closed
+                       form.
+  model loss value  -- parity unpinned beyond the above: the pages print no
+                       worked loss or gradient.
+"""
