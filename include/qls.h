@@ -1,0 +1,286 @@
+/*
+ * qls.h -- C ABI of the layer-streamed QLoRA step for AMD Instinct MI355X (gfx950).
+ *
+ * One LoRA fine-tuning step in which the frozen NF4-quantised decoder stack
+ * lives in pinned host memory and streams into a two-slot device pool one
+ * layer at a time, prefetched one layer ahead.  Each resident layer runs the
+ * forward pass; the backward sweep reloads the layers, recomputes each
+ * forward from its checkpointed input and back-propagates to the LoRA A/B
+ * matrices only.
+ *
+ * Sources (web pages on the "layer streaming" feature of the Soup fine-tuning
+ * tool; cited by title and section):
+ *   [P1] "Can You Fine-Tune Llama 3.1 8B on a 4GB GPU? Soup's Layer Streaming
+ *        Explained": "How Soup's layer streaming actually works" (frozen base
+ *        off the GPU, page-locked host memory, reusable device buffers,
+ *        prefetch of the next layer, layers read again for the recomputed
+ *        backward); "Why NF4 matters so much" (NF4 host store, asynchronous
+ *        copies need page-locked memory); "Did a correctness bug invalidate the
+ *        Llama 3.1 8B result?" (size-dependent silent wrong gradients).
+ *   [P2] "Fine tune an 8B model on a 4GB laptop GPU (Soup setup)": "The
+ *        number, and exactly what it means" (embeddings and LM head stay
+ *        resident; streamed run bit-exact against the resident run); "Step 2,
+ *        train" (32 layers, two device buffers, base store pinned in RAM).
+ *   [P4] "Soup ... fine-tune 8B on a 4 GB laptop GPU" radar note: "In detail"
+ *        (DPO reference = the same base stream with the adapters disabled).
+ *   [P5] "How Layer Streaming Enables Fine-Tuning an 8B Model on a 4 GB GPU":
+ *        "Runtime Execution Flow" (per-layer load / release, runtime stats).
+ *
+ * Conventions
+ *   - Every function returns QLS_OK (0) or a negative QLS_E* code; the
+ *     thread-local text of the last failure is returned by qls_last_error().
+ *   - "d_" pointers are device pointers (HIP), "h_" pointers host pointers.
+ *     Device buffers are borrowed: the caller (normally PyTorch) owns them and
+ *     must keep them alive while work that uses them is in flight.
+ *   - Streams are hipStream_t passed as void*.  Entry points taking a session
+ *     enqueue asynchronously on the session's compute stream and return before
+ *     the GPU finishes, unless a host output (h_*) is requested.
+ *   - bf16 tensors are passed as uint16_t (raw bfloat16 bits), row-major.
+ *   - A session is used by one host thread at a time.
+ */
+#ifndef QLS_H
+#define QLS_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define QLS_ABI_VERSION 1
+
+enum {
+  QLS_OK = 0,
+  QLS_EINVAL = -1,       /* bad argument or shape */
+  QLS_ENOMEM = -2,       /* host allocation failed or workspace too small */
+  QLS_ENOPIN = -3,       /* pinned host allocation failed or exceeds the cap */
+  QLS_EHIP = -4,         /* a HIP runtime call failed (message has hipGetErrorString) */
+  QLS_ESTATE = -5,       /* object not ready (e.g. a store layer never set) */
+  QLS_EUNSUPPORTED = -6  /* shape outside what the kernels support */
+};
+
+enum { QLS_STREAMED = 0, QLS_RESIDENT = 1 };
+
+/* Module order used everywhere (records, LoRA packing): */
+enum { QLS_Q = 0, QLS_K, QLS_V, QLS_O, QLS_GATE, QLS_UP, QLS_DOWN, QLS_NMOD };
+
+/* Llama-style decoder shape plus LoRA hyper-parameters.
+ * Linears as (out x in): q (H*hd x d), k and v (KV*hd x d), o (d x H*hd),
+ * gate and up (I x d), down (d x I).  LoRA scale s = alpha / r.
+ * Supported: head_dim in {64, 128}; n_heads % n_kv_heads == 0; hidden,
+ * intermediate and every linear's in/out multiples of 16; lora_r a multiple
+ * of 8 in [8, 128]. */
+typedef struct qls_model_cfg {
+  int32_t n_layers, hidden, n_heads, n_kv_heads, head_dim, intermediate, vocab;
+  float rms_eps, rope_theta;
+  int32_t lora_r;
+  float lora_alpha;
+} qls_model_cfg;
+
+/* Per-session run configuration.
+ *   mode        QLS_STREAMED: two device slots, layers copied host->device
+ *               on a copy stream one layer ahead; QLS_RESIDENT: the whole
+ *               store is copied to the device once at session creation.
+ *   max_tokens  upper bound on B*S of any call (DPO uses 2*S).
+ *   max_seq     upper bound on S.
+ *   ce_chunk    vocabulary columns per cross-entropy chunk (0 = 32768;
+ *               rounded up to a multiple of 128).
+ *   timing      non-zero: record hipEvents around every copy and layer so
+ *               qls_session_stats can report copy / compute / overlap time. */
+typedef struct qls_run_cfg {
+  int32_t mode;
+  int32_t max_tokens;
+  int32_t max_seq;
+  int32_t ce_chunk;
+  int32_t timing;
+} qls_run_cfg;
+
+/* Resident (never streamed) tensors, bf16, device pointers, borrowed:
+ * embedding [vocab x hidden], LM head [vocab x hidden], final norm [hidden]. */
+typedef struct qls_resident {
+  const uint16_t* d_embed;
+  const uint16_t* d_lm_head;
+  const uint16_t* d_final_norm;
+} qls_resident;
+
+/* Read-only view of one layer record in the pinned host store.
+ * codes[m]: NF4 codes of module m, numel/2 bytes, element 2k in the high
+ * nibble of byte k; absmax[m]: numel/64 float32; norms: bf16 [hidden]. */
+typedef struct qls_layer_view {
+  const uint8_t* codes[QLS_NMOD];
+  const float* absmax[QLS_NMOD];
+  const uint16_t* norm_attn;
+  const uint16_t* norm_mlp;
+  const void* record;
+  int64_t record_bytes;
+} qls_layer_view;
+
+typedef struct qls_stats {
+  int64_t steps;          /* step-like calls since the last reset */
+  int64_t layer_loads;    /* host->device layer copies issued */
+  int64_t h2d_bytes;      /* bytes of those copies */
+  double copy_ms;         /* sum of copy durations (timing on) */
+  double compute_ms;      /* sum of per-layer compute spans (timing on) */
+  double overlap_ms;      /* copy time overlapped by layer compute (timing on) */
+  double step_ms;         /* wall time of the last step on the GPU (timing on) */
+  int64_t ws_bytes;       /* workspace bytes the session uses */
+} qls_stats;
+
+typedef struct qls_store qls_store;
+typedef struct qls_session qls_session;
+
+/* ---------------------------------------------------------------- basics */
+int qls_abi_version(void);
+/* Message for the last non-zero return on this thread; valid until the next
+ * qls_* call on the same thread. */
+const char* qls_last_error(void);
+
+/* ---------------------------------------------------------------- NF4
+ * [P1] "Why NF4 matters so much": the frozen store is NF4, about a quarter of
+ * bf16.  Levels: QLoRA's NormalFloat construction (7 negative quantiles of
+ * N(0,1), 8 positive, an exact 0, scaled so the ends are -1 and +1), float32,
+ * ascending.  Blocks of 64 consecutive elements of the row-major flattened
+ * tensor share one float32 absmax. */
+int qls_nf4_codebook(float out[16]);
+
+/* Host quantiser.  w: n float32 (n % 64 == 0).  codes: n/2 bytes (element 2k
+ * high nibble); absmax: n/64 float32.  code = argmin_j |w/a - cb[j]| taken in
+ * float32, ties to the lower index; an all-zero block gets code 7 and absmax
+ * 0.  n_threads <= 0 uses all hardware threads.  Errors: QLS_EINVAL. */
+int qls_nf4_quantize(const float* h_w, int64_t n, uint8_t* h_codes, float* h_absmax,
+                     int n_threads);
+
+/* Device dequantiser: d_out[i] = bf16_rne(float32(cb[code_i] * absmax[i/64])).
+ * Bit-exact reference of the in-GEMM dequantisation.  Asynchronous on stream. */
+int qls_nf4_dequant_dev(const uint8_t* d_codes, const float* d_absmax, int64_t n,
+                        uint16_t* d_out, void* stream);
+
+/* ---------------------------------------------------------------- one QLoRA linear
+ * y = bf16( x W^T + s * u B^T ),  u = bf16( x A^T ),  s = alpha / r,
+ * with W the dequantised NF4 weight [N x K].  x bf16 [T x K]; A bf16 [r x K];
+ * B bf16 [N x r]; outputs y bf16 [T x N] and u bf16 [T x r].  d_A/d_B NULL
+ * runs the base product only (u untouched).  K, N multiples of 16; r multiple
+ * of 8.  d_ws: scratch of qls_linear_ws_bytes(T, N, K, r) bytes. */
+int64_t qls_linear_ws_bytes(int T, int N, int K, int r);
+int qls_linear_fwd(const uint8_t* d_codes, const float* d_absmax, int N, int K,
+                   const uint16_t* d_x, int T, const uint16_t* d_A, const uint16_t* d_B,
+                   int r, float alpha, uint16_t* d_y, uint16_t* d_u, void* d_ws,
+                   void* stream);
+/* Backward of the same linear for upstream dY bf16 [T x N]:
+ *   du = bf16(s dY B);  dA = du^T x  [r x K] fp32;  dB = s dY^T u [N x r] fp32;
+ *   dX = dY W + du A    [T x K] fp32. */
+int qls_linear_bwd(const uint8_t* d_codes, const float* d_absmax, int N, int K,
+                   const uint16_t* d_x, const uint16_t* d_u, const uint16_t* d_dy, int T,
+                   const uint16_t* d_A, const uint16_t* d_B, int r, float alpha,
+                   float* d_dx, float* d_dA, float* d_dB, void* d_ws, void* stream);
+
+/* ---------------------------------------------------------------- sizes */
+/* Bytes of one layer record: 7 code blobs, 7 absmax arrays, 2 bf16 norms,
+ * each 256-byte aligned. */
+int64_t qls_layer_record_bytes(const qls_model_cfg* cfg);
+/* Length of the packed LoRA vector: layer-major, modules q,k,v,o,gate,up,down,
+ * each A [r x in] row-major then B [out x r] row-major. */
+int64_t qls_lora_numel(const qls_model_cfg* cfg);
+
+/* ---------------------------------------------------------------- host store
+ * [P1] "How Soup's layer streaming actually works", item 2 and [P2] "Step 2,
+ * train": the frozen decoder stack lives in page-locked host memory, one
+ * record per layer.  Records are allocated with hipHostMalloc; if pinning
+ * fails, or n_layers * record bytes exceeds max_pinned_bytes (0 = no cap),
+ * creation fails with QLS_ENOPIN.  The store owns its host memory and must
+ * outlive every session created over it. */
+int qls_store_create(const qls_model_cfg* cfg, uint64_t max_pinned_bytes, qls_store** out);
+/* Quantise and pack one layer.  w[m]: float32 [out x in] of module m; norms
+ * bf16 [hidden].  Inputs are borrowed for the call.  n_threads as for
+ * qls_nf4_quantize.  Errors: QLS_EINVAL (layer out of range / NULL). */
+int qls_store_set_layer_fp32(qls_store* st, int layer, const float* const h_w[QLS_NMOD],
+                             const uint16_t* h_norm_attn, const uint16_t* h_norm_mlp,
+                             int n_threads);
+/* Pack a layer that is already quantised (codes / absmax as in qls_nf4_quantize). */
+int qls_store_set_layer_nf4(qls_store* st, int layer, const uint8_t* const h_codes[QLS_NMOD],
+                            const float* const h_absmax[QLS_NMOD],
+                            const uint16_t* h_norm_attn, const uint16_t* h_norm_mlp);
+int qls_store_layer_view(const qls_store* st, int layer, qls_layer_view* out);
+void qls_store_destroy(qls_store* st);   /* NULL-safe */
+
+/* ---------------------------------------------------------------- session
+ * Device bytes a session needs: the two slots (or the whole store when
+ * RESIDENT), layer-input checkpoints, one layer's activations and gradients,
+ * the bf16 LoRA working copy, the cross-entropy chunk and split-K scratch. */
+int qls_workspace_bytes(const qls_store* st, const qls_run_cfg* run, int64_t* out);
+
+/* Bind a store, a device workspace, two streams (compute and copy, both at
+ * default priority) and the resident tensors.  Everything is borrowed and must
+ * outlive the session; the session owns only its hipEvents.  RESIDENT mode
+ * copies the whole store to the workspace before returning.  Errors:
+ * QLS_ENOMEM (ws_bytes too small, checked before any launch), QLS_ESTATE (a
+ * store layer never set), QLS_EINVAL, QLS_EHIP. */
+int qls_session_create(const qls_store* st, const qls_run_cfg* run, void* d_ws, int64_t ws_bytes,
+                       void* compute_stream, void* copy_stream, const qls_resident* res,
+                       qls_session** out);
+void qls_session_destroy(qls_session* s);  /* NULL-safe; synchronises its streams */
+
+/* One streamed SFT step (page [P1] "How Soup's layer streaming actually
+ * works"): forward sweep over the layers as they stream in, final RMSNorm and
+ * vocabulary-chunked next-token cross-entropy against the resident LM head
+ * (mean over B*(S-1) targets), then the backward sweep in reverse layer order
+ * that recomputes each layer from its checkpoint.  d_ids int32 [B x S] in
+ * [0, vocab); d_lora float32 packed (qls_lora_numel); d_grads float32, same
+ * packing, overwritten with dL/dA, dL/dB; d_loss float32 [1].  h_loss non-NULL
+ * blocks until the step is done and copies the loss there. */
+int qls_sft_step(qls_session* s, const int32_t* d_ids, int B, int S, const float* d_lora,
+                 float* d_grads, float* d_loss, float* h_loss);
+
+/* Forward-only sweep returning per-sequence sums of next-token log-probs over
+ * positions [prompt_len, S): d_seq_logp float32 [B]; d_tok_logp (optional)
+ * float32 [B x S] with entry t = log p(ids_{t+1} | ids_{<=t}) (0 at t = S-1).
+ * d_lora == NULL disables the adapters: the DPO reference pass of [P4]. */
+int qls_logprobs(qls_session* s, const int32_t* d_ids, int B, int S, int prompt_len,
+                 const float* d_lora, float* d_seq_logp, float* d_tok_logp);
+
+/* One DPO step on a (chosen, rejected) pair of length S sharing a prompt of
+ * prompt_len tokens.  The reference (adapters disabled, [P4]) is computed on
+ * each resident layer inside the same forward sweep as the policy, so the
+ * step streams the stack exactly as an SFT step does.  Loss = softplus(-z),
+ * z = beta((pi_c - ref_c) - (pi_r - ref_r)), log-probs summed over the
+ * response positions.  d_aux (optional) float32 [4] = pi_c, pi_r, ref_c, ref_r. */
+int qls_dpo_step(qls_session* s, const int32_t* d_chosen, const int32_t* d_rejected, int S,
+                 int prompt_len, float beta, const float* d_lora, float* d_grads,
+                 float* d_loss, float* h_loss, float* d_aux);
+
+/* One streamed decoder layer on its own: forward, recomputed forward and
+ * backward of layer `layer` for input d_x bf16 [B*S x hidden] and upstream
+ * gradient d_gout bf16 [B*S x hidden].  Writes d_out bf16 [B*S x hidden]
+ * (layer output), d_gin float32 [B*S x hidden] (dL/dx) and that layer's
+ * slice of d_grads (packed LoRA layout, other layers untouched). */
+int qls_layer_fwd_bwd(qls_session* s, int layer, const uint16_t* d_x, const uint16_t* d_gout,
+                      int B, int S, const float* d_lora, uint16_t* d_out, float* d_gin,
+                      float* d_grads);
+
+/* Device pointer to the layer-input checkpoints of the last step: bf16
+ * [(n_layers + 1) x tokens x hidden] (entry n_layers = final hidden state). */
+int qls_session_checkpoints(qls_session* s, const uint16_t** d_ptr, int64_t* tokens);
+
+int qls_session_stats(qls_session* s, qls_stats* out);   /* synchronises the session */
+int qls_session_reset_stats(qls_session* s);
+
+/* Test hooks; they add operations and never switch kernels.
+ *   QLS_DBG_POISON_ON_RELEASE  fill a slot with 0xFF bytes (NaN bf16/fp32) on
+ *                              the copy stream right after it is released
+ *   QLS_DBG_COPY_DELAY         a host callback sleeping delay_us on the copy
+ *                              stream before each layer copy
+ *   QLS_DBG_COMPUTE_DELAY      a bounded spin kernel of about delay_us on the
+ *                              compute stream before each slot release
+ *   QLS_DBG_NO_REUSE           reload every layer even when a slot still holds it */
+enum {
+  QLS_DBG_POISON_ON_RELEASE = 1u,
+  QLS_DBG_COPY_DELAY = 2u,
+  QLS_DBG_COMPUTE_DELAY = 4u,
+  QLS_DBG_NO_REUSE = 8u
+};
+int qls_debug_set(qls_session* s, uint32_t flags, int delay_us);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* QLS_H */

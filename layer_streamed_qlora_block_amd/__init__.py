@@ -1,0 +1,274 @@
+"""Layer-streamed QLoRA step for AMD Instinct MI355X (gfx950) -- Python binding.
+
+A thin ctypes layer over ``libqls.so`` (the C ABI declared in ``include/qls.h``):
+every function here marshals arguments and calls the library of the same
+name; all computation runs in the HIP kernels.  PyTorch only supplies device
+memory and streams.  Importing fails loudly when the library is not built.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libqls.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"{LIB_PATH} is missing: build it with __graft_entry__.build() "
+                      "(hipcc --offload-arch=gfx950); there is no fallback path")
+_lib = C.CDLL(LIB_PATH)
+
+QLS_OK, QLS_EINVAL, QLS_ENOMEM, QLS_ENOPIN, QLS_EHIP, QLS_ESTATE, QLS_EUNSUPPORTED = 0, -1, -2, -3, -4, -5, -6
+QLS_STREAMED, QLS_RESIDENT = 0, 1
+NMOD = 7
+MODULES = ("q", "k", "v", "o", "gate", "up", "down")
+DBG_POISON_ON_RELEASE, DBG_COPY_DELAY, DBG_COMPUTE_DELAY, DBG_NO_REUSE = 1, 2, 4, 8
+
+
+class QlsError(RuntimeError):
+    def __init__(self, code, msg):
+        super().__init__(f"qls error {code}: {msg}")
+        self.code = code
+
+
+class ModelCfg(C.Structure):
+    _fields_ = [("n_layers", C.c_int32), ("hidden", C.c_int32), ("n_heads", C.c_int32),
+                ("n_kv_heads", C.c_int32), ("head_dim", C.c_int32), ("intermediate", C.c_int32),
+                ("vocab", C.c_int32), ("rms_eps", C.c_float), ("rope_theta", C.c_float),
+                ("lora_r", C.c_int32), ("lora_alpha", C.c_float)]
+
+
+class RunCfg(C.Structure):
+    _fields_ = [("mode", C.c_int32), ("max_tokens", C.c_int32), ("max_seq", C.c_int32),
+                ("ce_chunk", C.c_int32), ("timing", C.c_int32)]
+
+
+class Resident(C.Structure):
+    _fields_ = [("d_embed", C.c_void_p), ("d_lm_head", C.c_void_p), ("d_final_norm", C.c_void_p)]
+
+
+class LayerView(C.Structure):
+    _fields_ = [("codes", C.c_void_p * NMOD), ("absmax", C.c_void_p * NMOD), ("norm_attn", C.c_void_p),
+                ("norm_mlp", C.c_void_p), ("record", C.c_void_p), ("record_bytes", C.c_int64)]
+
+
+class Stats(C.Structure):
+    _fields_ = [("steps", C.c_int64), ("layer_loads", C.c_int64), ("h2d_bytes", C.c_int64),
+                ("copy_ms", C.c_double), ("compute_ms", C.c_double), ("overlap_ms", C.c_double),
+                ("step_ms", C.c_double), ("ws_bytes", C.c_int64)]
+
+    def as_dict(self):
+        return {k: getattr(self, k) for k, _ in self._fields_}
+
+
+_P = C.c_void_p
+_I = C.c_int
+_I64 = C.c_int64
+_F = C.c_float
+_SIG = {
+    "qls_abi_version": (_I, []),
+    "qls_last_error": (C.c_char_p, []),
+    "qls_nf4_codebook": (_I, [_P]),
+    "qls_nf4_quantize": (_I, [_P, _I64, _P, _P, _I]),
+    "qls_nf4_dequant_dev": (_I, [_P, _P, _I64, _P, _P]),
+    "qls_linear_ws_bytes": (_I64, [_I, _I, _I, _I]),
+    "qls_linear_fwd": (_I, [_P, _P, _I, _I, _P, _I, _P, _P, _I, _F, _P, _P, _P, _P]),
+    "qls_linear_bwd": (_I, [_P, _P, _I, _I, _P, _P, _P, _I, _P, _P, _I, _F, _P, _P, _P, _P, _P]),
+    "qls_layer_record_bytes": (_I64, [C.POINTER(ModelCfg)]),
+    "qls_lora_numel": (_I64, [C.POINTER(ModelCfg)]),
+    "qls_store_create": (_I, [C.POINTER(ModelCfg), C.c_uint64, C.POINTER(_P)]),
+    "qls_store_set_layer_fp32": (_I, [_P, _I, _P * NMOD, _P, _P, _I]),
+    "qls_store_set_layer_nf4": (_I, [_P, _I, _P * NMOD, _P * NMOD, _P, _P]),
+    "qls_store_layer_view": (_I, [_P, _I, C.POINTER(LayerView)]),
+    "qls_store_destroy": (None, [_P]),
+    "qls_workspace_bytes": (_I, [_P, C.POINTER(RunCfg), C.POINTER(_I64)]),
+    "qls_session_create": (_I, [_P, C.POINTER(RunCfg), _P, _I64, _P, _P, C.POINTER(Resident), C.POINTER(_P)]),
+    "qls_session_destroy": (None, [_P]),
+    "qls_sft_step": (_I, [_P, _P, _I, _I, _P, _P, _P, _P]),
+    "qls_logprobs": (_I, [_P, _P, _I, _I, _I, _P, _P, _P]),
+    "qls_dpo_step": (_I, [_P, _P, _P, _I, _I, _F, _P, _P, _P, _P, _P]),
+    "qls_layer_fwd_bwd": (_I, [_P, _I, _P, _P, _I, _I, _P, _P, _P, _P]),
+    "qls_session_checkpoints": (_I, [_P, C.POINTER(_P), C.POINTER(_I64)]),
+    "qls_session_stats": (_I, [_P, C.POINTER(Stats)]),
+    "qls_session_reset_stats": (_I, [_P]),
+    "qls_debug_set": (_I, [_P, C.c_uint32, _I]),
+}
+for _name, (_res, _args) in _SIG.items():
+    _fn = getattr(_lib, _name)
+    _fn.restype = _res
+    _fn.argtypes = _args
+
+
+def exported_symbols():
+    return list(_SIG)
+
+
+def last_error() -> str:
+    return _lib.qls_last_error().decode()
+
+
+def _check(rc):
+    if rc is not None and rc < 0:
+        raise QlsError(rc, last_error())
+    return rc
+
+
+def _ptr(t):
+    """Device/host pointer of a tensor or ndarray (None -> NULL)."""
+    if t is None:
+        return None
+    if hasattr(t, "data_ptr"):
+        return t.data_ptr()
+    return t.ctypes.data
+
+
+def _stream(s):
+    if s is None:
+        return None
+    return getattr(s, "cuda_stream", s)
+
+
+def model_cfg(cfg) -> ModelCfg:
+    """From a synth.ModelCfg-like object (L, d, H, KV, hd, I, V, eps, theta, r, alpha)."""
+    return ModelCfg(cfg.L, cfg.d, cfg.H, cfg.KV, cfg.hd, cfg.I, cfg.V, cfg.eps, cfg.theta, cfg.r, cfg.alpha)
+
+
+# ---------------------------------------------------------------- thin wrappers
+def qls_abi_version() -> int:
+    return _lib.qls_abi_version()
+
+
+def qls_nf4_codebook():
+    import numpy as np
+    out = np.zeros(16, np.float32)
+    _check(_lib.qls_nf4_codebook(out.ctypes.data))
+    return out
+
+
+def qls_nf4_quantize(w, n_threads: int = 0):
+    import numpy as np
+    w = np.ascontiguousarray(w, dtype=np.float32).reshape(-1)
+    codes = np.empty(w.size // 2, np.uint8)
+    absmax = np.empty(w.size // 64, np.float32)
+    _check(_lib.qls_nf4_quantize(w.ctypes.data, w.size, codes.ctypes.data, absmax.ctypes.data, n_threads))
+    return codes, absmax
+
+
+def qls_nf4_dequant_dev(d_codes, d_absmax, n, d_out, stream=None):
+    _check(_lib.qls_nf4_dequant_dev(_ptr(d_codes), _ptr(d_absmax), n, _ptr(d_out), _stream(stream)))
+
+
+def qls_linear_ws_bytes(T, N, K, r) -> int:
+    return _check(_lib.qls_linear_ws_bytes(T, N, K, r))
+
+
+def qls_linear_fwd(codes, absmax, N, K, x, T, A, B, r, alpha, y, u, ws, stream=None):
+    _check(_lib.qls_linear_fwd(_ptr(codes), _ptr(absmax), N, K, _ptr(x), T, _ptr(A), _ptr(B), r, alpha,
+                               _ptr(y), _ptr(u), _ptr(ws), _stream(stream)))
+
+
+def qls_linear_bwd(codes, absmax, N, K, x, u, dy, T, A, B, r, alpha, dx, dA, dB, ws, stream=None):
+    _check(_lib.qls_linear_bwd(_ptr(codes), _ptr(absmax), N, K, _ptr(x), _ptr(u), _ptr(dy), T, _ptr(A),
+                               _ptr(B), r, alpha, _ptr(dx), _ptr(dA), _ptr(dB), _ptr(ws), _stream(stream)))
+
+
+def qls_layer_record_bytes(mc: ModelCfg) -> int:
+    return _check(_lib.qls_layer_record_bytes(C.byref(mc)))
+
+
+def qls_lora_numel(mc: ModelCfg) -> int:
+    return _check(_lib.qls_lora_numel(C.byref(mc)))
+
+
+def qls_store_create(mc: ModelCfg, max_pinned_bytes: int = 0):
+    h = _P()
+    _check(_lib.qls_store_create(C.byref(mc), max_pinned_bytes, C.byref(h)))
+    return h
+
+
+def qls_store_set_layer_fp32(store, layer, ws, norm_attn, norm_mlp, n_threads: int = 0):
+    arr = (_P * NMOD)(*[_ptr(w) for w in ws])
+    _check(_lib.qls_store_set_layer_fp32(store, layer, arr, _ptr(norm_attn), _ptr(norm_mlp), n_threads))
+
+
+def qls_store_set_layer_nf4(store, layer, codes, absmax, norm_attn, norm_mlp):
+    ca = (_P * NMOD)(*[_ptr(c) for c in codes])
+    aa = (_P * NMOD)(*[_ptr(a) for a in absmax])
+    _check(_lib.qls_store_set_layer_nf4(store, layer, ca, aa, _ptr(norm_attn), _ptr(norm_mlp)))
+
+
+def qls_store_layer_view(store, layer) -> LayerView:
+    v = LayerView()
+    _check(_lib.qls_store_layer_view(store, layer, C.byref(v)))
+    return v
+
+
+def qls_store_destroy(store):
+    _lib.qls_store_destroy(store)
+
+
+def qls_workspace_bytes(store, run: RunCfg) -> int:
+    out = _I64()
+    _check(_lib.qls_workspace_bytes(store, C.byref(run), C.byref(out)))
+    return out.value
+
+
+def qls_session_create(store, run: RunCfg, ws, ws_bytes, compute_stream, copy_stream, embed, lm_head,
+                       final_norm):
+    res = Resident(_ptr(embed), _ptr(lm_head), _ptr(final_norm))
+    h = _P()
+    _check(_lib.qls_session_create(store, C.byref(run), _ptr(ws), ws_bytes, _stream(compute_stream),
+                                   _stream(copy_stream), C.byref(res), C.byref(h)))
+    return h
+
+
+def qls_session_destroy(sess):
+    _lib.qls_session_destroy(sess)
+
+
+def qls_sft_step(sess, ids, B, S, lora, grads, loss, want_host_loss=False):
+    hl = C.c_float(0.0)
+    _check(_lib.qls_sft_step(sess, _ptr(ids), B, S, _ptr(lora), _ptr(grads), _ptr(loss),
+                             C.byref(hl) if want_host_loss else None))
+    return hl.value if want_host_loss else None
+
+
+def qls_logprobs(sess, ids, B, S, prompt_len, lora, seq_logp, tok_logp=None):
+    _check(_lib.qls_logprobs(sess, _ptr(ids), B, S, prompt_len, _ptr(lora), _ptr(seq_logp), _ptr(tok_logp)))
+
+
+def qls_dpo_step(sess, chosen, rejected, S, prompt_len, beta, lora, grads, loss, aux=None,
+                 want_host_loss=False):
+    hl = C.c_float(0.0)
+    _check(_lib.qls_dpo_step(sess, _ptr(chosen), _ptr(rejected), S, prompt_len, beta, _ptr(lora),
+                             _ptr(grads), _ptr(loss), C.byref(hl) if want_host_loss else None, _ptr(aux)))
+    return hl.value if want_host_loss else None
+
+
+def qls_layer_fwd_bwd(sess, layer, x, gout, B, S, lora, out, gin, grads):
+    _check(_lib.qls_layer_fwd_bwd(sess, layer, _ptr(x), _ptr(gout), B, S, _ptr(lora), _ptr(out), _ptr(gin),
+                                  _ptr(grads)))
+
+
+def qls_session_checkpoints(sess):
+    p = _P()
+    n = _I64()
+    _check(_lib.qls_session_checkpoints(sess, C.byref(p), C.byref(n)))
+    return p.value, n.value
+
+
+def qls_session_stats(sess) -> dict:
+    s = Stats()
+    _check(_lib.qls_session_stats(sess, C.byref(s)))
+    return s.as_dict()
+
+
+def qls_session_reset_stats(sess):
+    _check(_lib.qls_session_reset_stats(sess))
+
+
+def qls_debug_set(sess, flags, delay_us=0):
+    _check(_lib.qls_debug_set(sess, flags, delay_us))
+
+
+from .runtime import Session, Store  # noqa: E402  (torch-facing convenience objects)

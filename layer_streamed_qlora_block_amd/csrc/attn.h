@@ -1,0 +1,29 @@
+// Causal GQA attention launchers.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+// q, k, v live in one bf16 buffer qkv [B*S, ld] at column offsets q_off,
+// k_off, v_off (heads back to back, hd each).  Head h reads kv head
+// h / (H / KV).  out bf16 [B*S, ldo]; lse float [B, H, S] (natural log).
+struct AttnArgs {
+  const uint16_t* qkv; int64_t ld; int q_off, k_off, v_off;
+  int S, H, KV, hd;
+  float scale;                 // 1/sqrt(hd)
+  uint16_t* out; int64_t ldo;
+  float* lse;
+};
+int attn_fwd(const AttnArgs& a, int B, hipStream_t st);
+
+// Backward: dO and O bf16 [B*S, lddo] (o is the forward output); D float
+// [B, H, S] scratch; dq float [B*S, lddq]; dk, dv float [B*S, lddkv].
+struct AttnBwdArgs {
+  const uint16_t* qkv; int64_t ld; int q_off, k_off, v_off;
+  int S, H, KV, hd;
+  float scale;
+  const uint16_t* dO; const uint16_t* O; int64_t lddo;
+  const float* lse; float* D;
+  float* dq; int64_t lddq;
+  float* dk; float* dv; int64_t lddkv;
+};
+int attn_bwd(const AttnBwdArgs& a, int B, hipStream_t st);

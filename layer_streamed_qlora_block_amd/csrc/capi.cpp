@@ -1,0 +1,91 @@
+// C ABI: error plumbing, the NF4 dequant hook and the one-linear entry points.
+#include <algorithm>
+#include <string>
+
+#include "gemm.h"
+#include "internal.h"
+#include "ops.h"
+
+static thread_local std::string t_err;
+
+void set_error(const std::string& msg) { t_err = msg; }
+int fail(int code, const std::string& msg) {
+  t_err = msg;
+  return code;
+}
+int hip_fail(hipError_t e, const char* what) {
+  t_err = std::string(what) + ": " + hipGetErrorString(e);
+  return QLS_EHIP;
+}
+
+extern "C" {
+
+int qls_abi_version(void) { return QLS_ABI_VERSION; }
+const char* qls_last_error(void) { return t_err.c_str(); }
+
+int qls_nf4_dequant_dev(const uint8_t* d_codes, const float* d_absmax, int64_t n, uint16_t* d_out,
+                        void* stream) {
+  if (!d_codes || !d_absmax || !d_out) return fail(QLS_EINVAL, "NULL buffer");
+  if (n < 0 || n % 64) return fail(QLS_EINVAL, "n must be a non-negative multiple of 64");
+  if (nf4_dequant_launch(d_codes, d_absmax, n, d_out, (hipStream_t)stream))
+    return fail(QLS_EHIP, "codebook upload failed");
+  QLS_HIP(hipGetLastError());
+  return QLS_OK;
+}
+
+int64_t qls_linear_ws_bytes(int T, int N, int K, int r) {
+  if (T <= 0 || N <= 0 || K <= 0 || r <= 0) return fail(QLS_EINVAL, "sizes must be positive");
+  return linear_ws_bytes(T, N, K, r);
+}
+
+int qls_linear_fwd(const uint8_t* codes, const float* absmax, int N, int K, const uint16_t* x, int T,
+                   const uint16_t* A, const uint16_t* B, int r, float alpha, uint16_t* y,
+                   uint16_t* u, void* ws, void* stream) {
+  if (!codes || !absmax || !x || !y) return fail(QLS_EINVAL, "NULL buffer");
+  if (T <= 0 || N <= 0 || K <= 0) return fail(QLS_EINVAL, "sizes must be positive");
+  if (N % 16 || K % 16) return fail(QLS_EUNSUPPORTED, "N and K must be multiples of 16");
+  const bool lora = A && B;
+  if (lora && (r <= 0 || r % 8 || r > 128 || !u || !ws))
+    return fail(QLS_EINVAL, "LoRA needs r in [8,128] (multiple of 8), u and ws");
+  LinearFwd f{};
+  f.T = T; f.N = N; f.K = K; f.r = lora ? r : 0;
+  f.x = x; f.codes = codes; f.absmax = absmax;
+  f.A = lora ? A : nullptr; f.nmod = 1; f.mod_end[0] = N; f.Bm[0] = lora ? B : nullptr;
+  f.s = lora ? alpha / (float)r : 0.f;
+  f.y = y; f.ldy = N; f.u = lora ? u : nullptr;
+  f.ws = reinterpret_cast<float*>(ws);
+  int rc = linear_fwd(f, (hipStream_t)stream);
+  if (rc) return fail(QLS_EHIP, "kernel combination not built");
+  QLS_HIP(hipGetLastError());
+  return QLS_OK;
+}
+
+int qls_linear_bwd(const uint8_t* codes, const float* absmax, int N, int K, const uint16_t* x,
+                   const uint16_t* u, const uint16_t* dy, int T, const uint16_t* A,
+                   const uint16_t* B, int r, float alpha, float* dx, float* dA, float* dB, void* ws,
+                   void* stream) {
+  if (!codes || !absmax || !x || !u || !dy || !A || !B || !dx || !dA || !dB || !ws)
+    return fail(QLS_EINVAL, "NULL buffer");
+  if (T <= 0 || N <= 0 || K <= 0) return fail(QLS_EINVAL, "sizes must be positive");
+  if (N % 16 || K % 16) return fail(QLS_EUNSUPPORTED, "N and K must be multiples of 16");
+  if (r <= 0 || r % 8 || r > 128) return fail(QLS_EUNSUPPORTED, "r must be a multiple of 8 in [8,128]");
+  hipStream_t st = (hipStream_t)stream;
+  const float s = alpha / (float)r;
+  uint16_t* du = reinterpret_cast<uint16_t*>(ws);
+  float* part = reinterpret_cast<float*>(reinterpret_cast<char*>(ws) + align_up((int64_t)T * r * 2, 256));
+  int rc = 0;
+  rc |= skinny_du(dy, N, T, N, B, r, s, du, r, part, st);
+  rc |= skinny_dB(dy, N, T, N, u, r, s, dB, part, st);
+  rc |= skinny_dA(du, r, T, r, x, K, K, dA, part, st);
+  LinearDx d{};
+  d.T = T; d.Kc = N; d.Nout = K;
+  d.dy = dy; d.lddy = N; d.codes = codes; d.absmax = absmax; d.ldq = K;
+  d.du = du; d.lddu = r; d.Acat = A; d.rc = r;
+  d.out = dx; d.ldo = K; d.epi = EPI_F32;
+  rc |= linear_dx(d, st);
+  if (rc) return fail(QLS_EHIP, "kernel combination not built");
+  QLS_HIP(hipGetLastError());
+  return QLS_OK;
+}
+
+}  // extern "C"

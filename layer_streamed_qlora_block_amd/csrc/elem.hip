@@ -1,0 +1,352 @@
+// Memory-bound layer kernels: RMSNorm, RoPE, SwiGLU, embedding gather, casts,
+// cross-entropy reductions and the DPO head.  All are row- or element-parallel
+// with 16-byte accesses where the layout allows; reductions use a fixed order
+// so repeated runs give identical bits.
+#include "common.h"
+#include "ops.h"
+
+namespace {
+
+constexpr int TB = 256;
+
+QLS_DEV float block_sum(float v, float* red) {
+  v = warp_sum(v);
+  const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
+  __syncthreads();
+  if (l == 0) red[w] = v;
+  __syncthreads();
+  float s = 0.f;
+  for (int i = 0; i < (int)(blockDim.x >> 6); ++i) s += red[i];
+  return s;
+}
+
+// y = bf16(x * rho * w), rho = (mean(x^2) + eps)^-1/2, one block per row.
+__global__ void __launch_bounds__(TB) rmsnorm_fwd_k(const uint16_t* __restrict__ x,
+                                                    const uint16_t* __restrict__ w, float eps,
+                                                    uint16_t* __restrict__ y, int d) {
+  __shared__ float red[4];
+  const int64_t row = blockIdx.x;
+  const u32x4* xr = reinterpret_cast<const u32x4*>(x + row * d);
+  const int nc = d / 8;
+  float ss = 0.f;
+  for (int c = threadIdx.x; c < nc; c += TB) {
+    const u32x4 v = xr[c];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const float a = bflo(v[q]), b = bfhi(v[q]);
+      ss += a * a + b * b;
+    }
+  }
+  const float tot = block_sum(ss, red);
+  const float rho = 1.f / sqrtf(tot / (float)d + eps);
+  const u32x4* wr = reinterpret_cast<const u32x4*>(w);
+  u32x4* yr = reinterpret_cast<u32x4*>(y + row * d);
+  for (int c = threadIdx.x; c < nc; c += TB) {
+    const u32x4 v = xr[c], ww = wr[c];
+    u32x4 o;
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      o[q] = pack2_bf16(bflo(v[q]) * rho * bflo(ww[q]), bfhi(v[q]) * rho * bfhi(ww[q]));
+    yr[c] = o;
+  }
+}
+
+// out = gres + rho (dy*w - xhat * mean(dy*w*xhat)), xhat = rho x.
+__global__ void __launch_bounds__(TB) rmsnorm_bwd_k(const uint16_t* __restrict__ x,
+                                                    const uint16_t* __restrict__ w, float eps,
+                                                    const float* __restrict__ dy,
+                                                    const float* gres, float* out,
+                                                    uint16_t* __restrict__ out_bf16, int d) {
+  __shared__ float red[4];
+  const int64_t row = blockIdx.x;
+  const uint16_t* xr = x + row * d;
+  const float* dr = dy + row * d;
+  float ss = 0.f;
+  for (int i = threadIdx.x; i < d; i += TB) {
+    const float a = bf2f(xr[i]);
+    ss += a * a;
+  }
+  const float rho = 1.f / sqrtf(block_sum(ss, red) / (float)d + eps);
+  float dot = 0.f;
+  for (int i = threadIdx.x; i < d; i += TB) dot += dr[i] * bf2f(w[i]) * (bf2f(xr[i]) * rho);
+  const float mean = block_sum(dot, red) / (float)d;
+  for (int i = threadIdx.x; i < d; i += TB) {
+    const float xh = bf2f(xr[i]) * rho;
+    const float dyw = dr[i] * bf2f(w[i]);
+    const float v = (gres ? gres[row * d + i] : 0.f) + rho * (dyw - xh * mean);
+    out[row * d + i] = v;
+    if (out_bf16) out_bf16[row * d + i] = f2bf(v);
+  }
+}
+
+// cs: [S][hd/2][2] (cos, sin).  One thread per rotated pair.
+__global__ void rope_fwd_k(uint16_t* __restrict__ qkv, int64_t ld, int T, int S, int nh_q,
+                           int nh_k, int hd, const float* __restrict__ cs) {
+  const int h2 = hd / 2;
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t per_t = (int64_t)(nh_q + nh_k) * h2;
+  if (idx >= (int64_t)T * per_t) return;
+  const int t = (int)(idx / per_t);
+  const int rem = (int)(idx % per_t);
+  const int head = rem / h2, j = rem % h2;
+  const int pos = t % S;
+  const float c = cs[((int64_t)pos * h2 + j) * 2], s = cs[((int64_t)pos * h2 + j) * 2 + 1];
+  uint16_t* p = qkv + (int64_t)t * ld + (int64_t)head * hd;   // k heads follow q heads
+  const float x1 = bf2f(p[j]), x2 = bf2f(p[j + h2]);
+  p[j] = f2bf(x1 * c - x2 * s);
+  p[j + h2] = f2bf(x2 * c + x1 * s);
+}
+
+__global__ void rope_bwd_k(const float* __restrict__ dq, const float* __restrict__ dk,
+                           const float* __restrict__ dv, uint16_t* __restrict__ out, int64_t ld,
+                           int T, int S, int nh_q, int nh_k, int hd, const float* __restrict__ cs) {
+  const int h2 = hd / 2;
+  const int qd = nh_q * hd, kvd = nh_k * hd;
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t per_t = (int64_t)(nh_q + nh_k) * h2 + kvd / 2;
+  if (idx >= (int64_t)T * per_t) return;
+  const int t = (int)(idx / per_t);
+  const int rem = (int)(idx % per_t);
+  uint16_t* o = out + (int64_t)t * ld;
+  if (rem < (nh_q + nh_k) * h2) {
+    const int head = rem / h2, j = rem % h2;
+    const int pos = t % S;
+    const float c = cs[((int64_t)pos * h2 + j) * 2], s = cs[((int64_t)pos * h2 + j) * 2 + 1];
+    const float* src = head < nh_q ? dq + (int64_t)t * qd + (int64_t)head * hd
+                                   : dk + (int64_t)t * kvd + (int64_t)(head - nh_q) * hd;
+    const float x1 = src[j], x2 = src[j + h2];
+    o[(int64_t)head * hd + j] = f2bf(x1 * c + x2 * s);
+    o[(int64_t)head * hd + j + h2] = f2bf(x2 * c - x1 * s);
+  } else {
+    const int e = 2 * (rem - (nh_q + nh_k) * h2);
+    const float* src = dv + (int64_t)t * kvd;
+    o[qd + kvd + e] = f2bf(src[e]);
+    o[qd + kvd + e + 1] = f2bf(src[e + 1]);
+  }
+}
+
+// a = bf16(g sigmoid(g) u); gu rows hold g in [0, I) and u in [I, 2I).
+__global__ void swiglu_fwd_k(const uint16_t* __restrict__ gu, uint16_t* __restrict__ a, int T, int I) {
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int i8 = I / 8;
+  if (idx >= (int64_t)T * i8) return;
+  const int t = (int)(idx / i8), c = (int)(idx % i8);
+  const u32x4 g = reinterpret_cast<const u32x4*>(gu + (int64_t)t * 2 * I)[c];
+  const u32x4 u = reinterpret_cast<const u32x4*>(gu + (int64_t)t * 2 * I + I)[c];
+  u32x4 o;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const float g0 = bflo(g[q]), g1 = bfhi(g[q]);
+    const float s0 = 1.f / (1.f + __expf(-g0)), s1 = 1.f / (1.f + __expf(-g1));
+    o[q] = pack2_bf16(g0 * s0 * bflo(u[q]), g1 * s1 * bfhi(u[q]));
+  }
+  reinterpret_cast<u32x4*>(a + (int64_t)t * I)[c] = o;
+}
+
+// x[t] = E[ids[t]]; an out-of-range id yields a zero row and sets *bad.
+__global__ void embed_k(const int32_t* __restrict__ ids, const uint16_t* __restrict__ E,
+                        uint16_t* __restrict__ x, int d, int V, int* bad) {
+  const int t = blockIdx.x;
+  const int id = ids[t];
+  u32x4* dst = reinterpret_cast<u32x4*>(x + (int64_t)t * d);
+  if (id < 0 || id >= V) {
+    for (int c = threadIdx.x; c < d / 8; c += blockDim.x) dst[c] = u32x4{0, 0, 0, 0};
+    if (threadIdx.x == 0 && bad) atomicOr(bad, 1);
+    return;
+  }
+  const u32x4* src = reinterpret_cast<const u32x4*>(E + (int64_t)id * d);
+  for (int c = threadIdx.x; c < d / 8; c += blockDim.x) dst[c] = src[c];
+}
+
+__global__ void f32_to_bf16_k(const float* __restrict__ x, uint16_t* __restrict__ y, int64_t n) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) y[i] = f2bf(x[i]);
+}
+
+__global__ void bf16_to_f32_k(const uint16_t* __restrict__ x, float* __restrict__ y, int64_t n) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) y[i] = bf2f(x[i]);
+}
+
+__global__ void lora_cast_k(const float* __restrict__ src, int64_t ss, uint16_t* __restrict__ dst,
+                            int64_t ds, CastSeg seg) {
+  const int j = blockIdx.y, l = blockIdx.z;
+  const int64_t n = seg.n[j];
+  const float* s = src + (int64_t)l * ss + seg.so[j];
+  uint16_t* d = dst + (int64_t)l * ds + seg.dof[j];
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
+       i += (int64_t)gridDim.x * blockDim.x)
+    d[i] = f2bf(s[i]);
+}
+
+__global__ void ce_targets_k(const int32_t* __restrict__ ids, int B, int S, int32_t* __restrict__ tgt) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= B * S) return;
+  const int s = i % S;
+  tgt[i] = s < S - 1 ? ids[i + 1] : -1;
+}
+
+// Per row: lse = log sum over the vocabulary tiles of sum_i exp(m_i) s_i; logp = tgt_logit - lse.
+__global__ void ce_finalize_k(const float* __restrict__ stats, int ntiles,
+                              const float* __restrict__ tgt_logit, const int32_t* __restrict__ tgt,
+                              int T, float* __restrict__ lse, float* __restrict__ logp) {
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int l = threadIdx.x & 63;
+  if (row >= T) return;
+  const float* st = stats + (int64_t)row * ntiles * 2;
+  float m = -INFINITY;
+  for (int i = l; i < ntiles; i += 64) m = fmaxf(m, st[2 * i]);
+  m = warp_max(m);
+  float s = 0.f;
+  for (int i = l; i < ntiles; i += 64) s += st[2 * i + 1] * __expf(st[2 * i] - m);
+  s = warp_sum(s);
+  if (l == 0) {
+    const float v = m + logf(s);
+    lse[row] = v;
+    logp[row] = tgt[row] >= 0 ? tgt_logit[row] - v : 0.f;
+  }
+}
+
+// w_t = 1/N on rows with a target; loss = sum_t w_t (lse_t - tgt_logit_t), fixed-order sum.
+__global__ void __launch_bounds__(TB) sft_loss_k(const float* __restrict__ logp,
+                                                 const int32_t* __restrict__ tgt, int T, int N,
+                                                 float* __restrict__ w, float* __restrict__ loss) {
+  __shared__ float red[4];
+  const float inv = 1.f / (float)N;
+  float acc = 0.f;
+  for (int t = threadIdx.x; t < T; t += TB) {
+    const bool ok = tgt[t] >= 0;
+    w[t] = ok ? inv : 0.f;
+    acc += ok ? -logp[t] : 0.f;
+  }
+  const float s = block_sum(acc, red);
+  if (threadIdx.x == 0) *loss = s * inv;
+}
+
+__global__ void __launch_bounds__(TB) seq_logp_k(const float* __restrict__ logp, int S, int P,
+                                                 float* __restrict__ seq, float* __restrict__ tok) {
+  __shared__ float red[4];
+  const int b = blockIdx.x;
+  float acc = 0.f;
+  for (int t = threadIdx.x; t < S; t += TB) {
+    const float v = logp[(int64_t)b * S + t];
+    if (tok) tok[(int64_t)b * S + t] = v;
+    if (t >= P - 1 && t < S - 1) acc += v;
+  }
+  const float s = block_sum(acc, red);
+  if (threadIdx.x == 0) seq[b] = s;
+}
+
+// Sigmoid DPO on one pair (rows [0, S) chosen, [S, 2S) rejected).
+__global__ void __launch_bounds__(TB) dpo_k(const float* __restrict__ lp, const float* __restrict__ lr,
+                                            int S, int P, float beta, float* __restrict__ w,
+                                            float* __restrict__ loss, float* aux) {
+  __shared__ float red[4];
+  float v[4];
+  for (int q = 0; q < 4; ++q) {
+    const float* src = (q & 2) ? lr : lp;
+    const int b = q & 1;
+    float acc = 0.f;
+    for (int t = threadIdx.x; t < S; t += TB)
+      if (t >= P - 1 && t < S - 1) acc += src[(int64_t)b * S + t];
+    v[q] = block_sum(acc, red);
+  }
+  // v = pi_c, pi_r, ref_c, ref_r
+  const float z = beta * ((v[0] - v[2]) - (v[1] - v[3]));
+  const float sg = 1.f / (1.f + expf(z));                       // sigmoid(-z)
+  const float wc = beta * sg;                                   // -dL/dpi_c
+  for (int t = threadIdx.x; t < 2 * S; t += TB) {
+    const int s = t % S;
+    const bool resp = s >= P - 1 && s < S - 1;
+    w[t] = resp ? (t < S ? wc : -wc) : 0.f;
+  }
+  if (threadIdx.x == 0) {
+    *loss = z > 0 ? log1pf(expf(-z)) : -z + log1pf(expf(z));   // softplus(-z)
+    if (aux) { aux[0] = v[0]; aux[1] = v[1]; aux[2] = v[2]; aux[3] = v[3]; }
+  }
+}
+
+// Bounded spin of `ticks` wall-clock ticks (at most 2^24 polls).
+__global__ void spin_k(int64_t ticks) {
+  const int64_t t0 = wall_clock64();
+  for (int i = 0; i < (1 << 24); ++i) {
+    if (wall_clock64() - t0 >= ticks) break;
+    __builtin_amdgcn_s_sleep(2);
+  }
+}
+
+}  // namespace
+
+void rmsnorm_fwd(const uint16_t* x, const uint16_t* w, float eps, uint16_t* y, int T, int d,
+                 hipStream_t st) {
+  if (T <= 0) return;
+  hipLaunchKernelGGL(rmsnorm_fwd_k, dim3(T), dim3(TB), 0, st, x, w, eps, y, d);
+}
+void rmsnorm_bwd(const uint16_t* x, const uint16_t* w, float eps, const float* dy, const float* gres,
+                 float* out, uint16_t* out_bf16, int T, int d, hipStream_t st) {
+  if (T <= 0) return;
+  hipLaunchKernelGGL(rmsnorm_bwd_k, dim3(T), dim3(TB), 0, st, x, w, eps, dy, gres, out, out_bf16, d);
+}
+void rope_fwd(uint16_t* qkv, int64_t ld, int T, int S, int H, int KV, int hd, const float* cs,
+              hipStream_t st) {
+  const int64_t n = (int64_t)T * (H + KV) * (hd / 2);
+  if (n <= 0) return;
+  hipLaunchKernelGGL(rope_fwd_k, dim3((unsigned)ceil_div64(n, 256)), dim3(256), 0, st, qkv, ld, T, S,
+                     H, KV, hd, cs);
+}
+void rope_bwd(const float* dq, const float* dk, const float* dv, uint16_t* dqkv, int64_t ld, int T,
+              int S, int H, int KV, int hd, const float* cs, hipStream_t st) {
+  const int64_t n = (int64_t)T * ((H + KV) * (hd / 2) + KV * hd / 2);
+  if (n <= 0) return;
+  hipLaunchKernelGGL(rope_bwd_k, dim3((unsigned)ceil_div64(n, 256)), dim3(256), 0, st, dq, dk, dv,
+                     dqkv, ld, T, S, H, KV, hd, cs);
+}
+void swiglu_fwd(const uint16_t* gu, uint16_t* a, int T, int I, hipStream_t st) {
+  const int64_t n = (int64_t)T * (I / 8);
+  if (n <= 0) return;
+  hipLaunchKernelGGL(swiglu_fwd_k, dim3((unsigned)ceil_div64(n, 256)), dim3(256), 0, st, gu, a, T, I);
+}
+void embed_gather(const int32_t* ids, const uint16_t* E, uint16_t* x, int T, int d, int V, int* bad,
+                  hipStream_t st) {
+  if (T <= 0) return;
+  hipLaunchKernelGGL(embed_k, dim3(T), dim3(256), 0, st, ids, E, x, d, V, bad);
+}
+void f32_to_bf16(const float* x, uint16_t* y, int64_t n, hipStream_t st) {
+  if (n <= 0) return;
+  hipLaunchKernelGGL(f32_to_bf16_k, dim3((unsigned)ceil_div64(n, 256)), dim3(256), 0, st, x, y, n);
+}
+void bf16_to_f32(const uint16_t* x, float* y, int64_t n, hipStream_t st) {
+  if (n <= 0) return;
+  hipLaunchKernelGGL(bf16_to_f32_k, dim3((unsigned)ceil_div64(n, 256)), dim3(256), 0, st, x, y, n);
+}
+void lora_cast(const float* src, int64_t ss, uint16_t* dst, int64_t ds, int L, const CastSeg& seg,
+               hipStream_t st) {
+  int64_t mx = 0;
+  for (int j = 0; j < seg.nseg; ++j) mx = seg.n[j] > mx ? seg.n[j] : mx;
+  const unsigned gx = (unsigned)(ceil_div64(mx, 256) < 1024 ? ceil_div64(mx, 256) : 1024);
+  hipLaunchKernelGGL(lora_cast_k, dim3(gx, seg.nseg, L), dim3(256), 0, st, src, ss, dst, ds, seg);
+}
+void ce_targets(const int32_t* ids, int B, int S, int32_t* tgt, hipStream_t st) {
+  hipLaunchKernelGGL(ce_targets_k, dim3(ceil_div(B * S, 256)), dim3(256), 0, st, ids, B, S, tgt);
+}
+void ce_finalize(const float* stats, int ntiles, const float* tgt_logit, const int32_t* tgt, int T,
+                 float* lse, float* logp, hipStream_t st) {
+  hipLaunchKernelGGL(ce_finalize_k, dim3(ceil_div(T, 4)), dim3(256), 0, st, stats, ntiles, tgt_logit,
+                     tgt, T, lse, logp);
+}
+void sft_weights_loss(const float* logp, const int32_t* tgt, int T, int N, float* w, float* loss,
+                      hipStream_t st) {
+  hipLaunchKernelGGL(sft_loss_k, dim3(1), dim3(TB), 0, st, logp, tgt, T, N, w, loss);
+}
+void seq_logp(const float* logp, int B, int S, int prompt_len, float* seq, float* tok, hipStream_t st) {
+  hipLaunchKernelGGL(seq_logp_k, dim3(B), dim3(TB), 0, st, logp, S, prompt_len, seq, tok);
+}
+void dpo_loss(const float* logp_pol, const float* logp_ref, int S, int prompt_len, float beta,
+              float* w, float* loss, float* aux, hipStream_t st) {
+  hipLaunchKernelGGL(dpo_k, dim3(1), dim3(TB), 0, st, logp_pol, logp_ref, S, prompt_len, beta, w,
+                     loss, aux);
+}
+void spin_delay(int64_t ticks, hipStream_t st) {
+  if (ticks <= 0) return;
+  hipLaunchKernelGGL(spin_k, dim3(1), dim3(64), 0, st, ticks);
+}

@@ -1,0 +1,54 @@
+// Launch interface of the bf16 / NF4 MFMA GEMM family.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+// How operand A (M x K) is stored.
+enum ALoad { A_ROW = 0,    // A[m * lda + k]
+             A_COL = 1 };  // A[k * lda + m]
+// How operand B (contraction k, output column n) is stored.
+enum BLoad { B_BF16_NT = 0,  // bf16 B[n * ldb + k]
+             B_BF16_NN = 1,  // bf16 B[k * ldb + n]
+             B_NF4_NT = 2,   // NF4 W, flat element n * ldq + k
+             B_NF4_NN = 3 }; // NF4 W, flat element k * ldq + n
+enum Epi {
+  EPI_BF16 = 0,       // C bf16 = alpha*acc (+ s2*acc2 LoRA) (+ R residual)
+  EPI_F32 = 1,        // C f32 = alpha*acc
+  EPI_F32_ACC = 2,    // C f32 += alpha*acc
+  EPI_PARTIAL = 3,    // split-K partial sums (reduced by gemm_reduce)
+  EPI_SWIGLU_BWD = 4, // acc = dL/da; writes bf16 dg (col n) and du (col I + n)
+  EPI_CE_STATS = 5,   // per-row (max, sum exp) over the tile's columns + target logit
+  EPI_CE_GRAD = 6     // C bf16 = w_m (exp(acc - lse_m) - [n == tgt_m])
+};
+enum LoraMode { LORA_NONE = 0, LORA_FWD = 1, LORA_DX = 2 };
+
+struct GemmArgs {
+  int M, N, K;
+  const uint16_t* A; int64_t lda;
+  const uint16_t* Bh; int64_t ldb;
+  const uint8_t* Bq; const float* Bs; int64_t ldq;
+  // LoRA second contraction
+  int lora;
+  const uint16_t* A2; int64_t lda2;  // U_cat [M, nmod*r] (FWD) or du_cat [M, K2] (DX)
+  const uint16_t* B2; int64_t ldb2;  // A_cat [K2, N] row-major (DX)
+  int K2;                            // r (FWD) or total contraction (DX)
+  int nmod;                          // FWD: modules along N
+  int mod_end[4];                    // FWD: cumulative column end of each module
+  const uint16_t* modB[4];           // FWD: B_g [N_g, r] row-major
+  float s2;                          // FWD: LoRA scale
+  // epilogue
+  float alpha;
+  void* C; int64_t ldc;
+  const uint16_t* R; int64_t ldr;
+  const uint16_t* gu; int64_t ldgu; int I;
+  const int32_t* tgt; const float* lse; const float* roww;
+  float* stats; int stats_ld; float* tgt_logit; int col0;
+  int ksplit; float* partial;
+};
+
+// Returns 0, or -1 when the (tile, loaders, epilogue) combination is not built.
+int gemm_launch(const GemmArgs& g, int aload, int bload, int epi, int tile, hipStream_t st);
+// out = epilogue(sum_z partial[z]) for split-K: mode 0 -> bf16 alpha*sum, 1 -> f32 alpha*sum.
+void gemm_reduce(const float* partial, int ksplit, int M, int N, float alpha, int mode,
+                 void* C, int64_t ldc, hipStream_t st);
+int64_t gemm_partial_elems(int M, int N, int ksplit);

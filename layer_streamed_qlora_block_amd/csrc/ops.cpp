@@ -1,0 +1,106 @@
+// Host-side orchestration of GEMM launches for the QLoRA linears.
+#include <algorithm>
+
+#include "gemm.h"
+#include "internal.h"
+#include "ops.h"
+
+namespace {
+
+constexpr int kSkinnyTarget = 512;   // workgroups to aim for with split-K
+constexpr int kMaxSplit = 64;
+
+int pick_split(int M, int N, int K) {
+  const int64_t tiles = cdiv(M, 64) * cdiv(N, 64);
+  const int nk = (int)cdiv(K, 64);
+  int ks = (int)std::max<int64_t>(1, kSkinnyTarget / std::max<int64_t>(tiles, 1));
+  return std::max(1, std::min({ks, nk, kMaxSplit}));
+}
+
+int skinny(int aload, const uint16_t* A, int64_t lda, int bload, const uint16_t* B, int64_t ldb,
+           int M, int N, int K, float alpha, int mode, void* C, int64_t ldc, float* part,
+           hipStream_t st) {
+  GemmArgs g{};
+  g.M = M; g.N = N; g.K = K;
+  g.A = A; g.lda = lda;
+  g.Bh = B; g.ldb = ldb;
+  g.ksplit = pick_split(M, N, K);
+  g.partial = part;
+  if (gemm_launch(g, aload, bload, EPI_PARTIAL, 64, st)) return -1;
+  gemm_reduce(part, g.ksplit, M, N, alpha, mode, C, ldc, st);
+  return 0;
+}
+
+}  // namespace
+
+int64_t skinny_partial_floats(int64_t max_mn) {
+  return std::max<int64_t>(max_mn, (int64_t)kSkinnyTarget * 64 * 64);
+}
+
+int64_t linear_ws_bytes(int T, int N, int K, int r) {
+  const int64_t du = align_up((int64_t)T * r * 2, 256);
+  const int64_t mn = std::max({(int64_t)T * r, (int64_t)N * r, (int64_t)r * K});
+  return du + 4 * skinny_partial_floats(mn);
+}
+
+int skinny_U(const uint16_t* x, int64_t ldx, int T, int K, const uint16_t* A, int n, uint16_t* U,
+             int64_t ldu, float* part, hipStream_t st) {
+  return skinny(A_ROW, x, ldx, B_BF16_NT, A, K, T, n, K, 1.f, 0, U, ldu, part, st);
+}
+
+int skinny_du(const uint16_t* dy, int64_t lddy, int T, int N, const uint16_t* B, int r, float s,
+              uint16_t* du, int64_t lddu, float* part, hipStream_t st) {
+  return skinny(A_ROW, dy, lddy, B_BF16_NN, B, r, T, r, N, s, 0, du, lddu, part, st);
+}
+
+int skinny_dB(const uint16_t* dy, int64_t lddy, int T, int N, const uint16_t* u, int64_t ldu,
+              float s, float* dB, float* part, hipStream_t st, int r) {
+  const int rr = r > 0 ? r : (int)ldu;
+  return skinny(A_COL, dy, lddy, B_BF16_NN, u, ldu, N, rr, T, s, 1, dB, rr, part, st);
+}
+
+int skinny_dA(const uint16_t* du, int64_t lddu, int T, int r, const uint16_t* x, int64_t ldx, int K,
+              float* dA, float* part, hipStream_t st) {
+  return skinny(A_COL, du, lddu, B_BF16_NN, x, ldx, r, K, T, 1.f, 1, dA, K, part, st);
+}
+
+int linear_fwd(const LinearFwd& f, hipStream_t st) {
+  const int64_t ldx = f.ldx ? f.ldx : f.K;
+  const bool lora = f.A != nullptr && f.r > 0;
+  if (lora) {
+    if (skinny_U(f.x, ldx, f.T, f.K, f.A, f.nmod * f.r, f.u, f.nmod * f.r, f.ws, st)) return -1;
+  }
+  GemmArgs g{};
+  g.M = f.T; g.N = f.N; g.K = f.K;
+  g.A = f.x; g.lda = ldx;
+  g.Bq = f.codes; g.Bs = f.absmax; g.ldq = f.K;
+  g.alpha = 1.f;
+  g.C = f.y; g.ldc = f.ldy ? f.ldy : f.N;
+  g.R = f.res; g.ldr = f.ldres ? f.ldres : f.N;
+  if (lora) {
+    g.lora = LORA_FWD;
+    g.A2 = f.u; g.lda2 = f.nmod * f.r;
+    g.K2 = f.r;
+    g.nmod = f.nmod;
+    for (int i = 0; i < f.nmod; ++i) { g.mod_end[i] = f.mod_end[i]; g.modB[i] = f.Bm[i]; }
+    g.s2 = f.s;
+  }
+  return gemm_launch(g, A_ROW, B_NF4_NT, EPI_BF16, 128, st);
+}
+
+int linear_dx(const LinearDx& d, hipStream_t st) {
+  GemmArgs g{};
+  g.M = d.T; g.N = d.Nout; g.K = d.Kc;
+  g.A = d.dy; g.lda = d.lddy;
+  g.Bq = d.codes; g.Bs = d.absmax; g.ldq = d.ldq;
+  g.alpha = 1.f;
+  g.C = d.out; g.ldc = d.ldo;
+  if (d.du && d.rc > 0) {
+    g.lora = LORA_DX;
+    g.A2 = d.du; g.lda2 = d.lddu;
+    g.B2 = d.Acat; g.ldb2 = d.Nout;
+    g.K2 = d.rc;
+  }
+  g.gu = d.gu; g.ldgu = d.ldgu; g.I = d.I;
+  return gemm_launch(g, A_ROW, B_NF4_NN, d.epi, 128, st);
+}

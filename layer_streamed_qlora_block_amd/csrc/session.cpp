@@ -1,0 +1,803 @@
+// Session: workspace plan, two-slot streaming pool and the step schedules.
+//
+// The frozen decoder stack streams from the pinned store into a small pool of
+// device buffers, one layer ahead of compute; a slot is reused once the layer
+// it held is finished (page "Can You Fine-Tune Llama 3.1 8B on a 4GB GPU?
+// ...", section "How Soup's layer streaming actually works", item 3).  The
+// backward sweep reads the layers again because each layer's forward is
+// recomputed from its checkpointed input (same section, item 4).  The last two
+// layers of the forward sweep are still resident at the turn, so a step loads
+// 2L - 2 records; a slot that still holds the layer a prefetch asks for is not
+// copied again (across steps too).
+//
+// Ordering is two-sided with events: the copy stream waits on `released[s]`
+// (recorded on the compute stream after the last kernel that reads slot s)
+// before overwriting the slot, and the compute stream waits on `copied[s]`
+// before the first kernel that reads it.  That is the guard against the
+// size-dependent silent wrong-gradient class of bug described on the same page
+// ("Did a correctness bug invalidate the Llama 3.1 8B result?").
+#include <algorithm>
+#include <chrono>
+#include <cmath>
+#include <cstring>
+#include <thread>
+#include <vector>
+
+#include "attn.h"
+#include "gemm.h"
+#include "internal.h"
+#include "ops.h"
+
+namespace {
+
+constexpr int kTile = 128;
+
+struct Plan {
+  int64_t slots, ckpt, n1, qkv, attn, lse, Dv, h, n2, gu, a, uqkv, uo, ugu, udown;
+  int64_t g, dh, dn, dyb, dgu, dattn, dqf, dkf, dvf, dqkv, du, xo;
+  int64_t lbf, hf, stats, lse_t, tgt_logit, logp, logp_ref, roww, tgt, ids, dlog, dhf, part;
+  int64_t xref0, xref1, scal, rope;
+  int64_t total;
+};
+
+struct Sizes {
+  int Tm, Smax, Vc, ntiles, nchunks;
+};
+
+Sizes sizes_of(const Shape& sh, const qls_run_cfg& run) {
+  Sizes z{};
+  z.Tm = run.max_tokens;
+  z.Smax = run.max_seq;
+  int vc = run.ce_chunk > 0 ? run.ce_chunk : 32768;
+  vc = (int)align_up(vc, kTile);
+  z.Vc = std::min<int>(vc, (int)align_up(sh.c.vocab, kTile));
+  z.ntiles = (int)cdiv(sh.c.vocab, kTile);
+  z.nchunks = (int)cdiv(sh.c.vocab, z.Vc);
+  return z;
+}
+
+Plan make_plan(const Shape& sh, const RecordLayout& lay, const qls_run_cfg& run, int64_t lora_numel) {
+  const Sizes z = sizes_of(sh, run);
+  const int64_t T = z.Tm, d = sh.c.hidden, I = sh.c.intermediate, r = sh.c.lora_r;
+  const int64_t L = sh.c.n_layers, H = sh.c.n_heads;
+  Plan p{};
+  int64_t off = 0;
+  auto take = [&](int64_t bytes) { const int64_t o = off; off = align_up(off + std::max<int64_t>(bytes, 1), 256); return o; };
+  p.slots = take((run.mode == QLS_RESIDENT ? L : 2) * lay.bytes);
+  p.ckpt = take((L + 1) * T * d * 2);
+  p.n1 = take(T * d * 2);
+  p.qkv = take(T * sh.nqkv * 2);
+  p.attn = take(T * sh.qd * 2);
+  p.lse = take(T * H * 4);
+  p.Dv = take(T * H * 4);
+  p.h = take(T * d * 2);
+  p.n2 = take(T * d * 2);
+  p.gu = take(T * 2 * I * 2);
+  p.a = take(T * I * 2);
+  p.uqkv = take(T * 3 * r * 2);
+  p.uo = take(T * r * 2);
+  p.ugu = take(T * 2 * r * 2);
+  p.udown = take(T * r * 2);
+  p.g = take(T * d * 4);
+  p.dh = take(T * d * 4);
+  p.dn = take(T * d * 4);
+  p.dyb = take(T * d * 2);
+  p.dgu = take(T * 2 * I * 2);
+  p.dattn = take(T * sh.qd * 2);
+  p.dqf = take(T * sh.qd * 4);
+  p.dkf = take(T * sh.kvd * 4);
+  p.dvf = take(T * sh.kvd * 4);
+  p.dqkv = take(T * sh.nqkv * 2);
+  p.du = take(T * 3 * r * 2);
+  p.xo = take(T * d * 2);
+  p.lbf = take(lora_numel * 2);
+  p.hf = take(T * d * 2);
+  p.stats = take(T * z.ntiles * 2 * 4);
+  p.lse_t = take(T * 4);
+  p.tgt_logit = take(T * 4);
+  p.logp = take(T * 4);
+  p.logp_ref = take(T * 4);
+  p.roww = take(T * 4);
+  p.tgt = take(T * 4);
+  p.ids = take(T * 4);
+  p.dlog = take(T * z.Vc * 2);
+  p.dhf = take(T * d * 4);
+  const int64_t mx = std::max({T * 3 * r, I * r, (int64_t)sh.qd * r, r * std::max<int64_t>(d, I)});
+  p.part = take(skinny_partial_floats(mx) * 4);
+  p.xref0 = take(T * d * 2);
+  p.xref1 = take(T * d * 2);
+  p.scal = take(64);
+  p.rope = take((int64_t)z.Smax * (sh.c.head_dim / 2) * 2 * 4);
+  p.total = off;
+  return p;
+}
+
+bool check_run(const Shape& sh, const qls_run_cfg* run, std::string* why) {
+  auto bad = [&](const char* m) { *why = m; return false; };
+  if (!run) return bad("run cfg is NULL");
+  if (run->mode != QLS_STREAMED && run->mode != QLS_RESIDENT) return bad("mode must be STREAMED or RESIDENT");
+  if (run->max_tokens <= 0 || run->max_seq < 2) return bad("max_tokens must be > 0 and max_seq >= 2");
+  const qls_model_cfg& c = sh.c;
+  if (c.head_dim != 64 && c.head_dim != 128) return bad("head_dim must be 64 or 128");
+  if (c.hidden % 16 || c.intermediate % 16 || sh.qd % 16 || sh.kvd % 16)
+    return bad("hidden, intermediate and head widths must be multiples of 16");
+  if (c.lora_r % 8 || c.lora_r > 128) return bad("lora_r must be a multiple of 8 up to 128");
+  if (c.vocab % 8) return bad("vocab must be a multiple of 8");
+  return true;
+}
+
+struct TimedEv { hipEvent_t a, b; };
+
+}  // namespace
+
+struct qls_session {
+  const qls_store* st = nullptr;
+  Shape sh;
+  RecordLayout lay;
+  LoraLayout ll;
+  int64_t wa[QLS_NMOD], wb[QLS_NMOD];   // bf16 working-copy offsets (elements, per layer)
+  CastSeg seg;
+  qls_run_cfg run;
+  Sizes z;
+  Plan p;
+  uint8_t* ws = nullptr;
+  hipStream_t cs = nullptr, ps = nullptr;
+  qls_resident res;
+  hipEvent_t copied[2] = {}, released[2] = {};
+  int slot_layer[2] = {-1, -1};
+  uint32_t dbg = 0;
+  int delay_us = 0;
+  int64_t wall_khz = 100000;
+  // stats
+  int64_t steps = 0, loads = 0, h2d = 0;
+  bool timing = false;
+  std::vector<hipEvent_t> ev_pool;
+  size_t ev_next = 0;
+  std::vector<TimedEv> copy_ev, comp_ev;
+  hipEvent_t step_a = nullptr, step_b = nullptr;
+
+  template <class T> T* at(int64_t off) const { return reinterpret_cast<T*>(ws + off); }
+  uint16_t* ck(int l) const { return at<uint16_t>(p.ckpt) + (int64_t)l * z.Tm * sh.c.hidden; }
+  uint16_t* lw(int l) const { return at<uint16_t>(p.lbf) + (int64_t)l * ll.per_layer; }
+
+  hipEvent_t next_ev() {
+    if (ev_next >= ev_pool.size()) {
+      hipEvent_t e;
+      if (hipEventCreate(&e) != hipSuccess) return nullptr;
+      ev_pool.push_back(e);
+    }
+    return ev_pool[ev_next++];
+  }
+};
+
+namespace {
+
+void sleep_cb(void* us) {
+  std::this_thread::sleep_for(std::chrono::microseconds((int64_t)(intptr_t)us));
+}
+
+// ---------------------------------------------------------------- pool
+int prefetch(qls_session* S, int layer) {
+  if (S->run.mode == QLS_RESIDENT) return QLS_OK;
+  const int s = layer & 1;
+  const bool reuse = !(S->dbg & (QLS_DBG_NO_REUSE | QLS_DBG_POISON_ON_RELEASE));
+  if (reuse && S->slot_layer[s] == layer) return QLS_OK;
+  QLS_HIP(hipStreamWaitEvent(S->ps, S->released[s], 0));
+  if (S->dbg & QLS_DBG_COPY_DELAY)
+    QLS_HIP(hipLaunchHostFunc(S->ps, sleep_cb, (void*)(intptr_t)S->delay_us));
+  TimedEv te{};
+  if (S->timing) { te.a = S->next_ev(); te.b = S->next_ev(); QLS_HIP(hipEventRecord(te.a, S->ps)); }
+  QLS_HIP(hipMemcpyAsync(S->at<uint8_t>(S->p.slots) + s * S->lay.bytes, store_record(S->st, layer),
+                         S->lay.bytes, hipMemcpyHostToDevice, S->ps));
+  if (S->timing) { QLS_HIP(hipEventRecord(te.b, S->ps)); S->copy_ev.push_back(te); }
+  QLS_HIP(hipEventRecord(S->copied[s], S->ps));
+  S->slot_layer[s] = layer;
+  S->loads += 1;
+  S->h2d += S->lay.bytes;
+  return QLS_OK;
+}
+
+int acquire(qls_session* S, int layer, const uint8_t** rec, TimedEv* te) {
+  if (S->run.mode == QLS_RESIDENT) {
+    *rec = S->at<uint8_t>(S->p.slots) + (int64_t)layer * S->lay.bytes;
+  } else {
+    const int s = layer & 1;
+    if (S->slot_layer[s] != layer) {
+      int rc = prefetch(S, layer);
+      if (rc) return rc;
+    }
+    QLS_HIP(hipStreamWaitEvent(S->cs, S->copied[s], 0));
+    *rec = S->at<uint8_t>(S->p.slots) + s * S->lay.bytes;
+  }
+  if (S->timing) { te->a = S->next_ev(); te->b = S->next_ev(); QLS_HIP(hipEventRecord(te->a, S->cs)); }
+  return QLS_OK;
+}
+
+int release(qls_session* S, int layer, TimedEv* te) {
+  if (S->dbg & QLS_DBG_COMPUTE_DELAY) spin_delay((int64_t)S->delay_us * S->wall_khz / 1000, S->cs);
+  if (S->timing) { QLS_HIP(hipEventRecord(te->b, S->cs)); S->comp_ev.push_back(*te); }
+  if (S->run.mode == QLS_RESIDENT) return QLS_OK;
+  const int s = layer & 1;
+  QLS_HIP(hipEventRecord(S->released[s], S->cs));
+  if (S->dbg & QLS_DBG_POISON_ON_RELEASE) {
+    QLS_HIP(hipStreamWaitEvent(S->ps, S->released[s], 0));
+    QLS_HIP(hipMemsetAsync(S->at<uint8_t>(S->p.slots) + s * S->lay.bytes, 0xFF, S->lay.bytes, S->ps));
+    S->slot_layer[s] = -1;
+  }
+  return QLS_OK;
+}
+
+// ---------------------------------------------------------------- layer
+struct W {
+  const uint8_t* code[QLS_NMOD];
+  const float* amax[QLS_NMOD];
+  const uint16_t* na;
+  const uint16_t* nm;
+};
+
+W weights(const qls_session* S, const uint8_t* rec) {
+  W w{};
+  for (int m = 0; m < QLS_NMOD; ++m) {
+    w.code[m] = rec + S->lay.code_off[m];
+    w.amax[m] = reinterpret_cast<const float*>(rec + S->lay.absmax_off[m]);
+  }
+  w.na = reinterpret_cast<const uint16_t*>(rec + S->lay.norm_attn_off);
+  w.nm = reinterpret_cast<const uint16_t*>(rec + S->lay.norm_mlp_off);
+  return w;
+}
+
+#define QLS_RC(x) do { if (x) return fail(QLS_EHIP, "kernel launch configuration not built: " #x); } while (0)
+
+int fwd_layer(qls_session* S, int l, const uint8_t* rec, const uint16_t* x, uint16_t* xout, bool lora,
+              int T, int B, int Sq) {
+  const Shape& sh = S->sh;
+  const int d = sh.c.hidden, I = sh.c.intermediate, r = sh.c.lora_r;
+  const W w = weights(S, rec);
+  const uint16_t* lw = S->lw(l);
+  hipStream_t st = S->cs;
+  uint16_t* n1 = S->at<uint16_t>(S->p.n1);
+  uint16_t* qkv = S->at<uint16_t>(S->p.qkv);
+  uint16_t* attn = S->at<uint16_t>(S->p.attn);
+  uint16_t* h = S->at<uint16_t>(S->p.h);
+  uint16_t* n2 = S->at<uint16_t>(S->p.n2);
+  uint16_t* gu = S->at<uint16_t>(S->p.gu);
+  uint16_t* a = S->at<uint16_t>(S->p.a);
+  float* part = S->at<float>(S->p.part);
+
+  rmsnorm_fwd(x, w.na, sh.c.rms_eps, n1, T, d, st);
+  LinearFwd f{};
+  f.T = T; f.N = sh.nqkv; f.K = d; f.r = r; f.x = n1; f.ldx = d;
+  f.codes = w.code[QLS_Q]; f.absmax = w.amax[QLS_Q];
+  f.A = lora ? lw + S->wa[QLS_Q] : nullptr;
+  f.nmod = 3; f.mod_end[0] = sh.qd; f.mod_end[1] = sh.qd + sh.kvd; f.mod_end[2] = sh.nqkv;
+  f.Bm[0] = lw + S->wb[QLS_Q]; f.Bm[1] = lw + S->wb[QLS_K]; f.Bm[2] = lw + S->wb[QLS_V];
+  f.s = sh.s; f.y = qkv; f.ldy = sh.nqkv; f.u = S->at<uint16_t>(S->p.uqkv); f.ws = part;
+  QLS_RC(linear_fwd(f, st));
+  rope_fwd(qkv, sh.nqkv, T, Sq, sh.c.n_heads, sh.c.n_kv_heads, sh.c.head_dim, S->at<float>(S->p.rope), st);
+  AttnArgs aa{};
+  aa.qkv = qkv; aa.ld = sh.nqkv; aa.q_off = 0; aa.k_off = sh.qd; aa.v_off = sh.qd + sh.kvd;
+  aa.S = Sq; aa.H = sh.c.n_heads; aa.KV = sh.c.n_kv_heads; aa.hd = sh.c.head_dim;
+  aa.scale = 1.f / std::sqrt((float)sh.c.head_dim);
+  aa.out = attn; aa.ldo = sh.qd; aa.lse = S->at<float>(S->p.lse);
+  QLS_RC(attn_fwd(aa, B, st));
+
+  f = LinearFwd{};
+  f.T = T; f.N = d; f.K = sh.qd; f.r = r; f.x = attn; f.ldx = sh.qd;
+  f.codes = w.code[QLS_O]; f.absmax = w.amax[QLS_O];
+  f.A = lora ? lw + S->wa[QLS_O] : nullptr;
+  f.nmod = 1; f.mod_end[0] = d; f.Bm[0] = lw + S->wb[QLS_O];
+  f.s = sh.s; f.res = x; f.ldres = d; f.y = h; f.ldy = d; f.u = S->at<uint16_t>(S->p.uo); f.ws = part;
+  QLS_RC(linear_fwd(f, st));
+
+  rmsnorm_fwd(h, w.nm, sh.c.rms_eps, n2, T, d, st);
+  f = LinearFwd{};
+  f.T = T; f.N = 2 * I; f.K = d; f.r = r; f.x = n2; f.ldx = d;
+  f.codes = w.code[QLS_GATE]; f.absmax = w.amax[QLS_GATE];
+  f.A = lora ? lw + S->wa[QLS_GATE] : nullptr;
+  f.nmod = 2; f.mod_end[0] = I; f.mod_end[1] = 2 * I;
+  f.Bm[0] = lw + S->wb[QLS_GATE]; f.Bm[1] = lw + S->wb[QLS_UP];
+  f.s = sh.s; f.y = gu; f.ldy = 2 * I; f.u = S->at<uint16_t>(S->p.ugu); f.ws = part;
+  QLS_RC(linear_fwd(f, st));
+  swiglu_fwd(gu, a, T, I, st);
+
+  f = LinearFwd{};
+  f.T = T; f.N = d; f.K = I; f.r = r; f.x = a; f.ldx = I;
+  f.codes = w.code[QLS_DOWN]; f.absmax = w.amax[QLS_DOWN];
+  f.A = lora ? lw + S->wa[QLS_DOWN] : nullptr;
+  f.nmod = 1; f.mod_end[0] = d; f.Bm[0] = lw + S->wb[QLS_DOWN];
+  f.s = sh.s; f.res = h; f.ldres = d; f.y = xout; f.ldy = d; f.u = S->at<uint16_t>(S->p.udown); f.ws = part;
+  QLS_RC(linear_fwd(f, st));
+  return QLS_OK;
+}
+
+// g (float [T, d]) holds dL/d(layer output) on entry and dL/d(layer input) on exit.
+int bwd_layer(qls_session* S, int l, const uint8_t* rec, const uint16_t* x, float* grads, int T, int B,
+              int Sq) {
+  const Shape& sh = S->sh;
+  const int d = sh.c.hidden, I = sh.c.intermediate, r = sh.c.lora_r;
+  const float s = sh.s;
+  const W w = weights(S, rec);
+  const uint16_t* lw = S->lw(l);
+  hipStream_t st = S->cs;
+  float* gl = grads + (int64_t)l * S->ll.per_layer;
+  auto dA = [&](int m) { return gl + S->ll.a_off[m]; };
+  auto dB = [&](int m) { return gl + S->ll.b_off[m]; };
+  float* g = S->at<float>(S->p.g);
+  float* dh = S->at<float>(S->p.dh);
+  float* dn = S->at<float>(S->p.dn);
+  uint16_t* dyb = S->at<uint16_t>(S->p.dyb);
+  uint16_t* dgu = S->at<uint16_t>(S->p.dgu);
+  uint16_t* du = S->at<uint16_t>(S->p.du);
+  float* part = S->at<float>(S->p.part);
+  const uint16_t* n1 = S->at<uint16_t>(S->p.n1);
+  const uint16_t* n2 = S->at<uint16_t>(S->p.n2);
+  const uint16_t* attn = S->at<uint16_t>(S->p.attn);
+  const uint16_t* a = S->at<uint16_t>(S->p.a);
+  const uint16_t* h = S->at<uint16_t>(S->p.h);
+  const uint16_t* uqkv = S->at<uint16_t>(S->p.uqkv);
+  const uint16_t* ugu = S->at<uint16_t>(S->p.ugu);
+
+  // ---- down projection + SwiGLU
+  f32_to_bf16(g, dyb, (int64_t)T * d, st);
+  QLS_RC(skinny_du(dyb, d, T, d, lw + S->wb[QLS_DOWN], r, s, du, r, part, st));
+  QLS_RC(skinny_dB(dyb, d, T, d, S->at<uint16_t>(S->p.udown), r, s, dB(QLS_DOWN), part, st, r));
+  QLS_RC(skinny_dA(du, r, T, r, a, I, I, dA(QLS_DOWN), part, st));
+  LinearDx x1{};
+  x1.T = T; x1.Kc = d; x1.Nout = I; x1.dy = dyb; x1.lddy = d;
+  x1.codes = w.code[QLS_DOWN]; x1.absmax = w.amax[QLS_DOWN]; x1.ldq = I;
+  x1.du = du; x1.lddu = r; x1.Acat = lw + S->wa[QLS_DOWN]; x1.rc = r;
+  x1.out = dgu; x1.ldo = 2 * I; x1.epi = EPI_SWIGLU_BWD;
+  x1.gu = S->at<uint16_t>(S->p.gu); x1.ldgu = 2 * I; x1.I = I;
+  QLS_RC(linear_dx(x1, st));
+
+  // ---- gate / up
+  for (int k = 0; k < 2; ++k) {
+    const int m = k == 0 ? QLS_GATE : QLS_UP;
+    QLS_RC(skinny_du(dgu + k * I, 2 * I, T, I, lw + S->wb[m], r, s, du + k * r, 2 * r, part, st));
+    QLS_RC(skinny_dB(dgu + k * I, 2 * I, T, I, ugu + k * r, 2 * r, s, dB(m), part, st, r));
+    QLS_RC(skinny_dA(du + k * r, 2 * r, T, r, n2, d, d, dA(m), part, st));
+  }
+  LinearDx x2{};
+  x2.T = T; x2.Kc = 2 * I; x2.Nout = d; x2.dy = dgu; x2.lddy = 2 * I;
+  x2.codes = w.code[QLS_GATE]; x2.absmax = w.amax[QLS_GATE]; x2.ldq = d;
+  x2.du = du; x2.lddu = 2 * r; x2.Acat = lw + S->wa[QLS_GATE]; x2.rc = 2 * r;
+  x2.out = dn; x2.ldo = d; x2.epi = EPI_F32;
+  QLS_RC(linear_dx(x2, st));
+  rmsnorm_bwd(h, w.nm, sh.c.rms_eps, dn, g, dh, dyb, T, d, st);
+
+  // ---- o projection
+  QLS_RC(skinny_du(dyb, d, T, d, lw + S->wb[QLS_O], r, s, du, r, part, st));
+  QLS_RC(skinny_dB(dyb, d, T, d, S->at<uint16_t>(S->p.uo), r, s, dB(QLS_O), part, st, r));
+  QLS_RC(skinny_dA(du, r, T, r, attn, sh.qd, sh.qd, dA(QLS_O), part, st));
+  LinearDx x3{};
+  x3.T = T; x3.Kc = d; x3.Nout = sh.qd; x3.dy = dyb; x3.lddy = d;
+  x3.codes = w.code[QLS_O]; x3.absmax = w.amax[QLS_O]; x3.ldq = sh.qd;
+  x3.du = du; x3.lddu = r; x3.Acat = lw + S->wa[QLS_O]; x3.rc = r;
+  x3.out = S->at<uint16_t>(S->p.dattn); x3.ldo = sh.qd; x3.epi = EPI_BF16;
+  QLS_RC(linear_dx(x3, st));
+
+  // ---- attention + RoPE
+  AttnBwdArgs ab{};
+  ab.qkv = S->at<uint16_t>(S->p.qkv); ab.ld = sh.nqkv; ab.q_off = 0; ab.k_off = sh.qd; ab.v_off = sh.qd + sh.kvd;
+  ab.S = Sq; ab.H = sh.c.n_heads; ab.KV = sh.c.n_kv_heads; ab.hd = sh.c.head_dim;
+  ab.scale = 1.f / std::sqrt((float)sh.c.head_dim);
+  ab.dO = S->at<uint16_t>(S->p.dattn); ab.O = attn; ab.lddo = sh.qd;
+  ab.lse = S->at<float>(S->p.lse); ab.D = S->at<float>(S->p.Dv);
+  ab.dq = S->at<float>(S->p.dqf); ab.lddq = sh.qd;
+  ab.dk = S->at<float>(S->p.dkf); ab.dv = S->at<float>(S->p.dvf); ab.lddkv = sh.kvd;
+  QLS_RC(attn_bwd(ab, B, st));
+  uint16_t* dqkv = S->at<uint16_t>(S->p.dqkv);
+  rope_bwd(ab.dq, ab.dk, ab.dv, dqkv, sh.nqkv, T, Sq, sh.c.n_heads, sh.c.n_kv_heads, sh.c.head_dim,
+           S->at<float>(S->p.rope), st);
+
+  // ---- q, k, v
+  const int col[3] = {0, sh.qd, sh.qd + sh.kvd};
+  const int nout[3] = {sh.qd, sh.kvd, sh.kvd};
+  for (int k = 0; k < 3; ++k) {
+    const int m = QLS_Q + k;
+    QLS_RC(skinny_du(dqkv + col[k], sh.nqkv, T, nout[k], lw + S->wb[m], r, s, du + k * r, 3 * r, part, st));
+    QLS_RC(skinny_dB(dqkv + col[k], sh.nqkv, T, nout[k], uqkv + k * r, 3 * r, s, dB(m), part, st, r));
+    QLS_RC(skinny_dA(du + k * r, 3 * r, T, r, n1, d, d, dA(m), part, st));
+  }
+  LinearDx x4{};
+  x4.T = T; x4.Kc = sh.nqkv; x4.Nout = d; x4.dy = dqkv; x4.lddy = sh.nqkv;
+  x4.codes = w.code[QLS_Q]; x4.absmax = w.amax[QLS_Q]; x4.ldq = d;
+  x4.du = du; x4.lddu = 3 * r; x4.Acat = lw + S->wa[QLS_Q]; x4.rc = 3 * r;
+  x4.out = dn; x4.ldo = d; x4.epi = EPI_F32;
+  QLS_RC(linear_dx(x4, st));
+  rmsnorm_bwd(x, w.na, sh.c.rms_eps, dn, dh, g, nullptr, T, d, st);
+  return QLS_OK;
+}
+
+// ---------------------------------------------------------------- head
+// Pass 1 over vocabulary chunks: per-row (max, sum exp) per 128-column tile and
+// the target logit, then the log-sum-exp and per-row log-prob.
+int head_fwd(qls_session* S, const uint16_t* xL, int T, float* logp_out) {
+  const Shape& sh = S->sh;
+  const int d = sh.c.hidden, V = sh.c.vocab;
+  hipStream_t st = S->cs;
+  uint16_t* hf = S->at<uint16_t>(S->p.hf);
+  rmsnorm_fwd(xL, S->res.d_final_norm, sh.c.rms_eps, hf, T, d, st);
+  for (int c = 0; c < S->z.nchunks; ++c) {
+    const int col0 = c * S->z.Vc, width = std::min(S->z.Vc, V - col0);
+    GemmArgs g{};
+    g.M = T; g.N = width; g.K = d;
+    g.A = hf; g.lda = d;
+    g.Bh = S->res.d_lm_head + (int64_t)col0 * d; g.ldb = d;
+    g.tgt = S->at<int32_t>(S->p.tgt);
+    g.stats = S->at<float>(S->p.stats); g.stats_ld = S->z.ntiles;
+    g.tgt_logit = S->at<float>(S->p.tgt_logit); g.col0 = col0;
+    QLS_RC(gemm_launch(g, A_ROW, B_BF16_NT, EPI_CE_STATS, kTile, st));
+  }
+  ce_finalize(S->at<float>(S->p.stats), S->z.ntiles, S->at<float>(S->p.tgt_logit),
+              S->at<int32_t>(S->p.tgt), T, S->at<float>(S->p.lse_t), logp_out, st);
+  return QLS_OK;
+}
+
+// Pass 2: dlogits = w (softmax - onehot) chunk by chunk, dhf = sum_c dlogits_c W_c,
+// then back through the final RMSNorm into g.
+int head_bwd(qls_session* S, const uint16_t* xL, int T) {
+  const Shape& sh = S->sh;
+  const int d = sh.c.hidden, V = sh.c.vocab;
+  hipStream_t st = S->cs;
+  float* dhf = S->at<float>(S->p.dhf);
+  uint16_t* dlog = S->at<uint16_t>(S->p.dlog);
+  for (int c = 0; c < S->z.nchunks; ++c) {
+    const int col0 = c * S->z.Vc, width = std::min(S->z.Vc, V - col0);
+    GemmArgs g{};
+    g.M = T; g.N = width; g.K = d;
+    g.A = S->at<uint16_t>(S->p.hf); g.lda = d;
+    g.Bh = S->res.d_lm_head + (int64_t)col0 * d; g.ldb = d;
+    g.C = dlog; g.ldc = S->z.Vc;
+    g.tgt = S->at<int32_t>(S->p.tgt); g.lse = S->at<float>(S->p.lse_t); g.roww = S->at<float>(S->p.roww);
+    g.col0 = col0;
+    QLS_RC(gemm_launch(g, A_ROW, B_BF16_NT, EPI_CE_GRAD, kTile, st));
+    GemmArgs h{};
+    h.M = T; h.N = d; h.K = width;
+    h.A = dlog; h.lda = S->z.Vc;
+    h.Bh = S->res.d_lm_head + (int64_t)col0 * d; h.ldb = d;
+    h.alpha = 1.f; h.C = dhf; h.ldc = d;
+    QLS_RC(gemm_launch(h, A_ROW, B_BF16_NN, c == 0 ? EPI_F32 : EPI_F32_ACC, kTile, st));
+  }
+  rmsnorm_bwd(xL, S->res.d_final_norm, sh.c.rms_eps, dhf, nullptr, S->at<float>(S->p.g), nullptr, T, d, st);
+  return QLS_OK;
+}
+
+int check_tokens(qls_session* S, int B, int Sq) {
+  if (B <= 0 || Sq < 2) return fail(QLS_EINVAL, "need B >= 1 and S >= 2");
+  if (Sq > S->run.max_seq) return fail(QLS_EINVAL, "S exceeds max_seq");
+  if ((int64_t)B * Sq > S->run.max_tokens) return fail(QLS_EINVAL, "B*S exceeds max_tokens");
+  return QLS_OK;
+}
+
+int cast_lora(qls_session* S, const float* d_lora) {
+  lora_cast(d_lora, S->ll.per_layer, S->at<uint16_t>(S->p.lbf), S->ll.per_layer, S->sh.c.n_layers,
+            S->seg, S->cs);
+  return QLS_OK;
+}
+
+int begin_step(qls_session* S) {
+  S->ev_next = 0;
+  S->copy_ev.clear();
+  S->comp_ev.clear();
+  if (S->timing) QLS_HIP(hipEventRecord(S->step_a, S->cs));
+  QLS_HIP(hipMemsetAsync(S->at<int>(S->p.scal), 0, 64, S->cs));
+  int rc = prefetch(S, 0);
+  if (!rc && S->sh.c.n_layers > 1) rc = prefetch(S, 1);
+  return rc;
+}
+
+int end_step(qls_session* S, float* h_loss, const float* d_loss) {
+  S->steps += 1;
+  if (S->timing) QLS_HIP(hipEventRecord(S->step_b, S->cs));
+  if (h_loss) {
+    QLS_HIP(hipStreamSynchronize(S->cs));
+    int bad = 0;
+    QLS_HIP(hipMemcpy(&bad, S->at<int>(S->p.scal), sizeof(int), hipMemcpyDeviceToHost));
+    if (bad) return fail(QLS_EINVAL, "token id outside [0, vocab)");
+    if (d_loss) QLS_HIP(hipMemcpy(h_loss, d_loss, sizeof(float), hipMemcpyDeviceToHost));
+  }
+  return QLS_OK;
+}
+
+// Forward sweep; policy into the checkpoints, and (if ref) the adapters-disabled
+// reference stream alongside on each resident layer.
+int forward_sweep(qls_session* S, int T, int B, int Sq, bool lora, bool ref) {
+  const int L = S->sh.c.n_layers;
+  uint16_t* xr[2] = {S->at<uint16_t>(S->p.xref0), S->at<uint16_t>(S->p.xref1)};
+  for (int l = 0; l < L; ++l) {
+    const uint8_t* rec;
+    TimedEv te{};
+    int rc = acquire(S, l, &rec, &te);
+    if (rc) return rc;
+    if (ref) {
+      rc = fwd_layer(S, l, rec, xr[l & 1], xr[(l + 1) & 1], false, T, B, Sq);
+      if (rc) return rc;
+    }
+    rc = fwd_layer(S, l, rec, S->ck(l), S->ck(l + 1), lora, T, B, Sq);
+    if (rc) return rc;
+    rc = release(S, l, &te);
+    if (rc) return rc;
+    if (l + 2 < L && (rc = prefetch(S, l + 2))) return rc;
+  }
+  return QLS_OK;
+}
+
+int backward_sweep(qls_session* S, int T, int B, int Sq, float* grads) {
+  const int L = S->sh.c.n_layers;
+  for (int l = L - 1; l >= 0; --l) {
+    const uint8_t* rec;
+    TimedEv te{};
+    int rc = acquire(S, l, &rec, &te);
+    if (rc) return rc;
+    rc = fwd_layer(S, l, rec, S->ck(l), S->at<uint16_t>(S->p.xo), true, T, B, Sq);
+    if (rc) return rc;
+    rc = bwd_layer(S, l, rec, S->ck(l), grads, T, B, Sq);
+    if (rc) return rc;
+    rc = release(S, l, &te);
+    if (rc) return rc;
+    if (l - 2 >= 0 && (rc = prefetch(S, l - 2))) return rc;
+  }
+  return QLS_OK;
+}
+
+void fill_rope_table(const Shape& sh, int Smax, std::vector<float>* out) {
+  const int h2 = sh.c.head_dim / 2;
+  out->assign((size_t)Smax * h2 * 2, 0.f);
+  for (int j = 0; j < h2; ++j) {
+    const float inv = (float)std::pow((double)sh.c.rope_theta, -2.0 * j / sh.c.head_dim);
+    for (int p = 0; p < Smax; ++p) {
+      const float ang = (float)p * inv;
+      (*out)[((size_t)p * h2 + j) * 2] = (float)std::cos((double)ang);
+      (*out)[((size_t)p * h2 + j) * 2 + 1] = (float)std::sin((double)ang);
+    }
+  }
+}
+
+}  // namespace
+
+// ================================================================ C ABI
+extern "C" {
+
+int qls_workspace_bytes(const qls_store* st, const qls_run_cfg* run, int64_t* out) {
+  if (!st || !out) return fail(QLS_EINVAL, "NULL argument");
+  const Shape& sh = store_shape(st);
+  std::string why;
+  if (!check_run(sh, run, &why)) return fail(QLS_EINVAL, why);
+  *out = make_plan(sh, store_layout(st), *run, lora_layout(sh).per_layer * sh.c.n_layers).total;
+  return QLS_OK;
+}
+
+int qls_session_create(const qls_store* st, const qls_run_cfg* run, void* d_ws, int64_t ws_bytes,
+                       void* compute_stream, void* copy_stream, const qls_resident* res,
+                       qls_session** out) {
+  if (!out) return fail(QLS_EINVAL, "out is NULL");
+  *out = nullptr;
+  if (!st || !run || !d_ws || !res || !res->d_embed || !res->d_lm_head || !res->d_final_norm)
+    return fail(QLS_EINVAL, "NULL argument");
+  const Shape& sh = store_shape(st);
+  std::string why;
+  if (!check_run(sh, run, &why)) return fail(QLS_EINVAL, why);
+  int missing = -1;
+  if (!store_complete(st, &missing))
+    return fail(QLS_ESTATE, "store layer " + std::to_string(missing) + " was never set");
+  auto* S = new (std::nothrow) qls_session;
+  if (!S) return fail(QLS_ENOMEM, "host allocation failed");
+  S->st = st;
+  S->sh = sh;
+  S->lay = store_layout(st);
+  S->ll = lora_layout(sh);
+  S->run = *run;
+  S->z = sizes_of(sh, *run);
+  const int64_t lora_numel = S->ll.per_layer * sh.c.n_layers;
+  S->p = make_plan(sh, S->lay, *run, lora_numel);
+  if (ws_bytes < S->p.total) {
+    delete S;
+    return fail(QLS_ENOMEM, "workspace of " + std::to_string(ws_bytes) + " bytes is smaller than the " +
+                                std::to_string(S->p.total) + " this session needs");
+  }
+  S->ws = reinterpret_cast<uint8_t*>(d_ws);
+  S->cs = (hipStream_t)compute_stream;
+  S->ps = (hipStream_t)copy_stream;
+  S->res = *res;
+  S->timing = run->timing != 0;
+  // bf16 working copy: A_q A_k A_v A_o A_gate A_up A_down, then the Bs in module order.
+  const int r = sh.c.lora_r;
+  int64_t off = 0;
+  for (int m = 0; m < QLS_NMOD; ++m) { S->wa[m] = off; off += (int64_t)r * sh.mod[m].in; }
+  for (int m = 0; m < QLS_NMOD; ++m) { S->wb[m] = off; off += (int64_t)sh.mod[m].out * r; }
+  S->seg.nseg = 2 * QLS_NMOD;
+  for (int m = 0; m < QLS_NMOD; ++m) {
+    S->seg.so[2 * m] = S->ll.a_off[m]; S->seg.dof[2 * m] = S->wa[m]; S->seg.n[2 * m] = (int64_t)r * sh.mod[m].in;
+    S->seg.so[2 * m + 1] = S->ll.b_off[m]; S->seg.dof[2 * m + 1] = S->wb[m]; S->seg.n[2 * m + 1] = (int64_t)sh.mod[m].out * r;
+  }
+  int dev = 0, khz = 0;
+  if (hipGetDevice(&dev) == hipSuccess &&
+      hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, dev) == hipSuccess && khz > 0)
+    S->wall_khz = khz;
+  auto cleanup = [&](int rc) { qls_session_destroy(S); return rc; };
+  for (int i = 0; i < 2; ++i) {
+    if (hipEventCreateWithFlags(&S->copied[i], hipEventDisableTiming) != hipSuccess ||
+        hipEventCreateWithFlags(&S->released[i], hipEventDisableTiming) != hipSuccess)
+      return cleanup(fail(QLS_EHIP, "hipEventCreate failed"));
+    if (hipEventRecord(S->released[i], S->cs) != hipSuccess)
+      return cleanup(fail(QLS_EHIP, "hipEventRecord failed"));
+  }
+  if (hipEventCreate(&S->step_a) != hipSuccess || hipEventCreate(&S->step_b) != hipSuccess)
+    return cleanup(fail(QLS_EHIP, "hipEventCreate failed"));
+  std::vector<float> tab;
+  fill_rope_table(sh, run->max_seq, &tab);
+  hipError_t e = hipMemcpy(S->at<float>(S->p.rope), tab.data(), tab.size() * 4, hipMemcpyHostToDevice);
+  if (e != hipSuccess) return cleanup(hip_fail(e, "rope table upload"));
+  if (run->mode == QLS_RESIDENT) {
+    for (int l = 0; l < sh.c.n_layers; ++l) {
+      e = hipMemcpy(S->at<uint8_t>(S->p.slots) + (int64_t)l * S->lay.bytes, store_record(st, l), S->lay.bytes,
+                    hipMemcpyHostToDevice);
+      if (e != hipSuccess) return cleanup(hip_fail(e, "resident store upload"));
+    }
+  }
+  *out = S;
+  return QLS_OK;
+}
+
+void qls_session_destroy(qls_session* S) {
+  if (!S) return;
+  if (S->cs) (void)hipStreamSynchronize(S->cs);
+  if (S->ps) (void)hipStreamSynchronize(S->ps);
+  for (int i = 0; i < 2; ++i) {
+    if (S->copied[i]) (void)hipEventDestroy(S->copied[i]);
+    if (S->released[i]) (void)hipEventDestroy(S->released[i]);
+  }
+  if (S->step_a) (void)hipEventDestroy(S->step_a);
+  if (S->step_b) (void)hipEventDestroy(S->step_b);
+  for (auto e : S->ev_pool) (void)hipEventDestroy(e);
+  delete S;
+}
+
+int qls_sft_step(qls_session* S, const int32_t* d_ids, int B, int Sq, const float* d_lora,
+                 float* d_grads, float* d_loss, float* h_loss) {
+  if (!S || !d_ids || !d_lora || !d_grads || !d_loss) return fail(QLS_EINVAL, "NULL argument");
+  int rc = check_tokens(S, B, Sq);
+  if (rc) return rc;
+  const int T = B * Sq;
+  const Shape& sh = S->sh;
+  if ((rc = begin_step(S))) return rc;
+  cast_lora(S, d_lora);
+  embed_gather(d_ids, S->res.d_embed, S->ck(0), T, sh.c.hidden, sh.c.vocab, S->at<int>(S->p.scal), S->cs);
+  ce_targets(d_ids, B, Sq, S->at<int32_t>(S->p.tgt), S->cs);
+  if ((rc = forward_sweep(S, T, B, Sq, true, false))) return rc;
+  const uint16_t* xL = S->ck(sh.c.n_layers);
+  if ((rc = head_fwd(S, xL, T, S->at<float>(S->p.logp)))) return rc;
+  sft_weights_loss(S->at<float>(S->p.logp), S->at<int32_t>(S->p.tgt), T, B * (Sq - 1),
+                   S->at<float>(S->p.roww), d_loss, S->cs);
+  if ((rc = head_bwd(S, xL, T))) return rc;
+  if ((rc = backward_sweep(S, T, B, Sq, d_grads))) return rc;
+  QLS_HIP(hipGetLastError());
+  return end_step(S, h_loss, d_loss);
+}
+
+int qls_logprobs(qls_session* S, const int32_t* d_ids, int B, int Sq, int prompt_len, const float* d_lora,
+                 float* d_seq_logp, float* d_tok_logp) {
+  if (!S || !d_ids || !d_seq_logp) return fail(QLS_EINVAL, "NULL argument");
+  int rc = check_tokens(S, B, Sq);
+  if (rc) return rc;
+  if (prompt_len < 1 || prompt_len >= Sq) return fail(QLS_EINVAL, "prompt_len must be in [1, S)");
+  const int T = B * Sq;
+  const Shape& sh = S->sh;
+  if ((rc = begin_step(S))) return rc;
+  if (d_lora) cast_lora(S, d_lora);
+  embed_gather(d_ids, S->res.d_embed, S->ck(0), T, sh.c.hidden, sh.c.vocab, S->at<int>(S->p.scal), S->cs);
+  ce_targets(d_ids, B, Sq, S->at<int32_t>(S->p.tgt), S->cs);
+  if ((rc = forward_sweep(S, T, B, Sq, d_lora != nullptr, false))) return rc;
+  if ((rc = head_fwd(S, S->ck(sh.c.n_layers), T, S->at<float>(S->p.logp)))) return rc;
+  seq_logp(S->at<float>(S->p.logp), B, Sq, prompt_len, d_seq_logp, d_tok_logp, S->cs);
+  QLS_HIP(hipGetLastError());
+  return end_step(S, nullptr, nullptr);
+}
+
+int qls_dpo_step(qls_session* S, const int32_t* d_chosen, const int32_t* d_rejected, int Sq, int prompt_len,
+                 float beta, const float* d_lora, float* d_grads, float* d_loss, float* h_loss, float* d_aux) {
+  if (!S || !d_chosen || !d_rejected || !d_lora || !d_grads || !d_loss) return fail(QLS_EINVAL, "NULL argument");
+  int rc = check_tokens(S, 2, Sq);
+  if (rc) return rc;
+  if (prompt_len < 1 || prompt_len >= Sq) return fail(QLS_EINVAL, "prompt_len must be in [1, S)");
+  const int B = 2, T = 2 * Sq;
+  const Shape& sh = S->sh;
+  const int d = sh.c.hidden;
+  if ((rc = begin_step(S))) return rc;
+  int32_t* ids = S->at<int32_t>(S->p.ids);
+  QLS_HIP(hipMemcpyAsync(ids, d_chosen, Sq * 4, hipMemcpyDeviceToDevice, S->cs));
+  QLS_HIP(hipMemcpyAsync(ids + Sq, d_rejected, Sq * 4, hipMemcpyDeviceToDevice, S->cs));
+  cast_lora(S, d_lora);
+  embed_gather(ids, S->res.d_embed, S->ck(0), T, d, sh.c.vocab, S->at<int>(S->p.scal), S->cs);
+  QLS_HIP(hipMemcpyAsync(S->at<uint16_t>(S->p.xref0), S->ck(0), (size_t)T * d * 2, hipMemcpyDeviceToDevice, S->cs));
+  ce_targets(ids, B, Sq, S->at<int32_t>(S->p.tgt), S->cs);
+  if ((rc = forward_sweep(S, T, B, Sq, true, true))) return rc;
+  const int L = sh.c.n_layers;
+  const uint16_t* xref = S->at<uint16_t>(L & 1 ? S->p.xref1 : S->p.xref0);
+  if ((rc = head_fwd(S, xref, T, S->at<float>(S->p.logp_ref)))) return rc;
+  const uint16_t* xL = S->ck(L);
+  if ((rc = head_fwd(S, xL, T, S->at<float>(S->p.logp)))) return rc;
+  dpo_loss(S->at<float>(S->p.logp), S->at<float>(S->p.logp_ref), Sq, prompt_len, beta, S->at<float>(S->p.roww),
+           d_loss, d_aux, S->cs);
+  if ((rc = head_bwd(S, xL, T))) return rc;
+  if ((rc = backward_sweep(S, T, B, Sq, d_grads))) return rc;
+  QLS_HIP(hipGetLastError());
+  return end_step(S, h_loss, d_loss);
+}
+
+int qls_layer_fwd_bwd(qls_session* S, int layer, const uint16_t* d_x, const uint16_t* d_gout, int B, int Sq,
+                      const float* d_lora, uint16_t* d_out, float* d_gin, float* d_grads) {
+  if (!S || !d_x || !d_gout || !d_lora || !d_out || !d_gin || !d_grads) return fail(QLS_EINVAL, "NULL argument");
+  if (layer < 0 || layer >= S->sh.c.n_layers) return fail(QLS_EINVAL, "layer out of range");
+  int rc = check_tokens(S, B, Sq);
+  if (rc) return rc;
+  const int T = B * Sq, d = S->sh.c.hidden;
+  S->ev_next = 0;
+  S->copy_ev.clear();
+  S->comp_ev.clear();
+  if (S->timing) QLS_HIP(hipEventRecord(S->step_a, S->cs));
+  if ((rc = prefetch(S, layer))) return rc;
+  cast_lora(S, d_lora);
+  const uint8_t* rec;
+  TimedEv te{};
+  if ((rc = acquire(S, layer, &rec, &te))) return rc;
+  if ((rc = fwd_layer(S, layer, rec, d_x, d_out, true, T, B, Sq))) return rc;
+  if ((rc = fwd_layer(S, layer, rec, d_x, S->at<uint16_t>(S->p.xo), true, T, B, Sq))) return rc;
+  bf16_to_f32(d_gout, S->at<float>(S->p.g), (int64_t)T * d, S->cs);
+  if ((rc = bwd_layer(S, layer, rec, d_x, d_grads, T, B, Sq))) return rc;
+  QLS_HIP(hipMemcpyAsync(d_gin, S->at<float>(S->p.g), (size_t)T * d * 4, hipMemcpyDeviceToDevice, S->cs));
+  if ((rc = release(S, layer, &te))) return rc;
+  QLS_HIP(hipGetLastError());
+  return end_step(S, nullptr, nullptr);
+}
+
+int qls_session_checkpoints(qls_session* S, const uint16_t** d_ptr, int64_t* tokens) {
+  if (!S || !d_ptr || !tokens) return fail(QLS_EINVAL, "NULL argument");
+  *d_ptr = S->ck(0);
+  *tokens = S->z.Tm;
+  return QLS_OK;
+}
+
+int qls_session_stats(qls_session* S, qls_stats* o) {
+  if (!S || !o) return fail(QLS_EINVAL, "NULL argument");
+  QLS_HIP(hipStreamSynchronize(S->cs));
+  QLS_HIP(hipStreamSynchronize(S->ps));
+  std::memset(o, 0, sizeof(*o));
+  o->steps = S->steps;
+  o->layer_loads = S->loads;
+  o->h2d_bytes = S->h2d;
+  o->ws_bytes = S->p.total;
+  if (S->timing && S->steps > 0) {
+    auto rel = [&](hipEvent_t e) { float ms = 0; (void)hipEventElapsedTime(&ms, S->step_a, e); return (double)ms; };
+    std::vector<std::pair<double, double>> comp;
+    for (auto& c : S->comp_ev) {
+      comp.push_back({rel(c.a), rel(c.b)});
+      o->compute_ms += comp.back().second - comp.back().first;
+    }
+    for (auto& c : S->copy_ev) {
+      const double a = rel(c.a), b = rel(c.b);
+      o->copy_ms += b - a;
+      for (auto& k : comp) o->overlap_ms += std::max(0.0, std::min(b, k.second) - std::max(a, k.first));
+    }
+    o->step_ms = rel(S->step_b);
+  }
+  return QLS_OK;
+}
+
+int qls_session_reset_stats(qls_session* S) {
+  if (!S) return fail(QLS_EINVAL, "NULL argument");
+  S->steps = S->loads = S->h2d = 0;
+  return QLS_OK;
+}
+
+int qls_debug_set(qls_session* S, uint32_t flags, int delay_us) {
+  if (!S) return fail(QLS_EINVAL, "NULL argument");
+  if (delay_us < 0 || delay_us > 1000000) return fail(QLS_EINVAL, "delay_us must be in [0, 1e6]");
+  S->dbg = flags;
+  S->delay_us = delay_us;
+  if (flags & (QLS_DBG_POISON_ON_RELEASE | QLS_DBG_NO_REUSE)) S->slot_layer[0] = S->slot_layer[1] = -1;
+  return QLS_OK;
+}
+
+}  // extern "C"

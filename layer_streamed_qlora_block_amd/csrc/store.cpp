@@ -1,0 +1,249 @@
+// Pinned NF4 host store: one record per decoder layer.
+//
+// The frozen decoder stack lives in page-locked host memory so the layer
+// copies can run asynchronously next to compute (page "Can You Fine-Tune Llama
+// 3.1 8B on a 4GB GPU? ...", sections "How Soup's layer streaming actually
+// works", item 2, and "Why NF4 matters so much"; page "Fine tune an 8B model on
+// a 4GB laptop GPU (Soup setup)", section "Step 2, train": the base store is
+// pinned in RAM across 32 layers).
+#include <algorithm>
+#include <cmath>
+#include <cstring>
+#include <thread>
+
+#include "internal.h"
+
+struct qls_store {
+  Shape sh;
+  RecordLayout lay;
+  uint8_t* host = nullptr;          // n_layers * lay.bytes, hipHostMalloc
+  std::vector<char> ready;
+};
+
+bool make_shape(const qls_model_cfg* c, Shape* o, std::string* why) {
+  auto bad = [&](const char* m) { if (why) *why = m; return false; };
+  if (!c) return bad("cfg is NULL");
+  if (c->n_layers <= 0 || c->hidden <= 0 || c->n_heads <= 0 || c->n_kv_heads <= 0 ||
+      c->head_dim <= 0 || c->intermediate <= 0 || c->vocab <= 0 || c->lora_r <= 0)
+    return bad("all sizes must be positive");
+  if (c->n_heads % c->n_kv_heads) return bad("n_heads must be a multiple of n_kv_heads");
+  if (!(c->rms_eps > 0) || !(c->rope_theta > 0) || !(c->lora_alpha > 0))
+    return bad("rms_eps, rope_theta and lora_alpha must be positive");
+  o->c = *c;
+  o->qd = c->n_heads * c->head_dim;
+  o->kvd = c->n_kv_heads * c->head_dim;
+  o->nqkv = o->qd + 2 * o->kvd;
+  const int d = c->hidden, I = c->intermediate;
+  o->mod[QLS_Q] = {o->qd, d};
+  o->mod[QLS_K] = {o->kvd, d};
+  o->mod[QLS_V] = {o->kvd, d};
+  o->mod[QLS_O] = {d, o->qd};
+  o->mod[QLS_GATE] = {I, d};
+  o->mod[QLS_UP] = {I, d};
+  o->mod[QLS_DOWN] = {d, I};
+  for (int m = 0; m < QLS_NMOD; ++m) {
+    o->numel[m] = (int64_t)o->mod[m].out * o->mod[m].in;
+    if (o->numel[m] % 64) return bad("every linear's numel must be a multiple of 64");
+  }
+  o->s = c->lora_alpha / (float)c->lora_r;
+  return true;
+}
+
+RecordLayout record_layout(const Shape& sh) {
+  RecordLayout L{};
+  int64_t off = 0;
+  for (int m = 0; m < QLS_NMOD; ++m) { L.code_off[m] = off; off += sh.numel[m] / 2; }
+  off = align_up(off, 256);
+  for (int m = 0; m < QLS_NMOD; ++m) { L.absmax_off[m] = off; off += sh.numel[m] / 64 * 4; }
+  off = align_up(off, 256);
+  L.norm_attn_off = off; off = align_up(off + 2LL * sh.c.hidden, 256);
+  L.norm_mlp_off = off; off = align_up(off + 2LL * sh.c.hidden, 256);
+  L.bytes = off;
+  return L;
+}
+
+LoraLayout lora_layout(const Shape& sh) {
+  LoraLayout L{};
+  int64_t off = 0;
+  const int r = sh.c.lora_r;
+  for (int m = 0; m < QLS_NMOD; ++m) {
+    L.a_off[m] = off; off += (int64_t)r * sh.mod[m].in;
+    L.b_off[m] = off; off += (int64_t)sh.mod[m].out * r;
+  }
+  L.per_layer = off;
+  return L;
+}
+
+// ---------------------------------------------------------------- quantiser
+// code = argmin_j |w/a - cb[j]| with the division, subtraction and comparison
+// in float32 (ties to the lower index); an all-zero block is code 7, absmax 0.
+static void quantize_blocks(const float* w, int64_t b0, int64_t b1, uint8_t* codes, float* absmax,
+                            const float* cb) {
+  for (int64_t b = b0; b < b1; ++b) {
+    const float* x = w + b * 64;
+    float a = 0.f;
+    for (int e = 0; e < 64; ++e) a = std::max(a, std::fabs(x[e]));
+    absmax[b] = a;
+    uint8_t* out = codes + b * 32;
+    if (a == 0.f) {
+      std::memset(out, 0x77, 32);
+      continue;
+    }
+    uint8_t idx[64];
+    for (int e = 0; e < 64; ++e) {
+      const float n = x[e] / a;   // one IEEE float32 division (no fast-math)
+      int best = 0;
+      float bd = std::fabs(n - cb[0]);
+      for (int j = 1; j < 16; ++j) {
+        const float dj = std::fabs(n - cb[j]);
+        if (dj < bd) { bd = dj; best = j; }
+      }
+      idx[e] = (uint8_t)best;
+    }
+    for (int k = 0; k < 32; ++k) out[k] = (uint8_t)((idx[2 * k] << 4) | idx[2 * k + 1]);
+  }
+}
+
+void nf4_quantize_host(const float* w, int64_t n, uint8_t* codes, float* absmax, int n_threads) {
+  float cb[16];
+  nf4_codebook_host(cb);
+  const int64_t nb = n / 64;
+  int nt = n_threads > 0 ? n_threads : (int)std::max(1u, std::thread::hardware_concurrency());
+  nt = (int)std::min<int64_t>(nt, std::max<int64_t>(1, nb / 1024));
+  if (nt <= 1) { quantize_blocks(w, 0, nb, codes, absmax, cb); return; }
+  std::vector<std::thread> th;
+  for (int i = 0; i < nt; ++i) {
+    const int64_t b0 = nb * i / nt, b1 = nb * (i + 1) / nt;
+    th.emplace_back(quantize_blocks, w, b0, b1, codes, absmax, cb);
+  }
+  for (auto& x : th) x.join();
+}
+
+// ---------------------------------------------------------------- C ABI
+extern "C" {
+
+int64_t qls_layer_record_bytes(const qls_model_cfg* cfg) {
+  Shape sh;
+  std::string why;
+  if (!make_shape(cfg, &sh, &why)) return fail(QLS_EINVAL, why);
+  return record_layout(sh).bytes;
+}
+
+int64_t qls_lora_numel(const qls_model_cfg* cfg) {
+  Shape sh;
+  std::string why;
+  if (!make_shape(cfg, &sh, &why)) return fail(QLS_EINVAL, why);
+  return lora_layout(sh).per_layer * cfg->n_layers;
+}
+
+int qls_nf4_codebook(float out[16]) {
+  if (!out) return fail(QLS_EINVAL, "out is NULL");
+  nf4_codebook_host(out);
+  return QLS_OK;
+}
+
+int qls_nf4_quantize(const float* w, int64_t n, uint8_t* codes, float* absmax, int n_threads) {
+  if (!w || !codes || !absmax) return fail(QLS_EINVAL, "NULL buffer");
+  if (n < 0 || n % 64) return fail(QLS_EINVAL, "n must be a non-negative multiple of 64");
+  nf4_quantize_host(w, n, codes, absmax, n_threads);
+  return QLS_OK;
+}
+
+int qls_store_create(const qls_model_cfg* cfg, uint64_t max_pinned_bytes, qls_store** out) {
+  if (!out) return fail(QLS_EINVAL, "out is NULL");
+  *out = nullptr;
+  Shape sh;
+  std::string why;
+  if (!make_shape(cfg, &sh, &why)) return fail(QLS_EINVAL, why);
+  auto* st = new (std::nothrow) qls_store;
+  if (!st) return fail(QLS_ENOMEM, "host allocation failed");
+  st->sh = sh;
+  st->lay = record_layout(sh);
+  const uint64_t total = (uint64_t)st->lay.bytes * (uint64_t)cfg->n_layers;
+  if (max_pinned_bytes && total > max_pinned_bytes) {
+    delete st;
+    return fail(QLS_ENOPIN, "store of " + std::to_string(total) + " bytes exceeds the pinned cap of " +
+                                std::to_string(max_pinned_bytes));
+  }
+  hipError_t e = hipHostMalloc(reinterpret_cast<void**>(&st->host), total, hipHostMallocDefault);
+  if (e != hipSuccess || !st->host) {
+    delete st;
+    return fail(QLS_ENOPIN, std::string("hipHostMalloc of the store failed: ") + hipGetErrorString(e));
+  }
+  st->ready.assign(cfg->n_layers, 0);
+  *out = st;
+  return QLS_OK;
+}
+
+static int set_norms(qls_store* st, int layer, const uint16_t* na, const uint16_t* nm) {
+  uint8_t* rec = st->host + (int64_t)layer * st->lay.bytes;
+  std::memcpy(rec + st->lay.norm_attn_off, na, 2 * (size_t)st->sh.c.hidden);
+  std::memcpy(rec + st->lay.norm_mlp_off, nm, 2 * (size_t)st->sh.c.hidden);
+  return QLS_OK;
+}
+
+int qls_store_set_layer_fp32(qls_store* st, int layer, const float* const w[QLS_NMOD],
+                             const uint16_t* na, const uint16_t* nm, int n_threads) {
+  if (!st || !w || !na || !nm) return fail(QLS_EINVAL, "NULL argument");
+  if (layer < 0 || layer >= st->sh.c.n_layers) return fail(QLS_EINVAL, "layer out of range");
+  for (int m = 0; m < QLS_NMOD; ++m)
+    if (!w[m]) return fail(QLS_EINVAL, "NULL weight");
+  uint8_t* rec = st->host + (int64_t)layer * st->lay.bytes;
+  for (int m = 0; m < QLS_NMOD; ++m)
+    nf4_quantize_host(w[m], st->sh.numel[m], rec + st->lay.code_off[m],
+                      reinterpret_cast<float*>(rec + st->lay.absmax_off[m]), n_threads);
+  set_norms(st, layer, na, nm);
+  st->ready[layer] = 1;
+  return QLS_OK;
+}
+
+int qls_store_set_layer_nf4(qls_store* st, int layer, const uint8_t* const codes[QLS_NMOD],
+                            const float* const absmax[QLS_NMOD], const uint16_t* na,
+                            const uint16_t* nm) {
+  if (!st || !codes || !absmax || !na || !nm) return fail(QLS_EINVAL, "NULL argument");
+  if (layer < 0 || layer >= st->sh.c.n_layers) return fail(QLS_EINVAL, "layer out of range");
+  uint8_t* rec = st->host + (int64_t)layer * st->lay.bytes;
+  for (int m = 0; m < QLS_NMOD; ++m) {
+    if (!codes[m] || !absmax[m]) return fail(QLS_EINVAL, "NULL module buffer");
+    std::memcpy(rec + st->lay.code_off[m], codes[m], st->sh.numel[m] / 2);
+    std::memcpy(rec + st->lay.absmax_off[m], absmax[m], st->sh.numel[m] / 64 * 4);
+  }
+  set_norms(st, layer, na, nm);
+  st->ready[layer] = 1;
+  return QLS_OK;
+}
+
+int qls_store_layer_view(const qls_store* st, int layer, qls_layer_view* out) {
+  if (!st || !out) return fail(QLS_EINVAL, "NULL argument");
+  if (layer < 0 || layer >= st->sh.c.n_layers) return fail(QLS_EINVAL, "layer out of range");
+  const uint8_t* rec = st->host + (int64_t)layer * st->lay.bytes;
+  for (int m = 0; m < QLS_NMOD; ++m) {
+    out->codes[m] = rec + st->lay.code_off[m];
+    out->absmax[m] = reinterpret_cast<const float*>(rec + st->lay.absmax_off[m]);
+  }
+  out->norm_attn = reinterpret_cast<const uint16_t*>(rec + st->lay.norm_attn_off);
+  out->norm_mlp = reinterpret_cast<const uint16_t*>(rec + st->lay.norm_mlp_off);
+  out->record = rec;
+  out->record_bytes = st->lay.bytes;
+  return QLS_OK;
+}
+
+void qls_store_destroy(qls_store* st) {
+  if (!st) return;
+  if (st->host) (void)hipHostFree(st->host);
+  delete st;
+}
+
+}  // extern "C"
+
+// Accessors for the session code.
+const Shape& store_shape(const qls_store* st) { return st->sh; }
+const RecordLayout& store_layout(const qls_store* st) { return st->lay; }
+const uint8_t* store_record(const qls_store* st, int layer) {
+  return st->host + (int64_t)layer * st->lay.bytes;
+}
+bool store_complete(const qls_store* st, int* missing) {
+  for (int l = 0; l < (int)st->ready.size(); ++l)
+    if (!st->ready[l]) { if (missing) *missing = l; return false; }
+  return true;
+}

@@ -205,6 +205,20 @@ def lora_linear(P, x, W, ab, s, residual=None):
     return P.rb(acc), u
 
 
+def lora_linear_bwd(P, x, u, W, ab, s, dy):
+    """Backward of y = x W^T + s u B^T, u = x A^T, for an upstream dy (bf16 values).
+
+    du = bf16(s dy B);  dA = du^T x;  dB = s dy^T u;  dx = dy W + du A.
+    Returns (dx, (dA, dB)) with (dA, dB) None when the adapters are disabled."""
+    dx = dy @ P.c(W)
+    if ab is None:
+        return dx, None
+    A, Bm = ab
+    s = P.c(s)
+    du = P.rb(s * (dy @ P.rb(Bm)))
+    return dx + du @ P.rb(A), (du.T @ x, s * (dy.T @ u))
+
+
 # ------------------------------------------------------------------ layer
 def layer_forward(cfg, P, x, lw, lora_l, B, S, tabs):
     """One decoder layer.  x [T, d] (bf16 values) -> (out [T, d], cache)."""
@@ -246,12 +260,9 @@ def layer_backward(cfg, P, c, g_out, lw, lora_l, B, S, tabs):
     grads = {}
 
     def lin_bwd(name, x_in, u, dy):
-        dx = dy @ P.c(W[name])
-        if lora_l is not None:
-            A, Bm = lora_l[name]
-            du = P.rb(s * (dy @ P.rb(Bm)))
-            grads[name] = (du.T @ x_in, s * (dy.T @ u))
-            dx = dx + du @ P.rb(A)
+        dx, g = lora_linear_bwd(P, x_in, u, W[name], None if lora_l is None else lora_l[name], s, dy)
+        if g is not None:
+            grads[name] = g
         return dx
 
     dy_down = P.rb(g_out)

@@ -1,0 +1,38 @@
+"""Helpers for the GPU parity tests (all run through the C ABI)."""
+import numpy as np
+import torch
+
+
+def dev(a, dtype=None):
+    t = torch.from_numpy(np.ascontiguousarray(a)) if isinstance(a, np.ndarray) else a
+    if dtype is not None:
+        t = t.to(dtype)
+    return t.cuda()
+
+
+def bits(t: torch.Tensor) -> np.ndarray:
+    """Raw bits of a bf16 / fp32 tensor as unsigned ints (for bitwise compares)."""
+    t = t.detach().contiguous().cpu()
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).numpy().view(np.uint16)
+    if t.dtype == torch.float32:
+        return t.view(torch.int32).numpy().view(np.uint32)
+    return t.numpy()
+
+
+def f32(t: torch.Tensor) -> np.ndarray:
+    return t.detach().float().cpu().numpy()
+
+
+def same_values(a, b):
+    """Bitwise equality except that +0 and -0 compare equal."""
+    a = np.asarray(a)
+    b = np.asarray(b)
+    return a.shape == b.shape and bool(np.all((a == b) | (np.isnan(a) & np.isnan(b))))
+
+
+def report(name, got, want):
+    from tests.helpers import cosine, rel_l2
+    r, c = rel_l2(got, want), cosine(got, want)
+    print(f"{name}: rel_l2={r:.3e} cos={c:.7f}", flush=True)
+    return r, c
