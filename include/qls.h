@@ -124,6 +124,14 @@ typedef struct qls_stats {
   double overlap_ms;      /* copy time overlapped by layer compute (timing on) */
   double step_ms;         /* wall time of the last step on the GPU (timing on) */
   int64_t ws_bytes;       /* workspace bytes the session uses */
+  /* Dequant-GEMM launches of the steps since the last reset (timing on):
+   * forward Y = X W^T (+ LoRA) and transposed dX = dY W (+ LoRA), each with
+   * the summed launch time (hipEvents on the compute stream) and the summed
+   * algorithmic work 2*T*N*K (+ 2*T*N*r for the LoRA term) in GFLOP. */
+  double dq_fwd_ms, dq_fwd_gflop;
+  int64_t dq_fwd_launches;
+  double dq_dx_ms, dq_dx_gflop;
+  int64_t dq_dx_launches;
 } qls_stats;
 
 typedef struct qls_store qls_store;

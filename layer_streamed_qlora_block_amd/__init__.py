@@ -55,7 +55,9 @@ class LayerView(C.Structure):
 class Stats(C.Structure):
     _fields_ = [("steps", C.c_int64), ("layer_loads", C.c_int64), ("h2d_bytes", C.c_int64),
                 ("copy_ms", C.c_double), ("compute_ms", C.c_double), ("overlap_ms", C.c_double),
-                ("step_ms", C.c_double), ("ws_bytes", C.c_int64)]
+                ("step_ms", C.c_double), ("ws_bytes", C.c_int64),
+                ("dq_fwd_ms", C.c_double), ("dq_fwd_gflop", C.c_double), ("dq_fwd_launches", C.c_int64),
+                ("dq_dx_ms", C.c_double), ("dq_dx_gflop", C.c_double), ("dq_dx_launches", C.c_int64)]
 
     def as_dict(self):
         return {k: getattr(self, k) for k, _ in self._fields_}

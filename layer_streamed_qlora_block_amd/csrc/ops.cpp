@@ -85,7 +85,10 @@ int linear_fwd(const LinearFwd& f, hipStream_t st) {
     for (int i = 0; i < f.nmod; ++i) { g.mod_end[i] = f.mod_end[i]; g.modB[i] = f.Bm[i]; }
     g.s2 = f.s;
   }
-  return gemm_launch(g, A_ROW, B_NF4_NT, EPI_BF16, 128, st);
+  if (f.ev0) (void)hipEventRecord(f.ev0, st);
+  const int rc = gemm_launch(g, A_ROW, B_NF4_NT, EPI_BF16, 128, st);
+  if (f.ev1) (void)hipEventRecord(f.ev1, st);
+  return rc;
 }
 
 int linear_dx(const LinearDx& d, hipStream_t st) {
@@ -102,5 +105,8 @@ int linear_dx(const LinearDx& d, hipStream_t st) {
     g.K2 = d.rc;
   }
   g.gu = d.gu; g.ldgu = d.ldgu; g.I = d.I;
-  return gemm_launch(g, A_ROW, B_NF4_NN, d.epi, 128, st);
+  if (d.ev0) (void)hipEventRecord(d.ev0, st);
+  const int rc = gemm_launch(g, A_ROW, B_NF4_NN, d.epi, 128, st);
+  if (d.ev1) (void)hipEventRecord(d.ev1, st);
+  return rc;
 }

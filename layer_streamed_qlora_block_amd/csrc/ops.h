@@ -18,6 +18,7 @@ struct LinearFwd {
   uint16_t* y; int64_t ldy;
   uint16_t* u;                  // U_cat [T, nmod*r]
   float* ws;                    // split-K partials
+  hipEvent_t ev0, ev1;          // optional: recorded around the dequant-GEMM launch
 };
 int linear_fwd(const LinearFwd& f, hipStream_t st);
 
@@ -30,6 +31,7 @@ struct LinearDx {
   const uint16_t* du; int64_t lddu; const uint16_t* Acat; int rc;   // Acat [rc, Nout]
   void* out; int64_t ldo; int epi;    // EPI_F32 / EPI_BF16 / EPI_SWIGLU_BWD
   const uint16_t* gu; int64_t ldgu; int I;
+  hipEvent_t ev0, ev1;          // optional: recorded around the launch
 };
 int linear_dx(const LinearDx& d, hipStream_t st);
 

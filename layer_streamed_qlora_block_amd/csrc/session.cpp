@@ -127,6 +127,7 @@ bool check_run(const Shape& sh, const qls_run_cfg* run, std::string* why) {
 }
 
 struct TimedEv { hipEvent_t a, b; };
+struct TimedK { hipEvent_t a, b; double gflop; };
 
 }  // namespace
 
@@ -153,8 +154,21 @@ struct qls_session {
   bool timing = false;
   std::vector<hipEvent_t> ev_pool;
   size_t ev_next = 0;
-  std::vector<TimedEv> copy_ev, comp_ev;
-  hipEvent_t step_a = nullptr, step_b = nullptr;
+  // Timing mode: events accumulate over the steps since the last reset and are
+  // folded into sums when the stats are read.
+  std::vector<TimedEv> copy_ev, comp_ev, step_ev;
+  std::vector<TimedK> kf_ev, kd_ev;
+  void clear_timing() { ev_next = 0; copy_ev.clear(); comp_ev.clear(); step_ev.clear(); kf_ev.clear(); kd_ev.clear(); }
+  void tag_fwd(LinearFwd& f, bool lora) {
+    if (!timing) return;
+    f.ev0 = next_ev(); f.ev1 = next_ev();
+    kf_ev.push_back({f.ev0, f.ev1, 2e-9 * f.T * (double)f.N * (f.K + (lora ? f.r : 0))});
+  }
+  void tag_dx(LinearDx& d) {
+    if (!timing) return;
+    d.ev0 = next_ev(); d.ev1 = next_ev();
+    kd_ev.push_back({d.ev0, d.ev1, 2e-9 * d.T * (double)d.Nout * (d.Kc + d.rc)});
+  }
 
   template <class T> T* at(int64_t off) const { return reinterpret_cast<T*>(ws + off); }
   uint16_t* ck(int l) const { return at<uint16_t>(p.ckpt) + (int64_t)l * z.Tm * sh.c.hidden; }
@@ -272,6 +286,7 @@ int fwd_layer(qls_session* S, int l, const uint8_t* rec, const uint16_t* x, uint
   f.nmod = 3; f.mod_end[0] = sh.qd; f.mod_end[1] = sh.qd + sh.kvd; f.mod_end[2] = sh.nqkv;
   f.Bm[0] = lw + S->wb[QLS_Q]; f.Bm[1] = lw + S->wb[QLS_K]; f.Bm[2] = lw + S->wb[QLS_V];
   f.s = sh.s; f.y = qkv; f.ldy = sh.nqkv; f.u = S->at<uint16_t>(S->p.uqkv); f.ws = part;
+  S->tag_fwd(f, lora);
   QLS_RC(linear_fwd(f, st));
   rope_fwd(qkv, sh.nqkv, T, Sq, sh.c.n_heads, sh.c.n_kv_heads, sh.c.head_dim, S->at<float>(S->p.rope), st);
   AttnArgs aa{};
@@ -287,6 +302,7 @@ int fwd_layer(qls_session* S, int l, const uint8_t* rec, const uint16_t* x, uint
   f.A = lora ? lw + S->wa[QLS_O] : nullptr;
   f.nmod = 1; f.mod_end[0] = d; f.Bm[0] = lw + S->wb[QLS_O];
   f.s = sh.s; f.res = x; f.ldres = d; f.y = h; f.ldy = d; f.u = S->at<uint16_t>(S->p.uo); f.ws = part;
+  S->tag_fwd(f, lora);
   QLS_RC(linear_fwd(f, st));
 
   rmsnorm_fwd(h, w.nm, sh.c.rms_eps, n2, T, d, st);
@@ -297,6 +313,7 @@ int fwd_layer(qls_session* S, int l, const uint8_t* rec, const uint16_t* x, uint
   f.nmod = 2; f.mod_end[0] = I; f.mod_end[1] = 2 * I;
   f.Bm[0] = lw + S->wb[QLS_GATE]; f.Bm[1] = lw + S->wb[QLS_UP];
   f.s = sh.s; f.y = gu; f.ldy = 2 * I; f.u = S->at<uint16_t>(S->p.ugu); f.ws = part;
+  S->tag_fwd(f, lora);
   QLS_RC(linear_fwd(f, st));
   swiglu_fwd(gu, a, T, I, st);
 
@@ -306,6 +323,7 @@ int fwd_layer(qls_session* S, int l, const uint8_t* rec, const uint16_t* x, uint
   f.A = lora ? lw + S->wa[QLS_DOWN] : nullptr;
   f.nmod = 1; f.mod_end[0] = d; f.Bm[0] = lw + S->wb[QLS_DOWN];
   f.s = sh.s; f.res = h; f.ldres = d; f.y = xout; f.ldy = d; f.u = S->at<uint16_t>(S->p.udown); f.ws = part;
+  S->tag_fwd(f, lora);
   QLS_RC(linear_fwd(f, st));
   return QLS_OK;
 }
@@ -348,6 +366,7 @@ int bwd_layer(qls_session* S, int l, const uint8_t* rec, const uint16_t* x, floa
   x1.du = du; x1.lddu = r; x1.Acat = lw + S->wa[QLS_DOWN]; x1.rc = r;
   x1.out = dgu; x1.ldo = 2 * I; x1.epi = EPI_SWIGLU_BWD;
   x1.gu = S->at<uint16_t>(S->p.gu); x1.ldgu = 2 * I; x1.I = I;
+  S->tag_dx(x1);
   QLS_RC(linear_dx(x1, st));
 
   // ---- gate / up
@@ -362,6 +381,7 @@ int bwd_layer(qls_session* S, int l, const uint8_t* rec, const uint16_t* x, floa
   x2.codes = w.code[QLS_GATE]; x2.absmax = w.amax[QLS_GATE]; x2.ldq = d;
   x2.du = du; x2.lddu = 2 * r; x2.Acat = lw + S->wa[QLS_GATE]; x2.rc = 2 * r;
   x2.out = dn; x2.ldo = d; x2.epi = EPI_F32;
+  S->tag_dx(x2);
   QLS_RC(linear_dx(x2, st));
   rmsnorm_bwd(h, w.nm, sh.c.rms_eps, dn, g, dh, dyb, T, d, st);
 
@@ -374,6 +394,7 @@ int bwd_layer(qls_session* S, int l, const uint8_t* rec, const uint16_t* x, floa
   x3.codes = w.code[QLS_O]; x3.absmax = w.amax[QLS_O]; x3.ldq = sh.qd;
   x3.du = du; x3.lddu = r; x3.Acat = lw + S->wa[QLS_O]; x3.rc = r;
   x3.out = S->at<uint16_t>(S->p.dattn); x3.ldo = sh.qd; x3.epi = EPI_BF16;
+  S->tag_dx(x3);
   QLS_RC(linear_dx(x3, st));
 
   // ---- attention + RoPE
@@ -404,6 +425,7 @@ int bwd_layer(qls_session* S, int l, const uint8_t* rec, const uint16_t* x, floa
   x4.codes = w.code[QLS_Q]; x4.absmax = w.amax[QLS_Q]; x4.ldq = d;
   x4.du = du; x4.lddu = 3 * r; x4.Acat = lw + S->wa[QLS_Q]; x4.rc = 3 * r;
   x4.out = dn; x4.ldo = d; x4.epi = EPI_F32;
+  S->tag_dx(x4);
   QLS_RC(linear_dx(x4, st));
   rmsnorm_bwd(x, w.na, sh.c.rms_eps, dn, dh, g, nullptr, T, d, st);
   return QLS_OK;
@@ -477,10 +499,10 @@ int cast_lora(qls_session* S, const float* d_lora) {
 }
 
 int begin_step(qls_session* S) {
-  S->ev_next = 0;
-  S->copy_ev.clear();
-  S->comp_ev.clear();
-  if (S->timing) QLS_HIP(hipEventRecord(S->step_a, S->cs));
+  if (S->timing) {
+    S->step_ev.push_back({S->next_ev(), S->next_ev()});
+    QLS_HIP(hipEventRecord(S->step_ev.back().a, S->cs));
+  }
   QLS_HIP(hipMemsetAsync(S->at<int>(S->p.scal), 0, 64, S->cs));
   int rc = prefetch(S, 0);
   if (!rc && S->sh.c.n_layers > 1) rc = prefetch(S, 1);
@@ -489,7 +511,7 @@ int begin_step(qls_session* S) {
 
 int end_step(qls_session* S, float* h_loss, const float* d_loss) {
   S->steps += 1;
-  if (S->timing) QLS_HIP(hipEventRecord(S->step_b, S->cs));
+  if (S->timing) QLS_HIP(hipEventRecord(S->step_ev.back().b, S->cs));
   if (h_loss) {
     QLS_HIP(hipStreamSynchronize(S->cs));
     int bad = 0;
@@ -623,8 +645,6 @@ int qls_session_create(const qls_store* st, const qls_run_cfg* run, void* d_ws, 
     if (hipEventRecord(S->released[i], S->cs) != hipSuccess)
       return cleanup(fail(QLS_EHIP, "hipEventRecord failed"));
   }
-  if (hipEventCreate(&S->step_a) != hipSuccess || hipEventCreate(&S->step_b) != hipSuccess)
-    return cleanup(fail(QLS_EHIP, "hipEventCreate failed"));
   std::vector<float> tab;
   fill_rope_table(sh, run->max_seq, &tab);
   hipError_t e = hipMemcpy(S->at<float>(S->p.rope), tab.data(), tab.size() * 4, hipMemcpyHostToDevice);
@@ -648,8 +668,6 @@ void qls_session_destroy(qls_session* S) {
     if (S->copied[i]) (void)hipEventDestroy(S->copied[i]);
     if (S->released[i]) (void)hipEventDestroy(S->released[i]);
   }
-  if (S->step_a) (void)hipEventDestroy(S->step_a);
-  if (S->step_b) (void)hipEventDestroy(S->step_b);
   for (auto e : S->ev_pool) (void)hipEventDestroy(e);
   delete S;
 }
@@ -733,10 +751,10 @@ int qls_layer_fwd_bwd(qls_session* S, int layer, const uint16_t* d_x, const uint
   int rc = check_tokens(S, B, Sq);
   if (rc) return rc;
   const int T = B * Sq, d = S->sh.c.hidden;
-  S->ev_next = 0;
-  S->copy_ev.clear();
-  S->comp_ev.clear();
-  if (S->timing) QLS_HIP(hipEventRecord(S->step_a, S->cs));
+  if (S->timing) {
+    S->step_ev.push_back({S->next_ev(), S->next_ev()});
+    QLS_HIP(hipEventRecord(S->step_ev.back().a, S->cs));
+  }
   if ((rc = prefetch(S, layer))) return rc;
   cast_lora(S, d_lora);
   const uint8_t* rec;
@@ -768,8 +786,10 @@ int qls_session_stats(qls_session* S, qls_stats* o) {
   o->layer_loads = S->loads;
   o->h2d_bytes = S->h2d;
   o->ws_bytes = S->p.total;
-  if (S->timing && S->steps > 0) {
-    auto rel = [&](hipEvent_t e) { float ms = 0; (void)hipEventElapsedTime(&ms, S->step_a, e); return (double)ms; };
+  if (S->timing && !S->step_ev.empty()) {
+    hipEvent_t t0 = S->step_ev.front().a;
+    auto rel = [&](hipEvent_t e) { float ms = 0; (void)hipEventElapsedTime(&ms, t0, e); return (double)ms; };
+    auto span = [&](hipEvent_t a, hipEvent_t b) { float ms = 0; (void)hipEventElapsedTime(&ms, a, b); return (double)ms; };
     std::vector<std::pair<double, double>> comp;
     for (auto& c : S->comp_ev) {
       comp.push_back({rel(c.a), rel(c.b)});
@@ -780,14 +800,22 @@ int qls_session_stats(qls_session* S, qls_stats* o) {
       o->copy_ms += b - a;
       for (auto& k : comp) o->overlap_ms += std::max(0.0, std::min(b, k.second) - std::max(a, k.first));
     }
-    o->step_ms = rel(S->step_b);
+    for (auto& e : S->step_ev) o->step_ms += span(e.a, e.b);
+    o->step_ms /= (double)S->step_ev.size();
+    for (auto& k : S->kf_ev) { o->dq_fwd_ms += span(k.a, k.b); o->dq_fwd_gflop += k.gflop; }
+    for (auto& k : S->kd_ev) { o->dq_dx_ms += span(k.a, k.b); o->dq_dx_gflop += k.gflop; }
+    o->dq_fwd_launches = (int64_t)S->kf_ev.size();
+    o->dq_dx_launches = (int64_t)S->kd_ev.size();
   }
   return QLS_OK;
 }
 
 int qls_session_reset_stats(qls_session* S) {
   if (!S) return fail(QLS_EINVAL, "NULL argument");
+  QLS_HIP(hipStreamSynchronize(S->cs));
+  QLS_HIP(hipStreamSynchronize(S->ps));
   S->steps = S->loads = S->h2d = 0;
+  S->clear_timing();
   return QLS_OK;
 }
 

@@ -12,7 +12,8 @@ and exactly what it means" (vocabulary 128256 x hidden 4096 in bf16 = 2.10 GB).
 
 Distributions:
   * base weights  W[l,m] ~ N(0, 0.02) float32, generator seed 1000 + 10*l + m
-  * embedding / LM head ~ N(0, 0.02), seeds 11 / 12, stored bf16
+  * embedding / LM head ~ N(0, 0.02), stored bf16, drawn in chunks of 8192
+    rows with seeds 11*100000 + c / 12*100000 + c
   * RMSNorm weights: ones (or 1 + N(0, 0.1) when ``perturbed``), bf16
   * LoRA A ~ U(-1/sqrt(in), 1/sqrt(in)) (nn.Linear's Kaiming-uniform default),
     seed 2000 + 10*l + m; LoRA B ~ N(0, b_std), seed 2500 + 10*l + m (B = 0 when
@@ -110,12 +111,34 @@ def final_norm(cfg: ModelCfg, perturbed: bool = False) -> torch.Tensor:
     return to_bf16(1.0 + normal(3999, (cfg.d,), 0.1))
 
 
-def embedding(cfg: ModelCfg, std: float = 0.02) -> torch.Tensor:
-    return to_bf16(normal(11, (cfg.V, cfg.d), std))
+_VOCAB_CHUNK = 8192
 
 
-def lm_head(cfg: ModelCfg, std: float = 0.02) -> torch.Tensor:
-    return to_bf16(normal(12, (cfg.V, cfg.d), std))
+def _vocab_matrix(seed: int, cfg: ModelCfg, std: float, threads: int) -> torch.Tensor:
+    """[V, d] ~ N(0, std) drawn in row chunks of 8192, chunk c from seed*100000 + c."""
+    out = torch.empty(cfg.V, cfg.d, dtype=torch.bfloat16)
+
+    def fill(c):
+        r0 = c * _VOCAB_CHUNK
+        r1 = min(cfg.V, r0 + _VOCAB_CHUNK)
+        out[r0:r1] = to_bf16(normal(seed * 100000 + c, (r1 - r0, cfg.d), std))
+
+    n = (cfg.V + _VOCAB_CHUNK - 1) // _VOCAB_CHUNK
+    if threads <= 1:
+        for c in range(n):
+            fill(c)
+    else:
+        with _cf.ThreadPoolExecutor(threads) as ex:
+            list(ex.map(fill, range(n)))
+    return out
+
+
+def embedding(cfg: ModelCfg, std: float = 0.02, threads: int = 1) -> torch.Tensor:
+    return _vocab_matrix(11, cfg, std, threads)
+
+
+def lm_head(cfg: ModelCfg, std: float = 0.02, threads: int = 1) -> torch.Tensor:
+    return _vocab_matrix(12, cfg, std, threads)
 
 
 # ---------------------------------------------------------------- LoRA
