@@ -126,8 +126,10 @@ typedef struct qls_stats {
   int64_t ws_bytes;       /* workspace bytes the session uses */
   /* Dequant-GEMM launches of the steps since the last reset (timing on):
    * forward Y = X W^T (+ LoRA) and transposed dX = dY W (+ LoRA), each with
-   * the summed launch time (hipEvents on the compute stream) and the summed
-   * algorithmic work 2*T*N*K (+ 2*T*N*r for the LoRA term) in GFLOP. */
+   * the summed duration of the GEMM kernel itself (hipEvents on the compute
+   * stream around that launch; a split-K reduce that follows it is not
+   * included) and the summed algorithmic work 2*T*N*K (+ 2*T*N*r for the LoRA
+   * term) in GFLOP. */
   double dq_fwd_ms, dq_fwd_gflop;
   int64_t dq_fwd_launches;
   double dq_dx_ms, dq_dx_gflop;

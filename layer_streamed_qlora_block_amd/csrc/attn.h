@@ -16,7 +16,9 @@ struct AttnArgs {
 int attn_fwd(const AttnArgs& a, int B, hipStream_t st);
 
 // Backward: dO and O bf16 [B*S, lddo] (o is the forward output); D float
-// [B, H, S] scratch; dq float [B*S, lddq]; dk, dv float [B*S, lddkv].
+// [B, H, S] scratch; dq float [B*S, lddq]; dk, dv float [B*S, lddkv] hold one
+// partial per QUERY head (lddkv >= H*hd): the kv head's gradient is the sum
+// of the partials of its H/KV query heads.
 struct AttnBwdArgs {
   const uint16_t* qkv; int64_t ld; int q_off, k_off, v_off;
   int S, H, KV, hd;

@@ -12,9 +12,11 @@
 // Backward (no atomics, fixed summation order):
 //   dq kernel  -- per (64 query rows, head): recompute P from the saved LSE,
 //                 dP^T = V dO^T, dS = P (dP - D), dQ = dS K / sqrt(hd).
-//   dkv kernel -- per (64 keys, kv head): loops over the query heads of the
-//                 group and the query blocks on or below the diagonal,
-//                 dV += P^T dO, dK += dS^T Q / sqrt(hd).
+//   dkv kernel -- per (64 keys, query head): loops over the query blocks on
+//                 or below the diagonal, dV_h += P^T dO, dK_h += dS^T Q /
+//                 sqrt(hd), one float partial per query head; the sum over the
+//                 heads that share a kv head is taken in head order by the
+//                 RoPE-backward kernel that consumes dK and dV.
 //   D = rowsum(dO o) comes from a small preprocessing kernel.
 #include "common.h"
 #include "attn.h"
@@ -289,8 +291,8 @@ __global__ void __launch_bounds__(NT) attn_dkv_k(AttnBwdArgs a) {
   __shared__ float sL[BQ], sD[BQ];
   const int nqb = (a.S + BQ - 1) / BQ;
   const int kb = (int)blockIdx.x;
-  const int g = blockIdx.y, b = blockIdx.z;
-  const int grp = a.H / a.KV;
+  const int h = blockIdx.y, b = blockIdx.z;
+  const int g = h / (a.H / a.KV);
   const int t = threadIdx.x, lane = t & 63, w = t >> 6, g4 = lane >> 4, c16 = lane & 15;
   const int k0 = kb * BQ;
   const int myk = k0 + 16 * w + c16;
@@ -309,8 +311,7 @@ __global__ void __launch_bounds__(NT) attn_dkv_k(AttnBwdArgs a) {
 #pragma unroll
   for (int i = 0; i < HD / 16; ++i) { dk[i] = f32x4{0, 0, 0, 0}; dv[i] = f32x4{0, 0, 0, 0}; }
 
-  for (int hh = 0; hh < grp; ++hh) {
-    const int h = g * grp + hh;
+  {
     const uint16_t* Q = a.qkv + tb * a.ld + a.q_off + (int64_t)h * HD;
     const uint16_t* dO = a.dO + tb * a.lddo + (int64_t)h * HD;
     for (int qb = kb; qb < nqb; ++qb) {
@@ -362,13 +363,13 @@ __global__ void __launch_bounds__(NT) attn_dkv_k(AttnBwdArgs a) {
       __syncthreads();
     }
   }
-  // dk[hb][i] = dK[key = k0 + 16w + 4g4 + i][16hb + c16]
+  // dk[hb][i] = this query head's share of dK[key = k0 + 16w + 4g4 + i][16hb + c16]
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int key = k0 + 16 * w + 4 * g4 + i;
     if (key >= a.S) continue;
-    float* dkr = a.dk + (tb + key) * a.lddkv + (int64_t)g * HD;
-    float* dvr = a.dv + (tb + key) * a.lddkv + (int64_t)g * HD;
+    float* dkr = a.dk + (tb + key) * a.lddkv + (int64_t)h * HD;
+    float* dvr = a.dv + (tb + key) * a.lddkv + (int64_t)h * HD;
 #pragma unroll
     for (int hb = 0; hb < HD / 16; ++hb) {
       dkr[16 * hb + c16] = dk[hb][i] * a.scale;
@@ -390,7 +391,7 @@ int attn_fwd(const AttnArgs& a, int B, hipStream_t st) {
 int attn_bwd(const AttnBwdArgs& a, int B, hipStream_t st) {
   const int T = B * a.S;
   const int64_t waves = (int64_t)T * a.H;
-  const dim3 gq((a.S + BQ - 1) / BQ, a.H, B), gk((a.S + BQ - 1) / BQ, a.KV, B);
+  const dim3 gq((a.S + BQ - 1) / BQ, a.H, B), gk((a.S + BQ - 1) / BQ, a.H, B);
   if (a.hd == 128) {
     hipLaunchKernelGGL(attn_pre_k<128>, dim3((unsigned)ceil_div64(waves * 64, 256)), dim3(256), 0, st,
                        a.dO, a.O, a.lddo, a.S, a.H, T, a.D);

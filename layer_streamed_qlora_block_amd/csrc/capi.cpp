@@ -81,7 +81,7 @@ int qls_linear_bwd(const uint8_t* codes, const float* absmax, int N, int K, cons
   d.T = T; d.Kc = N; d.Nout = K;
   d.dy = dy; d.lddy = N; d.codes = codes; d.absmax = absmax; d.ldq = K;
   d.du = du; d.lddu = r; d.Acat = A; d.rc = r;
-  d.out = dx; d.ldo = K; d.epi = EPI_F32;
+  d.out = dx; d.ldo = K; d.epi = EPI_F32; d.ws = part;
   rc |= linear_dx(d, st);
   if (rc) return fail(QLS_EHIP, "kernel combination not built");
   QLS_HIP(hipGetLastError());

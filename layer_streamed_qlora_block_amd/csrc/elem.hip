@@ -108,20 +108,38 @@ __global__ void rope_bwd_k(const float* __restrict__ dq, const float* __restrict
   const int t = (int)(idx / per_t);
   const int rem = (int)(idx % per_t);
   uint16_t* o = out + (int64_t)t * ld;
+  const int grp = nh_q / nh_k;
   if (rem < (nh_q + nh_k) * h2) {
     const int head = rem / h2, j = rem % h2;
     const int pos = t % S;
     const float c = cs[((int64_t)pos * h2 + j) * 2], s = cs[((int64_t)pos * h2 + j) * 2 + 1];
-    const float* src = head < nh_q ? dq + (int64_t)t * qd + (int64_t)head * hd
-                                   : dk + (int64_t)t * kvd + (int64_t)(head - nh_q) * hd;
-    const float x1 = src[j], x2 = src[j + h2];
+    float x1, x2;
+    if (head < nh_q) {
+      const float* src = dq + (int64_t)t * qd + (int64_t)head * hd;
+      x1 = src[j];
+      x2 = src[j + h2];
+    } else {                      // kv head: sum the query-head partials in order
+      const float* src = dk + (int64_t)t * qd + (int64_t)(head - nh_q) * grp * hd;
+      x1 = 0.f;
+      x2 = 0.f;
+      for (int i = 0; i < grp; ++i) {
+        x1 += src[i * hd + j];
+        x2 += src[i * hd + j + h2];
+      }
+    }
     o[(int64_t)head * hd + j] = f2bf(x1 * c + x2 * s);
     o[(int64_t)head * hd + j + h2] = f2bf(x2 * c - x1 * s);
   } else {
-    const int e = 2 * (rem - (nh_q + nh_k) * h2);
-    const float* src = dv + (int64_t)t * kvd;
-    o[qd + kvd + e] = f2bf(src[e]);
-    o[qd + kvd + e + 1] = f2bf(src[e + 1]);
+    const int e = 2 * (rem - (nh_q + nh_k) * h2);      // element of the kv-width v row
+    const int g = e / hd, j = e % hd;
+    const float* src = dv + (int64_t)t * qd + (int64_t)g * grp * hd + j;
+    float v0 = 0.f, v1 = 0.f;
+    for (int i = 0; i < grp; ++i) {
+      v0 += src[i * hd];
+      v1 += src[i * hd + 1];
+    }
+    o[qd + kvd + e] = f2bf(v0);
+    o[qd + kvd + e + 1] = f2bf(v1);
   }
 }
 

@@ -44,6 +44,7 @@ struct GemmArgs {
   const int32_t* tgt; const float* lse; const float* roww;
   float* stats; int stats_ld; float* tgt_logit; int col0;
   int ksplit; float* partial;
+  hipEvent_t ev0, ev1;   // optional: recorded around the GEMM kernel itself (not the split-K reduce)
 };
 
 // Returns 0, or -1 when the (tile, loaders, epilogue) combination is not built.

@@ -7,14 +7,18 @@
 
 namespace {
 
-constexpr int kSkinnyTarget = 512;   // workgroups to aim for with split-K
+constexpr int kSkinnyTarget = 1024;  // workgroups to aim for with split-K
 constexpr int kMaxSplit = 64;
+constexpr int64_t kBigPartial = 512LL * 128 * 128;   // floats available to a split big GEMM
 
+// Skinny products (one side is the LoRA rank): each k-tile iteration of a
+// 64 x 64 tile is latency-bound, so the contraction is split into slices of at
+// least 4 k-tiles, up to ~1024 workgroups (partials <= 1024 * 64 * 64 floats).
 int pick_split(int M, int N, int K) {
   const int64_t tiles = cdiv(M, 64) * cdiv(N, 64);
   const int nk = (int)cdiv(K, 64);
-  int ks = (int)std::max<int64_t>(1, kSkinnyTarget / std::max<int64_t>(tiles, 1));
-  return std::max(1, std::min({ks, nk, kMaxSplit}));
+  const int64_t by_tiles = std::max<int64_t>(1, kSkinnyTarget / std::max<int64_t>(tiles, 1));
+  return (int)std::max<int64_t>(1, std::min<int64_t>({(int64_t)nk / 4, by_tiles, (int64_t)kMaxSplit}));
 }
 
 int skinny(int aload, const uint16_t* A, int64_t lda, int bload, const uint16_t* B, int64_t ldb,
@@ -25,6 +29,11 @@ int skinny(int aload, const uint16_t* A, int64_t lda, int bload, const uint16_t*
   g.A = A; g.lda = lda;
   g.Bh = B; g.ldb = ldb;
   g.ksplit = pick_split(M, N, K);
+  if (g.ksplit == 1) {
+    g.alpha = alpha;
+    g.C = C; g.ldc = ldc;
+    return gemm_launch(g, aload, bload, mode == 0 ? EPI_BF16 : EPI_F32, 64, st);
+  }
   g.partial = part;
   if (gemm_launch(g, aload, bload, EPI_PARTIAL, 64, st)) return -1;
   gemm_reduce(part, g.ksplit, M, N, alpha, mode, C, ldc, st);
@@ -33,8 +42,19 @@ int skinny(int aload, const uint16_t* A, int64_t lda, int bload, const uint16_t*
 
 }  // namespace
 
+// Split-K for the 128 x 128 GEMMs: aim for ~512 workgroups when M is small,
+// keep at least 8 k-tiles per split and the partials within kBigPartial.
+int big_split(int M, int N, int K) {
+  const int64_t tiles = cdiv(M, 128) * cdiv(N, 128);
+  if (tiles >= 384) return 1;
+  const int nk = (int)cdiv(K, 64);
+  int ks = (int)std::min<int64_t>(cdiv(512, tiles), nk / 8);
+  while (ks > 1 && (int64_t)M * N * ks > kBigPartial) --ks;
+  return std::max(1, std::min(ks, 16));
+}
+
 int64_t skinny_partial_floats(int64_t max_mn) {
-  return std::max<int64_t>(max_mn, (int64_t)kSkinnyTarget * 64 * 64);
+  return std::max<int64_t>({max_mn, (int64_t)kSkinnyTarget * 64 * 64, kBigPartial});
 }
 
 int64_t linear_ws_bytes(int T, int N, int K, int r) {
@@ -85,10 +105,11 @@ int linear_fwd(const LinearFwd& f, hipStream_t st) {
     for (int i = 0; i < f.nmod; ++i) { g.mod_end[i] = f.mod_end[i]; g.modB[i] = f.Bm[i]; }
     g.s2 = f.s;
   }
-  if (f.ev0) (void)hipEventRecord(f.ev0, st);
-  const int rc = gemm_launch(g, A_ROW, B_NF4_NT, EPI_BF16, 128, st);
-  if (f.ev1) (void)hipEventRecord(f.ev1, st);
-  return rc;
+  g.ksplit = big_split(f.T, f.N, f.K);
+  g.partial = f.ws;
+  g.ev0 = f.ev0;
+  g.ev1 = f.ev1;
+  return gemm_launch(g, A_ROW, B_NF4_NT, EPI_BF16, 128, st);
 }
 
 int linear_dx(const LinearDx& d, hipStream_t st) {
@@ -105,8 +126,11 @@ int linear_dx(const LinearDx& d, hipStream_t st) {
     g.K2 = d.rc;
   }
   g.gu = d.gu; g.ldgu = d.ldgu; g.I = d.I;
-  if (d.ev0) (void)hipEventRecord(d.ev0, st);
-  const int rc = gemm_launch(g, A_ROW, B_NF4_NN, d.epi, 128, st);
-  if (d.ev1) (void)hipEventRecord(d.ev1, st);
-  return rc;
+  if (d.ws) {
+    g.ksplit = big_split(d.T, d.Nout, d.Kc);
+    g.partial = d.ws;
+  }
+  g.ev0 = d.ev0;
+  g.ev1 = d.ev1;
+  return gemm_launch(g, A_ROW, B_NF4_NN, d.epi, 128, st);
 }

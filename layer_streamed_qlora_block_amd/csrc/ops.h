@@ -31,9 +31,13 @@ struct LinearDx {
   const uint16_t* du; int64_t lddu; const uint16_t* Acat; int rc;   // Acat [rc, Nout]
   void* out; int64_t ldo; int epi;    // EPI_F32 / EPI_BF16 / EPI_SWIGLU_BWD
   const uint16_t* gu; int64_t ldgu; int I;
+  float* ws;                    // split-K partials (nullptr: no split)
   hipEvent_t ev0, ev1;          // optional: recorded around the launch
 };
 int linear_dx(const LinearDx& d, hipStream_t st);
+// Split-K factor for a 128 x 128-tiled GEMM of M x N x K (partials fit in
+// skinny_partial_floats()).
+int big_split(int M, int N, int K);
 
 // Skinny LoRA products (split-K over the long dimension, deterministic reduce).
 // U = bf16(x A^T)                   x [T, K] (ldx), A [n, K]          -> U [T, n] (ldu)
@@ -63,6 +67,8 @@ void rmsnorm_bwd(const uint16_t* x, const uint16_t* w, float eps, const float* d
 void rope_fwd(uint16_t* qkv, int64_t ld, int T, int S, int H, int KV, int hd, const float* cs,
               hipStream_t st);
 // dq = bf16(R^-1 dq'), dk = bf16(R^-1 dk'), dv = bf16(dv) into dqkv [T, ld] (q | k | v).
+// dq [T, H*hd]; dk and dv [T, H*hd] hold per-query-head partials that are
+// summed over each kv head's group in head order.
 void rope_bwd(const float* dq, const float* dk, const float* dv, uint16_t* dqkv, int64_t ld, int T,
               int S, int H, int KV, int hd, const float* cs, hipStream_t st);
 void swiglu_fwd(const uint16_t* gu, uint16_t* a, int T, int I, hipStream_t st);

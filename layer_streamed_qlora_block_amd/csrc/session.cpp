@@ -85,8 +85,8 @@ Plan make_plan(const Shape& sh, const RecordLayout& lay, const qls_run_cfg& run,
   p.dgu = take(T * 2 * I * 2);
   p.dattn = take(T * sh.qd * 2);
   p.dqf = take(T * sh.qd * 4);
-  p.dkf = take(T * sh.kvd * 4);
-  p.dvf = take(T * sh.kvd * 4);
+  p.dkf = take(T * sh.qd * 4);    // per-query-head partials of dK and dV
+  p.dvf = take(T * sh.qd * 4);
   p.dqkv = take(T * sh.nqkv * 2);
   p.du = take(T * 3 * r * 2);
   p.xo = take(T * d * 2);
@@ -364,7 +364,7 @@ int bwd_layer(qls_session* S, int l, const uint8_t* rec, const uint16_t* x, floa
   x1.T = T; x1.Kc = d; x1.Nout = I; x1.dy = dyb; x1.lddy = d;
   x1.codes = w.code[QLS_DOWN]; x1.absmax = w.amax[QLS_DOWN]; x1.ldq = I;
   x1.du = du; x1.lddu = r; x1.Acat = lw + S->wa[QLS_DOWN]; x1.rc = r;
-  x1.out = dgu; x1.ldo = 2 * I; x1.epi = EPI_SWIGLU_BWD;
+  x1.out = dgu; x1.ldo = 2 * I; x1.epi = EPI_SWIGLU_BWD; x1.ws = part;
   x1.gu = S->at<uint16_t>(S->p.gu); x1.ldgu = 2 * I; x1.I = I;
   S->tag_dx(x1);
   QLS_RC(linear_dx(x1, st));
@@ -380,7 +380,7 @@ int bwd_layer(qls_session* S, int l, const uint8_t* rec, const uint16_t* x, floa
   x2.T = T; x2.Kc = 2 * I; x2.Nout = d; x2.dy = dgu; x2.lddy = 2 * I;
   x2.codes = w.code[QLS_GATE]; x2.absmax = w.amax[QLS_GATE]; x2.ldq = d;
   x2.du = du; x2.lddu = 2 * r; x2.Acat = lw + S->wa[QLS_GATE]; x2.rc = 2 * r;
-  x2.out = dn; x2.ldo = d; x2.epi = EPI_F32;
+  x2.out = dn; x2.ldo = d; x2.epi = EPI_F32; x2.ws = part;
   S->tag_dx(x2);
   QLS_RC(linear_dx(x2, st));
   rmsnorm_bwd(h, w.nm, sh.c.rms_eps, dn, g, dh, dyb, T, d, st);
@@ -393,7 +393,7 @@ int bwd_layer(qls_session* S, int l, const uint8_t* rec, const uint16_t* x, floa
   x3.T = T; x3.Kc = d; x3.Nout = sh.qd; x3.dy = dyb; x3.lddy = d;
   x3.codes = w.code[QLS_O]; x3.absmax = w.amax[QLS_O]; x3.ldq = sh.qd;
   x3.du = du; x3.lddu = r; x3.Acat = lw + S->wa[QLS_O]; x3.rc = r;
-  x3.out = S->at<uint16_t>(S->p.dattn); x3.ldo = sh.qd; x3.epi = EPI_BF16;
+  x3.out = S->at<uint16_t>(S->p.dattn); x3.ldo = sh.qd; x3.epi = EPI_BF16; x3.ws = part;
   S->tag_dx(x3);
   QLS_RC(linear_dx(x3, st));
 
@@ -405,7 +405,7 @@ int bwd_layer(qls_session* S, int l, const uint8_t* rec, const uint16_t* x, floa
   ab.dO = S->at<uint16_t>(S->p.dattn); ab.O = attn; ab.lddo = sh.qd;
   ab.lse = S->at<float>(S->p.lse); ab.D = S->at<float>(S->p.Dv);
   ab.dq = S->at<float>(S->p.dqf); ab.lddq = sh.qd;
-  ab.dk = S->at<float>(S->p.dkf); ab.dv = S->at<float>(S->p.dvf); ab.lddkv = sh.kvd;
+  ab.dk = S->at<float>(S->p.dkf); ab.dv = S->at<float>(S->p.dvf); ab.lddkv = sh.qd;
   QLS_RC(attn_bwd(ab, B, st));
   uint16_t* dqkv = S->at<uint16_t>(S->p.dqkv);
   rope_bwd(ab.dq, ab.dk, ab.dv, dqkv, sh.nqkv, T, Sq, sh.c.n_heads, sh.c.n_kv_heads, sh.c.head_dim,
@@ -424,7 +424,7 @@ int bwd_layer(qls_session* S, int l, const uint8_t* rec, const uint16_t* x, floa
   x4.T = T; x4.Kc = sh.nqkv; x4.Nout = d; x4.dy = dqkv; x4.lddy = sh.nqkv;
   x4.codes = w.code[QLS_Q]; x4.absmax = w.amax[QLS_Q]; x4.ldq = d;
   x4.du = du; x4.lddu = 3 * r; x4.Acat = lw + S->wa[QLS_Q]; x4.rc = 3 * r;
-  x4.out = dn; x4.ldo = d; x4.epi = EPI_F32;
+  x4.out = dn; x4.ldo = d; x4.epi = EPI_F32; x4.ws = part;
   S->tag_dx(x4);
   QLS_RC(linear_dx(x4, st));
   rmsnorm_bwd(x, w.na, sh.c.rms_eps, dn, dh, g, nullptr, T, d, st);
@@ -479,6 +479,8 @@ int head_bwd(qls_session* S, const uint16_t* xL, int T) {
     h.A = dlog; h.lda = S->z.Vc;
     h.Bh = S->res.d_lm_head + (int64_t)col0 * d; h.ldb = d;
     h.alpha = 1.f; h.C = dhf; h.ldc = d;
+    h.ksplit = big_split(T, d, width);
+    h.partial = S->at<float>(S->p.part);
     QLS_RC(gemm_launch(h, A_ROW, B_BF16_NN, c == 0 ? EPI_F32 : EPI_F32_ACC, kTile, st));
   }
   rmsnorm_bwd(xL, S->res.d_final_norm, sh.c.rms_eps, dhf, nullptr, S->at<float>(S->p.g), nullptr, T, d, st);
