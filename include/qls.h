@@ -170,7 +170,9 @@ int qls_nf4_dequant_dev(const uint8_t* d_codes, const float* d_absmax, int64_t n
  * with W the dequantised NF4 weight [N x K].  x bf16 [T x K]; A bf16 [r x K];
  * B bf16 [N x r]; outputs y bf16 [T x N] and u bf16 [T x r].  d_A/d_B NULL
  * runs the base product only (u untouched).  K, N multiples of 16; r multiple
- * of 8.  d_ws: scratch of qls_linear_ws_bytes(T, N, K, r) bytes. */
+ * of 8.  d_ws: scratch of qls_linear_ws_bytes(T, N, K, r) bytes; required with
+ * adapters, optional without (NULL: the base GEMM runs without split-K, so its
+ * fp32 sums may round differently from a run with the workspace). */
 int64_t qls_linear_ws_bytes(int T, int N, int K, int r);
 int qls_linear_fwd(const uint8_t* d_codes, const float* d_absmax, int N, int K,
                    const uint16_t* d_x, int T, const uint16_t* d_A, const uint16_t* d_B,

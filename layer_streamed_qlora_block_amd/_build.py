@@ -3,7 +3,9 @@
 Every HIP translation unit is compiled with packed-fp32 instructions disabled
 (the compiler otherwise forms v_pk_* float ops on its own).  The host
 quantiser is compiled with floating-point contraction off so its float32
-decisions match their IEEE definition.
+decisions match their IEEE definition.  The large-tile GEMM unit raises the
+full-unroll limit so its epilogue loops over the accumulator blocks unroll
+completely and the accumulators stay in registers.
 """
 from __future__ import annotations
 
@@ -24,8 +26,9 @@ HIPCC = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
 COMMON = ["-O3", "-fPIC", "-std=c++17", "-Wall", "-Wno-unused-function",
           "-I" + os.path.join(ROOT, "include")]
 DEVICE = ["-x", "hip", f"--offload-arch={ARCH}", "-Xclang", "-target-feature",
-          "-Xclang", "-packed-fp32-ops", "-fgpu-rdc" if False else "-fno-gpu-rdc"]
-PER_FILE = {"store.cpp": ["-ffp-contract=off"]}
+          "-Xclang", "-packed-fp32-ops", "-fno-gpu-rdc"]
+PER_FILE = {"store.cpp": ["-ffp-contract=off"],
+            "gemm_big.hip": ["-mllvm", "-pragma-unroll-threshold=200000"]}
 
 
 def sources():

@@ -49,6 +49,13 @@ struct GemmArgs {
 
 // Returns 0, or -1 when the (tile, loaders, epilogue) combination is not built.
 int gemm_launch(const GemmArgs& g, int aload, int bload, int epi, int tile, hipStream_t st);
+// Large-M dequant-GEMMs (256 x 256 tiles, 512 threads): B_NF4_NT with
+// EPI_BF16 (LORA_FWD allowed) and B_NF4_NN with EPI_F32 / EPI_BF16 (no
+// residual) / EPI_SWIGLU_BWD (LORA_DX allowed); no split-K.  gemm_big_ok
+// checks the shape and alignment conditions; gemm_big_launch returns -1 when
+// they do not hold.
+bool gemm_big_ok(const GemmArgs& g, int bload, int epi);
+int gemm_big_launch(const GemmArgs& g, int bload, int epi, hipStream_t st);
 // out = epilogue(sum_z partial[z]) for split-K: mode 0 -> bf16 alpha*sum, 1 -> f32 alpha*sum.
 void gemm_reduce(const float* partial, int ksplit, int M, int N, float alpha, int mode,
                  void* C, int64_t ldc, hipStream_t st);

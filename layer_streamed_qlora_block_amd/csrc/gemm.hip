@@ -17,7 +17,8 @@
 // reads of 16 consecutive rows hit distinct banks.  The LoRA term is
 // contracted first into the same accumulator (scaled by s), then the base
 // product accumulates on top, so one accumulator set serves both and the
-// kernel keeps two waves per SIMD.
+// kernel keeps two waves per SIMD.  Large-M dequant-GEMMs use the 256 x 256
+// kernels of gemm_big.hip instead.
 #include "common.h"
 #include "gemm.h"
 
@@ -778,6 +779,7 @@ bool fast_ok(const GemmArgs& g, int aload, int bload, int tile) {
 const float* nf4_codebook_dev();  // defined in nf4.hip
 
 int gemm_launch(const GemmArgs& g, int aload, int bload, int epi, int tile, hipStream_t st) {
+  if (g.ksplit > 1 && !g.partial) return -1;   // split-K partials need a buffer
   const float* cb = (bload == B_NF4_NT || bload == B_NF4_NN) ? nf4_codebook_dev() : nullptr;
   const bool fast = fast_ok(g, aload, bload, tile);
 #define QLS_CASE(BMV, AL, BL, EP)                                           \

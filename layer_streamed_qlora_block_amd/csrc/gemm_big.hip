@@ -1,0 +1,403 @@
+// Large-M dequant-GEMMs for gfx950: 256 x 256 output tile per 512-thread
+// workgroup, v_mfma_f32_32x32x16_bf16 with fp32 accumulation.
+//
+//   * NT:  Y = X W^T (+ s U_g B_g^T) (+ residual), W NF4 [N, K] (the forward);
+//   * NN:  dX = dY W (+ du_cat A_cat), contraction over W's rows (the backward).
+//
+// Eight waves, two per SIMD, in a 2 x 4 grid; each wave owns 128 x 64 of the
+// tile (4 x 2 MFMA blocks, 128 accumulators per lane), so the other wave on
+// the SIMD can issue while one waits on LDS or a barrier.  The k-loop runs in
+// steps of 64 (one NF4 block along K for NT): global loads run two steps
+// ahead through two register stages; each step dequantises the NF4 tile of
+// the next step (bf16 = RNE(float32(cb[c] * absmax)), one 2 KB LDS table that
+// maps a code byte to its two codebook values) into the other of two LDS
+// stages while the MFMAs consume the current one.  LDS rows are padded to 72
+// bf16 so the 16-byte fragment reads of 16 consecutive rows hit distinct
+// banks.  The epilogue goes through LDS, one 128-row half at a time, so
+// residual loads and output stores are 16 bytes per lane and row-contiguous.
+#include "common.h"
+#include "gemm.h"
+
+namespace {
+
+constexpr int NT = 512;
+constexpr int BM = 256, BN = 256, BK = 64, PITCH = BK + 8;
+constexpr int TILE = BM * PITCH;     // bf16 elements of one operand tile
+constexpr int STAGE = 2 * TILE;      // A tile then B tile
+constexpr int TP = BN + 4;           // fp32 pitch of the staged epilogue tile
+static_assert(128 * TP * 4 <= 2 * STAGE * 2, "epilogue half-tile must fit the stages");
+
+QLS_DEV __amdgpu_buffer_rsrc_t rsrc(const void* p, int64_t bytes) {
+  const int n = bytes <= 0 ? 0 : (bytes > 0x7fffffffLL ? 0x7fffffff : (int)bytes);
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, n, 0x00020000);
+}
+QLS_DEV u32x4 ld128(__amdgpu_buffer_rsrc_t r, uint32_t v, uint32_t s) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, v, s, 0));
+}
+QLS_DEV uint32_t ld32(__amdgpu_buffer_rsrc_t r, uint32_t v, uint32_t s) {
+  return __builtin_amdgcn_raw_buffer_load_b32(r, v, s, 0);
+}
+QLS_DEV float sigm(float x) { return 1.f / (1.f + __expf(-x)); }
+
+// One register stage of global data: the thread's A slice (row t/2, 32
+// contraction values) and its B codes (NT: 32 codes of one W row + absmax;
+// NN: 4 W rows x 8 columns + 4 absmax).
+template <int BL> struct Stage;
+template <> struct Stage<B_NF4_NT> { u32x4 a[4]; u32x4 q; float s; };
+template <> struct Stage<B_NF4_NN> { u32x4 a[4]; uint32_t q[4]; float s[4]; };
+
+template <int BL>
+struct Big {
+  const GemmArgs& g;
+  uint16_t* smem;
+  const float2* lut2;
+  int t, lane, wm, wn, m0, n0;
+  __amdgpu_buffer_rsrc_t ra, rq, rs;
+  uint32_t va, vq, vs;
+  f32x16 acc[4][2];
+
+  QLS_DEV Big(const GemmArgs& g_, uint16_t* smem_, const float2* lut2_, int m0_, int n0_)
+      : g(g_), smem(smem_), lut2(lut2_), m0(m0_), n0(n0_) {
+    t = threadIdx.x;
+    lane = t & 63;
+    const int wave = t >> 6;
+    wm = wave >> 2;
+    wn = wave & 3;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) acc[i][j] = f32x16{};
+    // A rows m0.. through a resource that ends at row M (rows past it read 0).
+    ra = rsrc(g.A + (int64_t)m0 * g.lda, (int64_t)(g.M - m0) * g.lda * 2);
+    va = (uint32_t)(((t >> 1) * g.lda + 32 * (t & 1)) * 2);
+    if constexpr (BL == B_NF4_NT) {
+      // W rows n0..: codes row n at n * ldq / 2, absmax at n * ldq / 64.
+      rq = rsrc(g.Bq + (int64_t)n0 * g.ldq / 2, (int64_t)(g.N - n0) * g.ldq / 2);
+      rs = rsrc(g.Bs + (int64_t)n0 * (g.ldq / 64), (int64_t)(g.N - n0) * (g.ldq / 64) * 4);
+      vq = (uint32_t)((t >> 1) * (g.ldq / 2) + 16 * (t & 1));
+      vs = (uint32_t)((t >> 1) * (g.ldq / 64) * 4);
+    } else {
+      // W columns n0..: element (k, n) at k * ldq + n; 32 groups of 8 columns,
+      // 16 groups of 4 contraction rows.
+      const int cg = t & 31, kq = t >> 5;
+      rq = rsrc(g.Bq + n0 / 2, ((int64_t)g.K * g.ldq - n0) / 2);
+      rs = rsrc(g.Bs + n0 / 64, ((int64_t)g.K * g.ldq - n0) / 64 * 4);
+      vq = (uint32_t)(((int64_t)4 * kq * g.ldq + 8 * cg) / 2);
+      vs = (uint32_t)(((int64_t)4 * kq * (g.ldq / 64) + cg / 8) * 4);
+    }
+  }
+
+  QLS_DEV void load(Stage<BL>& r, int k0) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) r.a[j] = ld128(ra, va + 16 * j, (uint32_t)k0 * 2);
+    if constexpr (BL == B_NF4_NT) {
+      r.q = ld128(rq, vq, (uint32_t)k0 / 2);
+      r.s = __uint_as_float(ld32(rs, vs, (uint32_t)k0 / 16));
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        r.q[i] = ld32(rq, vq, (uint32_t)(k0 + i) * (uint32_t)g.ldq / 2);
+        r.s[i] = __uint_as_float(ld32(rs, vs, (uint32_t)(k0 + i) * (uint32_t)(g.ldq / 64) * 4));
+      }
+    }
+  }
+
+  // Dequantise and write one register stage into LDS stage (sA, sB).
+  QLS_DEV void store(const Stage<BL>& r, uint16_t* sA, uint16_t* sB) const {
+    const int row = t >> 1, half = t & 1;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) *reinterpret_cast<u32x4*>(sA + row * PITCH + 32 * half + 8 * j) = r.a[j];
+    if constexpr (BL == B_NF4_NT) {
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const uint32_t c = r.q[w];
+        u32x4 o;
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+          const float2 v = lut2[(c >> (8 * b)) & 0xFFu];
+          o[b] = pack2_bf16(v.x * r.s, v.y * r.s);
+        }
+        *reinterpret_cast<u32x4*>(sB + row * PITCH + 32 * half + 8 * w) = o;
+      }
+    } else {
+      // Byte b of each of the 4 code words holds columns 2b, 2b+1 of one
+      // contraction row; each column's 4 rows land as one 8-byte LDS write.
+      const int cg = t & 31, kq = t >> 5;
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        float2 e[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) e[i] = lut2[(r.q[i] >> (8 * b)) & 0xFFu];
+        *reinterpret_cast<u32x2*>(sB + (8 * cg + 2 * b) * PITCH + 4 * kq) =
+            u32x2{pack2_bf16(e[0].x * r.s[0], e[1].x * r.s[1]), pack2_bf16(e[2].x * r.s[2], e[3].x * r.s[3])};
+        *reinterpret_cast<u32x2*>(sB + (8 * cg + 2 * b + 1) * PITCH + 4 * kq) =
+            u32x2{pack2_bf16(e[0].y * r.s[0], e[1].y * r.s[1]), pack2_bf16(e[2].y * r.s[2], e[3].y * r.s[3])};
+      }
+    }
+  }
+
+  QLS_DEV void mma(const uint16_t* sA, const uint16_t* sB) {
+#pragma unroll
+    for (int s = 0; s < BK / 16; ++s) {
+      const int kofs = 16 * s + 8 * (lane >> 5);
+      u32x4 a[4], b[2];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        a[i] = *reinterpret_cast<const u32x4*>(sA + (wm * 128 + 32 * i + (lane & 31)) * PITCH + kofs);
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+        b[j] = *reinterpret_cast<const u32x4*>(sB + (wn * 64 + 32 * j + (lane & 31)) * PITCH + kofs);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) acc[i][j] = mfma32(a[i], b[j], acc[i][j]);
+    }
+  }
+
+  // ---- LoRA contraction into the accumulator (before the base product).
+  // Plain guarded loads: it runs once per tile.
+  // Rows m0.. of P (row-major, ld), contraction columns [k0, k0+64) of [0, K):
+  QLS_DEV void stage_rows(uint16_t* s, const uint16_t* p, int64_t ld, int rlo, int rhi, int r0, int k0, int K) const {
+    const int row = t >> 1, half = t & 1;
+    const int gr = r0 + row;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int k = k0 + 32 * half + 8 * j;
+      u32x4 v = u32x4{0, 0, 0, 0};
+      if (gr >= rlo && gr < rhi && k < K) v = *reinterpret_cast<const u32x4*>(p + (int64_t)gr * ld + k);
+      *reinterpret_cast<u32x4*>(s + row * PITCH + 32 * half + 8 * j) = v;
+    }
+  }
+  // Columns n0.. of P stored k-major (element (k, n) at p[k * ld + n]), transposed into [n][k]:
+  QLS_DEV void stage_cols(uint16_t* s, const uint16_t* p, int64_t ld, int ncols, int k0, int K) const {
+    const int cg = t & 31, kq = t >> 5;   // 8 columns x 4 contraction rows
+    uint32_t w[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int k = k0 + 4 * kq + i;
+      const int n = n0 + 8 * cg;
+      u32x4 x = u32x4{0, 0, 0, 0};
+      if (k < K && n < ncols) x = *reinterpret_cast<const u32x4*>(p + (int64_t)k * ld + n);
+      w[i][0] = x.x; w[i][1] = x.y; w[i][2] = x.z; w[i][3] = x.w;
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int sh = 16 * (e & 1);
+      const uint32_t x0 = (w[0][e >> 1] >> sh) & 0xFFFFu, x1 = (w[1][e >> 1] >> sh) & 0xFFFFu;
+      const uint32_t x2 = (w[2][e >> 1] >> sh) & 0xFFFFu, x3 = (w[3][e >> 1] >> sh) & 0xFFFFu;
+      *reinterpret_cast<u32x2*>(s + (8 * cg + e) * PITCH + 4 * kq) = u32x2{x0 | (x1 << 16), x2 | (x3 << 16)};
+    }
+  }
+
+  QLS_DEV void lora() {
+    uint16_t* sA = smem;
+    uint16_t* sB = smem + TILE;
+    if constexpr (BL == B_NF4_NT) {
+      // acc = (s2 / alpha) sum_g U_g B_g^T; B_g is zero outside module g's columns.
+      int start = 0;
+      for (int gi = 0; gi < g.nmod; ++gi) {
+        const int end = g.mod_end[gi];
+        if (end > n0 && start < n0 + BN) {
+          const uint16_t* bp = g.modB[gi] - (int64_t)start * g.K2;
+          for (int k0 = 0; k0 < g.K2; k0 += BK) {
+            stage_rows(sA, g.A2 + gi * g.K2, g.lda2, 0, g.M, m0, k0, g.K2);
+            stage_rows(sB, bp, g.K2, start, end, n0, k0, g.K2);
+            __syncthreads();
+            mma(sA, sB);
+            __syncthreads();
+          }
+        }
+        start = end;
+      }
+      const float sc = g.s2 / g.alpha;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) acc[i][j] *= sc;
+    } else {
+      // acc = du_cat A_cat, A_cat [K2, N] row-major.
+      for (int k0 = 0; k0 < g.K2; k0 += BK) {
+        stage_rows(sA, g.A2, g.lda2, 0, g.M, m0, k0, g.K2);
+        stage_cols(sB, g.B2, g.ldb2, g.N, k0, g.K2);
+        __syncthreads();
+        mma(sA, sB);
+        __syncthreads();
+      }
+    }
+  }
+
+  // ---- base product: two register stages, two LDS stages, one barrier per step.
+  QLS_DEV void mainloop() {
+    const int nk = g.K / BK;
+    uint16_t* const s0 = smem;
+    uint16_t* const s1 = smem + STAGE;
+    Stage<BL> r0, r1;
+    load(r0, 0);
+    load(r1, min(1, nk - 1) * BK);
+    store(r0, s0, s0 + TILE);
+    __syncthreads();
+    // Loads past the last step re-read step nk-1 (in bounds, never consumed).
+    for (int kt = 0;; kt += 2) {
+      load(r0, min(kt + 2, nk - 1) * BK);
+      mma(s0, s0 + TILE);
+      store(r1, s1, s1 + TILE);
+      __syncthreads();
+      if (kt + 1 >= nk) break;
+      load(r1, min(kt + 3, nk - 1) * BK);
+      mma(s1, s1 + TILE);
+      store(r0, s0, s0 + TILE);
+      __syncthreads();
+      if (kt + 2 >= nk) break;
+    }
+  }
+
+  // ---- epilogue through LDS, one 128-row half at a time; 8 columns per thread.
+  template <int EPI>
+  QLS_DEV void epilogue() {
+    float* sT = reinterpret_cast<float*>(smem);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      if (wm == h) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int q = 0; q < 16; ++q) {
+              const int mm = 32 * i + 8 * (q >> 2) + 4 * (lane >> 5) + (q & 3);
+              const int nn = wn * 64 + 32 * j + (lane & 31);
+              sT[mm * TP + nn] = acc[i][j][q];
+            }
+      }
+      __syncthreads();
+#pragma unroll 2
+      for (int it = 0; it < 8; ++it) {
+        const int rr = (t >> 5) + 16 * it, c8 = 8 * (t & 31);
+        const int m = m0 + 128 * h + rr, n = n0 + c8;
+        if (m < g.M && n < g.N) {
+          const f32x4 x0 = *reinterpret_cast<const f32x4*>(sT + rr * TP + c8);
+          const f32x4 x1 = *reinterpret_cast<const f32x4*>(sT + rr * TP + c8 + 4);
+          float y[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+#pragma unroll
+          for (int e = 0; e < 8; ++e) y[e] *= g.alpha;
+          if constexpr (EPI == EPI_BF16) {
+            if (g.R) {
+              const u32x4 rv = *reinterpret_cast<const u32x4*>(g.R + (int64_t)m * g.ldr + n);
+#pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                y[2 * e] += bflo(rv[e]);
+                y[2 * e + 1] += bfhi(rv[e]);
+              }
+            }
+            u32x4 o;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) o[e] = pack2_bf16(y[2 * e], y[2 * e + 1]);
+            *reinterpret_cast<u32x4*>(reinterpret_cast<uint16_t*>(g.C) + (int64_t)m * g.ldc + n) = o;
+          } else if constexpr (EPI == EPI_F32) {
+            float* c = reinterpret_cast<float*>(g.C) + (int64_t)m * g.ldc + n;
+            *reinterpret_cast<f32x4*>(c) = f32x4{y[0], y[1], y[2], y[3]};
+            *reinterpret_cast<f32x4*>(c + 4) = f32x4{y[4], y[5], y[6], y[7]};
+          } else if constexpr (EPI == EPI_SWIGLU_BWD) {
+            // y = dL/da for a = silu(g) * u: dg = y u silu'(g), du = y silu(g).
+            const u32x4 gv = *reinterpret_cast<const u32x4*>(g.gu + (int64_t)m * g.ldgu + n);
+            const u32x4 uv = *reinterpret_cast<const u32x4*>(g.gu + (int64_t)m * g.ldgu + g.I + n);
+            u32x4 og, ou;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              float dg[2], du[2];
+#pragma unroll
+              for (int p = 0; p < 2; ++p) {
+                const float gg = p ? bfhi(gv[e]) : bflo(gv[e]);
+                const float uu = p ? bfhi(uv[e]) : bflo(uv[e]);
+                const float sg = sigm(gg);
+                dg[p] = y[2 * e + p] * uu * sg * (1.f + gg * (1.f - sg));
+                du[p] = y[2 * e + p] * (gg * sg);
+              }
+              og[e] = pack2_bf16(dg[0], dg[1]);
+              ou[e] = pack2_bf16(du[0], du[1]);
+            }
+            uint16_t* out = reinterpret_cast<uint16_t*>(g.C) + (int64_t)m * g.ldc;
+            *reinterpret_cast<u32x4*>(out + n) = og;
+            *reinterpret_cast<u32x4*>(out + g.I + n) = ou;
+          }
+        }
+      }
+      __syncthreads();
+    }
+  }
+};
+
+template <int BL, int EPI>
+__global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2)))
+big_kernel(GemmArgs g, const float* __restrict__ cb) {
+  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * STAGE];
+  __shared__ __attribute__((aligned(16))) float2 lut2[256];
+  const int t = threadIdx.x;
+  if (t < 256) lut2[t] = make_float2(cb[t >> 4], cb[t & 15]);   // byte -> (high, low) nibble levels
+  const int tiles_n = (g.N + BN - 1) / BN;
+  const int m0 = (blockIdx.x / tiles_n) * BM, n0 = (blockIdx.x % tiles_n) * BN;
+  Big<BL> k(g, smem, lut2, m0, n0);
+  __syncthreads();
+  if ((BL == B_NF4_NT && g.lora == LORA_FWD) || (BL == B_NF4_NN && g.lora == LORA_DX)) k.lora();
+  k.mainloop();
+  k.template epilogue<EPI>();
+}
+
+}  // namespace
+
+const float* nf4_codebook_dev();  // defined in nf4.hip
+
+namespace {
+bool a16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
+bool fits31(int64_t bytes) { return bytes < 0x7fffffffLL; }
+}  // namespace
+
+bool gemm_big_ok(const GemmArgs& g, int bload, int epi) {
+  if (g.M <= 0 || g.N <= 0 || g.K <= 0 || g.K % BK || g.ksplit > 1) return false;
+  if (g.lda % 8 || !a16(g.A) || !fits31((int64_t)g.M * g.lda * 2)) return false;
+  if (g.ldq % 64 || !g.Bq || !g.Bs || !a16(g.C)) return false;
+  if (bload == B_NF4_NT) {
+    if (epi != EPI_BF16 || g.N % 8 || g.ldc % 8 || g.ldq < g.K) return false;
+    if (!fits31((int64_t)g.N * g.ldq / 2)) return false;
+    if (g.R && (g.ldr % 8 || !a16(g.R))) return false;
+    if (g.lora == LORA_FWD) {
+      if (g.K2 % 8 || g.lda2 % 8 || !a16(g.A2) || g.nmod < 1 || g.nmod > 4) return false;
+      for (int i = 0; i < g.nmod; ++i)
+        if (!a16(g.modB[i])) return false;
+    }
+    return true;
+  }
+  if (bload == B_NF4_NN) {
+    if (g.N % BN || g.ldq < g.N || !fits31((int64_t)g.K * g.ldq / 2)) return false;
+    if (epi == EPI_F32) {
+      if (g.ldc % 4) return false;
+    } else if (epi == EPI_BF16) {
+      if (g.ldc % 8 || g.R) return false;
+    } else if (epi == EPI_SWIGLU_BWD) {
+      if (g.ldc % 8 || g.ldgu % 8 || g.I % 8 || !a16(g.gu)) return false;
+    } else {
+      return false;
+    }
+    if (g.lora == LORA_DX && (g.K2 % 8 || g.lda2 % 8 || g.ldb2 % 8 || !a16(g.A2) || !a16(g.B2)))
+      return false;
+    return true;
+  }
+  return false;
+}
+
+int gemm_big_launch(const GemmArgs& g, int bload, int epi, hipStream_t st) {
+  if (!gemm_big_ok(g, bload, epi)) return -1;
+  const float* cb = nf4_codebook_dev();
+  const unsigned tiles = (unsigned)(((g.M + BM - 1) / BM) * ((g.N + BN - 1) / BN));
+  if (g.ev0) (void)hipEventRecord(g.ev0, st);
+  if (bload == B_NF4_NT)
+    hipLaunchKernelGGL((big_kernel<B_NF4_NT, EPI_BF16>), dim3(tiles), dim3(NT), 0, st, g, cb);
+  else if (epi == EPI_F32)
+    hipLaunchKernelGGL((big_kernel<B_NF4_NN, EPI_F32>), dim3(tiles), dim3(NT), 0, st, g, cb);
+  else if (epi == EPI_BF16)
+    hipLaunchKernelGGL((big_kernel<B_NF4_NN, EPI_BF16>), dim3(tiles), dim3(NT), 0, st, g, cb);
+  else
+    hipLaunchKernelGGL((big_kernel<B_NF4_NN, EPI_SWIGLU_BWD>), dim3(tiles), dim3(NT), 0, st, g, cb);
+  if (g.ev1) (void)hipEventRecord(g.ev1, st);
+  return 0;
+}

@@ -53,6 +53,11 @@ int big_split(int M, int N, int K) {
   return std::max(1, std::min(ks, 16));
 }
 
+// The dequant-GEMMs take the 256 x 256 kernels once there are at least as
+// many such tiles as CUs (no split-K needed to fill the chip); 128 x 128 tiles
+// with split-K otherwise.
+bool use_big(int M, int N) { return cdiv(M, 256) * cdiv(N, 256) >= 256; }
+
 int64_t skinny_partial_floats(int64_t max_mn) {
   return std::max<int64_t>({max_mn, (int64_t)kSkinnyTarget * 64 * 64, kBigPartial});
 }
@@ -105,10 +110,13 @@ int linear_fwd(const LinearFwd& f, hipStream_t st) {
     for (int i = 0; i < f.nmod; ++i) { g.mod_end[i] = f.mod_end[i]; g.modB[i] = f.Bm[i]; }
     g.s2 = f.s;
   }
-  g.ksplit = big_split(f.T, f.N, f.K);
-  g.partial = f.ws;
   g.ev0 = f.ev0;
   g.ev1 = f.ev1;
+  if (use_big(f.T, f.N) && gemm_big_ok(g, B_NF4_NT, EPI_BF16))
+    return gemm_big_launch(g, B_NF4_NT, EPI_BF16, st);
+  // Split-K needs the workspace for its partials; without one the GEMM runs unsplit.
+  g.ksplit = f.ws ? big_split(f.T, f.N, f.K) : 1;
+  g.partial = f.ws;
   return gemm_launch(g, A_ROW, B_NF4_NT, EPI_BF16, 128, st);
 }
 
@@ -126,11 +134,12 @@ int linear_dx(const LinearDx& d, hipStream_t st) {
     g.K2 = d.rc;
   }
   g.gu = d.gu; g.ldgu = d.ldgu; g.I = d.I;
+  g.ev0 = d.ev0;
+  g.ev1 = d.ev1;
+  if (use_big(d.T, d.Nout) && gemm_big_ok(g, B_NF4_NN, d.epi)) return gemm_big_launch(g, B_NF4_NN, d.epi, st);
   if (d.ws) {
     g.ksplit = big_split(d.T, d.Nout, d.Kc);
     g.partial = d.ws;
   }
-  g.ev0 = d.ev0;
-  g.ev1 = d.ev1;
   return gemm_launch(g, A_ROW, B_NF4_NN, d.epi, 128, st);
 }

@@ -38,6 +38,8 @@ int linear_dx(const LinearDx& d, hipStream_t st);
 // Split-K factor for a 128 x 128-tiled GEMM of M x N x K (partials fit in
 // skinny_partial_floats()).
 int big_split(int M, int N, int K);
+// True when an M x N dequant-GEMM takes the 256 x 256 kernels.
+bool use_big(int M, int N);
 
 // Skinny LoRA products (split-K over the long dimension, deterministic reduce).
 // U = bf16(x A^T)                   x [T, K] (ldx), A [n, K]          -> U [T, n] (ldu)

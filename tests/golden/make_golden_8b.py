@@ -9,8 +9,9 @@ The NF4 store is built by the oracle's own quantiser (in worker processes);
 dequantised layers are produced on demand so the script stays within ~12 GB.
 Run time: ~20 min on 8 cores.
 
-    python tests/golden/make_golden_8b.py
+    python tests/golden/make_golden_8b.py [--prec fp64 --out PATH]
 """
+import argparse
 import json
 import multiprocessing as mp
 import os
@@ -53,6 +54,10 @@ class LazyLayers:
 
 
 def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--prec", choices=["mirror", "fp64"], default="mirror")
+    ap.add_argument("--out", default=os.path.join(os.path.dirname(os.path.abspath(__file__)), "sft_8b_seq512.json"))
+    args = ap.parse_args()
     t0 = time.time()
     with mp.get_context("spawn").Pool(min(4, os.cpu_count() or 1)) as pool:
         store = dict(pool.imap_unordered(quantize_layer, range(CFG.L)))
@@ -62,7 +67,7 @@ def main():
     lora = synth.lora_init(CFG)
     ids = synth.token_ids(CFG, 1, S, seed=41)
     t1 = time.time()
-    loss, grads, _ = om.sft_step(CFG, om.Prec("mirror"), model, lora, ids)
+    loss, grads, _ = om.sft_step(CFG, om.Prec(args.prec), model, lora, ids)
     print(f"sft step in {time.time() - t1:.0f} s, loss {loss:.7f}", flush=True)
     rng = np.random.default_rng(99)
     samples, norms = [], []
@@ -74,12 +79,12 @@ def main():
                 for i in rng.integers(0, g.size, SAMPLES):
                     samples.append([l, m, w, int(i), float(g[i])])
     out = {
-        "what": "oracle SFT step, 8B-shaped stack, batch 1 x seq 512, mirror precision",
+        "what": f"oracle SFT step, 8B-shaped stack, batch 1 x seq 512, {args.prec} precision",
         "config": CFG.as_dict(), "seq": S, "ids_seed": 41, "lora_b_std": 1e-3,
         "loss": loss, "grad_norms": norms, "samples": samples,
         "made_by": "tests/golden/make_golden_8b.py (oracle only)",
     }
-    path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "sft_8b_seq512.json")
+    path = args.out
     with open(path, "w") as f:
         json.dump(out, f)
     print(f"wrote {path} ({len(samples)} samples) in {time.time() - t0:.0f} s", flush=True)

@@ -3,7 +3,8 @@
 * One Llama-3.1-8B-shaped decoder layer streamed from pinned host memory,
   forward + recomputed forward + backward, against the oracle run on the same
   seeded inputs (rel. L2 <= 1e-2, cosine >= 0.999 for the output, dL/dx and
-  every LoRA matrix), and streamed == resident bitwise.
+  every LoRA matrix), and streamed == resident bitwise; the same for a
+  narrower layer at 8192 tokens, which takes the large-tile GEMM kernels.
 * A layer above 172 MiB (hidden 5120, SwiGLU 27648: 274 MB per record) streams
   bit-identically to the resident run -- page "Can You Fine-Tune Llama 3.1 8B
   on a 4GB GPU? ...", section "Did a correctness bug invalidate the Llama 3.1
@@ -51,10 +52,19 @@ def _grad_check(name, got, want):
     assert r <= 1e-2 and c >= 0.999, (name, r, c)
 
 
-def test_one_8b_layer_matches_oracle(q):
-    cfg = synth.scaled(synth.LLAMA8B, L=1)
-    T = 512
-    print("building one 8B layer", flush=True)
+# (config, batch, seq): one 8B layer at 512 tokens, and a narrower layer at
+# 4 x 2048 tokens whose every projection (fused q|k|v with three LoRA modules,
+# o and down with the residual, gate|up) and every dX product is large enough
+# for the 256 x 256 dequant-GEMM kernels.
+WIDE = synth.ModelCfg(L=1, d=2048, H=16, KV=4, hd=128, I=5632, V=1024, eps=1e-5, theta=500000.0,
+                      r=16, alpha=32.0)
+LAYER_CASES = [("8b", synth.scaled(synth.LLAMA8B, L=1), 1, 512), ("wide-8k-tokens", WIDE, 4, 2048)]
+
+
+@pytest.mark.parametrize("name,cfg,B,S", LAYER_CASES, ids=[c[0] for c in LAYER_CASES])
+def test_one_layer_matches_oracle(q, name, cfg, B, S):
+    T = B * S
+    print(f"building one layer ({name}, {B} x {S} tokens)", flush=True)
     store = _store(q, cfg)
     emb = torch.zeros(cfg.V, cfg.d, dtype=torch.bfloat16, device="cuda")   # unused by a single layer
     fn = torch.ones(cfg.d, dtype=torch.bfloat16, device="cuda")
@@ -64,11 +74,11 @@ def test_one_8b_layer_matches_oracle(q):
     gout = synth.activation(32, (T, cfg.d))
     res = {}
     for mode in (q.QLS_STREAMED, q.QLS_RESIDENT):
-        sess = q.Session(store, emb, emb, fn, max_tokens=T, max_seq=T, mode=mode)
+        sess = q.Session(store, emb, emb, fn, max_tokens=T, max_seq=S, mode=mode)
         out = torch.empty(T, cfg.d, dtype=torch.bfloat16, device="cuda")
         gin = torch.empty(T, cfg.d, dtype=torch.float32, device="cuda")
         grads = torch.zeros_like(d_lora)
-        sess.layer_fwd_bwd(0, x.cuda(), gout.cuda(), 1, T, d_lora, out, gin, grads)
+        sess.layer_fwd_bwd(0, x.cuda(), gout.cuda(), B, S, d_lora, out, gin, grads)
         torch.cuda.synchronize()
         res[mode] = (out.cpu(), gin.cpu(), grads.cpu())
         sess.close()
@@ -79,10 +89,10 @@ def test_one_8b_layer_matches_oracle(q):
     na, nm = synth.layer_norms(cfg, 0)
     lw = om.dequant_layer(cfg, ws, na.float().numpy(), nm.float().numpy())
     del ws
-    tabs = om.rope_tables(PM, T, cfg.hd, cfg.theta)
+    tabs = om.rope_tables(PM, S, cfg.hd, cfg.theta)
     xo = x.float().numpy()
-    out_o, cache = om.layer_forward(cfg, PM, xo, lw, lora[0], 1, T, tabs)
-    gin_o, grads_o = om.layer_backward(cfg, PM, cache, gout.float().numpy(), lw, lora[0], 1, T, tabs)
+    out_o, cache = om.layer_forward(cfg, PM, xo, lw, lora[0], B, S, tabs)
+    gin_o, grads_o = om.layer_backward(cfg, PM, cache, gout.float().numpy(), lw, lora[0], B, S, tabs)
     out, gin, grads = res[q.QLS_STREAMED]
     _grad_check("layer out", f32(out), out_o)
     _grad_check("dL/dx", f32(gin), gin_o)

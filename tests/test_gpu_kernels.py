@@ -60,9 +60,11 @@ def _linear_case(N, K, T, r, seed):
     return codes, absmax, Wd, x, A, B, dy
 
 
-# (N, K, T, r): the 8B MLP shape, and ragged shapes (T not a tile multiple,
-# K % 64 != 0 so NF4 blocks straddle rows).
-CASES = [(14336, 4096, 512, 64, 22), (256, 688, 101, 8, 30), (688, 256, 77, 8, 40)]
+# (N, K, T, r): the 8B MLP shape, ragged shapes (T not a tile multiple,
+# K % 64 != 0 so NF4 blocks straddle rows), and a forward and a dX with at
+# least 256 output tiles of 256 x 256 (the large-tile kernels; ragged in T).
+CASES = [(14336, 4096, 512, 64, 22), (256, 688, 101, 8, 30), (688, 256, 77, 8, 40),
+         (7680, 1024, 2100, 16, 50), (1024, 7680, 2100, 16, 60)]
 
 
 @pytest.mark.parametrize("N,K,T,r,seed", CASES)
@@ -97,10 +99,10 @@ def test_linear_one_hot_reproduces_weight(q, N, K, T, r, seed):
     assert not np.any(f32(dA))
 
 
-@pytest.mark.parametrize("N,K,T,r,seed", CASES)
-def test_linear_matches_oracle(q, N, K, T, r, seed):
-    print(f"linear vs oracle N={N} K={K} T={T} r={r}", flush=True)
-    alpha = 16.0
+# alpha / r = 1.5: a LoRA scale that is not a power of two.
+@pytest.mark.parametrize("N,K,T,r,seed,alpha", [c + (16.0,) for c in CASES] + [(7680, 1024, 2100, 16, 70, 24.0)])
+def test_linear_matches_oracle(q, N, K, T, r, seed, alpha):
+    print(f"linear vs oracle N={N} K={K} T={T} r={r} alpha={alpha}", flush=True)
     s = alpha / r
     codes, absmax, Wd, x, A, B, dy = _linear_case(N, K, T, r, seed)
     dc, da = dev(codes), dev(absmax)
@@ -112,9 +114,10 @@ def test_linear_matches_oracle(q, N, K, T, r, seed):
     dA = torch.empty(r, K, dtype=torch.float32, device="cuda")
     dB = torch.empty(N, r, dtype=torch.float32, device="cuda")
     q.qls_linear_bwd(dc, da, N, K, dev(x), u, dev(dy), T, dev(A), dev(B), r, alpha, dx, dA, dB, ws)
-    # adapters disabled and B = 0 must give the identical base output
+    # adapters disabled and B = 0 must give the identical base output (both with
+    # the workspace, so both take the same split-K)
     y0 = torch.empty_like(y)
-    q.qls_linear_fwd(dc, da, N, K, dev(x), T, None, None, r, alpha, y0, None, None)
+    q.qls_linear_fwd(dc, da, N, K, dev(x), T, None, None, r, alpha, y0, None, ws)
     yb0 = torch.empty_like(y)
     q.qls_linear_fwd(dc, da, N, K, dev(x), T, dev(A), torch.zeros_like(dev(B)), r, alpha, yb0, u.clone(), ws)
     torch.cuda.synchronize()
