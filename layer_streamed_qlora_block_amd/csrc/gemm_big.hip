@@ -39,6 +39,17 @@ QLS_DEV uint32_t ld32(__amdgpu_buffer_rsrc_t r, uint32_t v, uint32_t s) {
 }
 QLS_DEV float sigm(float x) { return 1.f / (1.f + __expf(-x)); }
 
+// NN B tile: each thread dequantises 4 contraction rows x 8 columns.  Column
+// group cg (8 columns) and row quad kq of thread t are interleaved so that a
+// half-wave covers 8 column groups x 4 row quads, and the 16-byte chunks of
+// each LDS row are XOR-swizzled by (row / 16) so that both the transposing
+// 8-byte writes and the 16-byte fragment reads are free of bank conflicts.
+QLS_DEV int nn_cg(int t) { return (t & 7) | (((t >> 5) & 3) << 3); }
+QLS_DEV int nn_kq(int t) { return ((t >> 3) & 3) | ((t >> 7) << 2); }
+QLS_DEV int nn_swz(int n) { return 2 * ((n >> 4) & 3); }
+// Element offset of contraction index k (multiple of 4) in LDS row n of an NN B tile.
+QLS_DEV int nn_pos(int n, int k) { return n * PITCH + 8 * ((k >> 3) ^ nn_swz(n)) + (k & 7); }
+
 // One register stage of global data: the thread's A slice (row t/2, 32
 // contraction values) and its B codes (NT: 32 codes of one W row + absmax;
 // NN: 4 W rows x 8 columns + 4 absmax).
@@ -79,7 +90,7 @@ struct Big {
     } else {
       // W columns n0..: element (k, n) at k * ldq + n; 32 groups of 8 columns,
       // 16 groups of 4 contraction rows.
-      const int cg = t & 31, kq = t >> 5;
+      const int cg = nn_cg(t), kq = nn_kq(t);
       rq = rsrc(g.Bq + n0 / 2, ((int64_t)g.K * g.ldq - n0) / 2);
       rs = rsrc(g.Bs + n0 / 64, ((int64_t)g.K * g.ldq - n0) / 64 * 4);
       vq = (uint32_t)(((int64_t)4 * kq * g.ldq + 8 * cg) / 2);
@@ -122,15 +133,15 @@ struct Big {
     } else {
       // Byte b of each of the 4 code words holds columns 2b, 2b+1 of one
       // contraction row; each column's 4 rows land as one 8-byte LDS write.
-      const int cg = t & 31, kq = t >> 5;
+      const int cg = nn_cg(t), kq = nn_kq(t);
 #pragma unroll
       for (int b = 0; b < 4; ++b) {
         float2 e[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) e[i] = lut2[(r.q[i] >> (8 * b)) & 0xFFu];
-        *reinterpret_cast<u32x2*>(sB + (8 * cg + 2 * b) * PITCH + 4 * kq) =
+        *reinterpret_cast<u32x2*>(sB + nn_pos(8 * cg + 2 * b, 4 * kq)) =
             u32x2{pack2_bf16(e[0].x * r.s[0], e[1].x * r.s[1]), pack2_bf16(e[2].x * r.s[2], e[3].x * r.s[3])};
-        *reinterpret_cast<u32x2*>(sB + (8 * cg + 2 * b + 1) * PITCH + 4 * kq) =
+        *reinterpret_cast<u32x2*>(sB + nn_pos(8 * cg + 2 * b + 1, 4 * kq)) =
             u32x2{pack2_bf16(e[0].y * r.s[0], e[1].y * r.s[1]), pack2_bf16(e[2].y * r.s[2], e[3].y * r.s[3])};
       }
     }
@@ -145,8 +156,13 @@ struct Big {
       for (int i = 0; i < 4; ++i)
         a[i] = *reinterpret_cast<const u32x4*>(sA + (wm * 128 + 32 * i + (lane & 31)) * PITCH + kofs);
 #pragma unroll
-      for (int j = 0; j < 2; ++j)
-        b[j] = *reinterpret_cast<const u32x4*>(sB + (wn * 64 + 32 * j + (lane & 31)) * PITCH + kofs);
+      for (int j = 0; j < 2; ++j) {
+        const int n = wn * 64 + 32 * j + (lane & 31);
+        if constexpr (BL == B_NF4_NN)
+          b[j] = *reinterpret_cast<const u32x4*>(sB + nn_pos(n, kofs));
+        else
+          b[j] = *reinterpret_cast<const u32x4*>(sB + n * PITCH + kofs);
+      }
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -168,9 +184,10 @@ struct Big {
       *reinterpret_cast<u32x4*>(s + row * PITCH + 32 * half + 8 * j) = v;
     }
   }
-  // Columns n0.. of P stored k-major (element (k, n) at p[k * ld + n]), transposed into [n][k]:
+  // Columns n0.. of P stored k-major (element (k, n) at p[k * ld + n]),
+  // transposed into the swizzled NN layout:
   QLS_DEV void stage_cols(uint16_t* s, const uint16_t* p, int64_t ld, int ncols, int k0, int K) const {
-    const int cg = t & 31, kq = t >> 5;   // 8 columns x 4 contraction rows
+    const int cg = nn_cg(t), kq = nn_kq(t);   // 8 columns x 4 contraction rows
     uint32_t w[4][4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -185,7 +202,7 @@ struct Big {
       const int sh = 16 * (e & 1);
       const uint32_t x0 = (w[0][e >> 1] >> sh) & 0xFFFFu, x1 = (w[1][e >> 1] >> sh) & 0xFFFFu;
       const uint32_t x2 = (w[2][e >> 1] >> sh) & 0xFFFFu, x3 = (w[3][e >> 1] >> sh) & 0xFFFFu;
-      *reinterpret_cast<u32x2*>(s + (8 * cg + e) * PITCH + 4 * kq) = u32x2{x0 | (x1 << 16), x2 | (x3 << 16)};
+      *reinterpret_cast<u32x2*>(s + nn_pos(8 * cg + e, 4 * kq)) = u32x2{x0 | (x1 << 16), x2 | (x3 << 16)};
     }
   }
 
