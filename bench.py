@@ -35,7 +35,11 @@ PCIE_GEN5_X16_GBPS = 64.0       # theoretical per direction
 
 
 def gpu_clock_mhz():
-    """Best effort, queried before this process touches the GPU."""
+    """Best effort: the current sclk from rocm-smi, run as a child process.  Skipped
+    under a profiler, whose preloaded library would initialise the GPU in the
+    child before rocm-smi's interpreter starts."""
+    if "rocprof" in os.environ.get("LD_PRELOAD", ""):
+        return None
     try:
         out = subprocess.run(["rocm-smi", "--showclocks"], capture_output=True, text=True, timeout=20).stdout
         for line in out.splitlines():
@@ -141,7 +145,7 @@ def main():
         print("bench.py measures one GPU: this build streams the layer store into a single MI355X; "
               "runs on more than one GPU are not part of it", file=sys.stderr)
         sys.exit(2)
-    clock = gpu_clock_mhz()
+    import threading
 
     import numpy as np
     import torch
@@ -174,11 +178,15 @@ def main():
     torch.cuda.synchronize()
     sess.reset_stats()
     torch.cuda.synchronize()
+    clock = [None]
+    sampler = threading.Thread(target=lambda: (time.sleep(0.2), clock.__setitem__(0, gpu_clock_mhz())))
     t0 = time.perf_counter()
+    sampler.start()   # samples the clock while the timed steps run
     for i in range(args.steps):
         sess.sft_step(ids, lora, grads, loss)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
+    sampler.join()
     st = sess.stats()
     loss_v = float(loss.item())
     print(f"[bench] {args.steps} steps in {elapsed:.3f} s, loss {loss_v:.4f}", file=sys.stderr, flush=True)
@@ -230,7 +238,7 @@ def main():
                 "copy_overlapped_by_layer_compute": round(st["overlap_ms"] / st["copy_ms"], 4) if st["copy_ms"] else None,
                 "layer_compute_ms_per_step": round(st["compute_ms"] / steps, 3)},
         "peak_hbm_GB": round(torch.cuda.max_memory_allocated() / 1e9, 3),
-        "gpu_clock": clock,
+        "gpu_clock": clock[0],
         "loss": round(loss_v, 5),
     }
     if args.dpo:
