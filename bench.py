@@ -31,6 +31,10 @@ sys.path.insert(0, ROOT)
 
 METRIC = "streamed QLoRA SFT tokens/sec (8B-shape, seq 512); % H2D BW and % MFMA peak"
 BF16_PEAK_TFLOPS = 2500.0       # MI355X dense bf16 MFMA
+# HBM bytes per launch of the forward dequant-GEMM, from rocprofv3 FETCH_SIZE /
+# WRITE_SIZE passes scaled by a known-size copy (profiles/hbm_traffic_dequant_gemm_8b.md);
+# valid for the kernels they were taken on, keyed by sequence length.
+TRAFFIC_BYTES_PER_LAUNCH = {512: 148.2e6, 4096: 787.5e6}
 PCIE_GEN5_X16_GBPS = 64.0       # theoretical per direction
 
 
@@ -140,7 +144,20 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--dpo", action="store_true", help="also time DPO steps (2 x seq, shared 128-token prompt)")
     ap.add_argument("--threads", type=int, default=min(16, os.cpu_count() or 1))
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="only copy a device buffer of this many MiB 3 times and exit: the known-size "
+                         "reference that scales the FETCH_SIZE / WRITE_SIZE counters")
     args = ap.parse_args()
+    if args.copy_probe_mib:
+        import torch
+        n = args.copy_probe_mib << 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_probe_bytes": n, "copies": 3}))
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this build streams the layer store into a single MI355X; "
               "runs on more than one GPU are not part of it", file=sys.stderr)
@@ -225,7 +242,8 @@ def main():
                      "achieved": round(dom["tflops"], 2) if dom["tflops"] else None,
                      "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(dom["tflops"] / BF16_PEAK_TFLOPS, 4) if dom["tflops"] else None,
-                     "traffic": None},
+                     "traffic": (TRAFFIC_BYTES_PER_LAUNCH.get(S) if dom is k_fwd and B == 1 else None),
+                     "traffic_unit": "HBM bytes per launch"},
         "kernels": {"dq_fwd": k_fwd, "dq_dx": k_dx},
         "h2d": {"bytes_per_step": st["h2d_bytes"] // steps, "layer_loads_per_step": st["layer_loads"] / steps,
                 "isolated_GBps": round(iso, 2),
