@@ -6,11 +6,10 @@ step computes.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
 does.  It shares no code with the HIP library and imports nothing from the
 package.
 
-Streaming is a reordering of when weights reach the device and changes no
-value (page "Soup ... radar note", section "In detail": the streamed result is
-"just a reordering" with zero difference against the resident run), so the
-oracle is simply the un-streamed computation: dequantise, run the decoder,
-back-propagate to the LoRA matrices.
+Streaming only changes when weights reach the device, not any value (page
+"Soup ... radar note", section "In detail", reports zero difference against
+the resident run), so the oracle is simply the un-streamed computation:
+dequantise, run the decoder, back-propagate to the LoRA matrices.
 
 Pins (what the oracle is checked against, in ``tests/test_oracle_*.py``):
   nf4.codebook      -- normal-CDF spacing of the levels (scipy ndtr), exact
@@ -19,6 +18,9 @@ Pins (what the oracle is checked against, in ``tests/test_oracle_*.py``):
   nf4.quantize      -- exact-rational optimality of every chosen code, absmax
                        element maps to an end code, idempotence, zero blocks.
   nf4.dequant       -- exact product in float64 + independent integer rounding.
+  nf4.double_quant  -- exact-rational nearest 8-bit code, group max -> 255, the
+                       s/2 error bound, zero groups, and the 8B record size
+                       against the pages' 3.60 GB / 32 layers.
   model.*           -- fp64 finite differences of the loss (LoRA A/B and the
                        embedded input), torch autograd on fp64, library
                        attention / cross-entropy, B = 0 identities, the

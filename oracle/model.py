@@ -76,12 +76,16 @@ class Model:
     final_norm: np.ndarray      # [d]
 
 
-def dequant_layer(cfg, weights_fp32, norm_attn, norm_mlp):
-    """Quantise the seven float32 weights with the oracle's NF4 and dequantise."""
+def dequant_layer(cfg, weights_fp32, norm_attn, norm_mlp, absmax="f32"):
+    """Quantise the seven float32 weights with the oracle's NF4 and dequantise;
+    absmax="dq8" double-quantises each weight's absmax first."""
     W = {}
     for name, w in zip(NAMES, weights_fp32):
-        codes, absmax = nf4.quantize(w)
-        W[name] = nf4.dequant(codes, absmax, w.shape)
+        codes, amax = nf4.quantize(w)
+        if absmax == "dq8":
+            W[name] = nf4.dequant_dq(codes, *nf4.double_quant(amax), w.shape)
+        else:
+            W[name] = nf4.dequant(codes, amax, w.shape)
     return {"W": W, "norm_attn": np.asarray(norm_attn, np.float32),
             "norm_mlp": np.asarray(norm_mlp, np.float32)}
 

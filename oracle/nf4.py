@@ -26,6 +26,16 @@ quantise
 dequantise
     w32 = float32(cb[c] * a) (one float32 multiply), then bf16 round to nearest
     even.
+double quantisation (the store of 112.5 MB per 8B layer)
+    The pages' pinned store is 3.60 GB for 32 layers and the device buffers
+    113 MB each (page "Fine tune an 8B model on a 4GB laptop GPU (Soup
+    setup)", section "Step 2, train"), which is NF4 codes plus 8-bit absmax
+    scales, QLoRA's double quantisation; the pages give no format, so the
+    plainest one is taken: each weight's float32 absmax array is cut into
+    groups of 256 consecutive entries (the last may be shorter); per group
+    s = float32(max(a) / 255) and q = clamp(rint(float32(a / s)), 0, 255)
+    (round half to even; s = 0 gives q = 0); the decoded absmax is
+    float32(float32(q) * s).  Codes are chosen with the exact absmax first.
 """
 from __future__ import annotations
 
@@ -112,3 +122,39 @@ def dequant_bits(codes: np.ndarray, absmax: np.ndarray) -> np.ndarray:
 def dequant(codes: np.ndarray, absmax: np.ndarray, shape) -> np.ndarray:
     """bf16-valued float32 array of the dequantised weight in ``shape``."""
     return bf16_bits_to_f32(dequant_bits(codes, absmax)).reshape(shape)
+
+
+# ---------------------------------------------------------------- double quantisation
+DQ_GROUP = 256
+
+
+def double_quant(absmax: np.ndarray):
+    """Second-level quantisation of one weight's absmax array.
+
+    Returns (q8 uint8 [nb], scales float32 [ceil(nb / 256)]).
+    """
+    a = np.ascontiguousarray(absmax, dtype=np.float32).reshape(-1)
+    nb = a.size
+    ng = -(-nb // DQ_GROUP)
+    g = np.zeros(ng * DQ_GROUP, np.float32)
+    g[:nb] = a
+    g = g.reshape(ng, DQ_GROUP)
+    c = g.max(axis=1)
+    s = (c / np.float32(255.0)).astype(np.float32)
+    x = np.zeros_like(g)
+    nz = s > 0
+    x[nz] = (g[nz] / s[nz, None]).astype(np.float32)
+    q = np.clip(np.rint(x), 0, 255).astype(np.uint8).reshape(-1)[:nb]
+    return q, s
+
+
+def dq_absmax(q8: np.ndarray, scales: np.ndarray) -> np.ndarray:
+    """Decoded absmax: float32(float32(q) * s_group)."""
+    q = np.asarray(q8, dtype=np.uint8).reshape(-1).astype(np.float32)
+    s = np.asarray(scales, dtype=np.float32).reshape(-1)
+    return (q * s[np.arange(q.size) // DQ_GROUP]).astype(np.float32)
+
+
+def dequant_dq(codes: np.ndarray, q8: np.ndarray, scales: np.ndarray, shape) -> np.ndarray:
+    """Dequantise NF4 codes with double-quantised absmax (bf16 values as float32)."""
+    return dequant(codes, dq_absmax(q8, scales), shape)

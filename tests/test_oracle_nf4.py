@@ -178,3 +178,64 @@ def test_quantize_dequant_idempotent():
 def test_quantize_rejects_ragged():
     with pytest.raises(ValueError):
         nf4.quantize(np.zeros(65, np.float32))
+
+
+# ---------------------------------------------------------------- double quantisation
+def _absmax_like(seed, nb):
+    rng = np.random.default_rng(seed)
+    return np.abs(rng.normal(0, 0.02, (nb, 64))).max(axis=1).astype(np.float32)
+
+
+@pytest.mark.parametrize("nb", [256, 1000, 1])
+def test_dq_code_is_exact_nearest_multiple(nb):
+    """Each 8-bit code is an integer j in [0, 255] nearest to a / s in exact
+    rational arithmetic (ties either way); the group maximum maps to 255."""
+    a = _absmax_like(3, nb)
+    q, s = nf4.double_quant(a)
+    assert q.dtype == np.uint8 and q.shape == (nb,) and s.shape == (-(-nb // 256),)
+    for i in range(0, nb, max(1, nb // 200)):
+        sg = Fraction(float(s[i // 256]))
+        x = Fraction(float(a[i])) / sg
+        assert abs(Fraction(int(q[i])) - x) <= Fraction(1, 2) + Fraction(1, 10**6), (i, q[i], float(x))
+    for gi in range(len(s)):
+        grp = a[gi * 256:(gi + 1) * 256]
+        assert q[gi * 256 + int(np.argmax(grp))] == 255
+        assert s[gi] == np.float32(np.float32(grp.max()) / np.float32(255))
+
+
+def test_dq_decoded_error_bound():
+    """|a_hat - a| <= s/2 (plus float32 rounding of the product): the linear
+    8-bit grid of the group max, exactly."""
+    a = _absmax_like(4, 4096)
+    q, s = nf4.double_quant(a)
+    ah = nf4.dq_absmax(q, s)
+    sg = s[np.arange(a.size) // 256].astype(np.float64)
+    err = np.abs(ah.astype(np.float64) - a.astype(np.float64))
+    assert np.all(err <= 0.5 * sg * (1 + 1e-6) + np.spacing(a.astype(np.float32)).astype(np.float64))
+    # the decoded value is exactly the float32 product q * s
+    want = np.array([Fraction(int(qi)) * Fraction(float(si)) for qi, si in zip(q[:64], sg[:64])])
+    assert all(np.float32(float(w)) == h for w, h in zip(want, ah[:64]))
+
+
+def test_dq_zero_group_and_short_tail():
+    a = np.concatenate([np.zeros(256, np.float32), _absmax_like(5, 100)])
+    q, s = nf4.double_quant(a)
+    assert s[0] == 0 and not np.any(q[:256]) and not np.any(nf4.dq_absmax(q, s)[:256])
+    assert s.shape == (2,) and q[256 + int(np.argmax(a[256:]))] == 255
+
+
+def test_dq_store_size_matches_the_pages():
+    """8B-shaped record with 8-bit absmax + one float32 scale per 256 blocks:
+    codes + absmax codes + scales + two bf16 norms (256-byte aligned regions)
+    must come to the pages' 3.60 GB / 32 = 112.5 MB per layer (within the
+    rounding of the printed 3.60), where float32 absmax gives 122.7 MB."""
+    d, I, qd, kvd = 4096, 14336, 4096, 1024
+    numel = [qd * d, kvd * d, kvd * d, d * qd, I * d, I * d, d * I]
+    al = lambda n: -(-n // 256) * 256
+    codes = sum(al(n // 2) for n in numel)
+    dq = sum(al(n // 64) for n in numel) + sum(al(4 * (-(-(n // 64) // 256))) for n in numel)
+    norms = 2 * al(2 * d)
+    f32 = codes + sum(al(n // 64 * 4) for n in numel) + norms
+    rec = codes + dq + norms
+    assert abs(rec * 32 / 3.60e9 - 1) < 0.0014, rec
+    assert abs(f32 - 122_699_776) < 4096
