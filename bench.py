@@ -54,8 +54,8 @@ def gpu_clock_mhz():
     return None
 
 
-def build_store(q, synth, cfg, threads):
-    store = q.Store(cfg)
+def build_store(q, synth, cfg, threads, absmax):
+    store = q.Store(cfg, absmax=absmax)
     per = max(1, threads // 4)
 
     def one(l):
@@ -141,6 +141,9 @@ def main():
     ap.add_argument("--seq", type=int, default=512)
     ap.add_argument("--batch", type=int, default=1)
     ap.add_argument("--mode", choices=["streamed", "resident"], default="streamed")
+    ap.add_argument("--absmax", choices=["dq8", "f32"], default="dq8",
+                    help="store format: double-quantised absmax (112.5 MB per 8B layer, the pages' store) "
+                         "or float32 absmax (122.7 MB)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--dpo", action="store_true", help="also time DPO steps (2 x seq, shared 128-token prompt)")
     ap.add_argument("--threads", type=int, default=min(16, os.cpu_count() or 1))
@@ -174,7 +177,7 @@ def main():
     B, S = args.batch, args.seq
     T = B * S
     t_setup = time.perf_counter()
-    store = build_store(q, synth, cfg, args.threads)
+    store = build_store(q, synth, cfg, args.threads, args.absmax)
     print(f"[bench] store built: {cfg.L} x {store.record_bytes} B in {time.perf_counter() - t_setup:.1f} s",
           file=sys.stderr, flush=True)
     emb = synth.embedding(cfg, threads=args.threads).cuda()
@@ -220,6 +223,8 @@ def main():
             "launches": st["dq_dx_launches"], "avg_us": 1e3 * st["dq_dx_ms"] / max(1, st["dq_dx_launches"]),
             "tflops": st["dq_dx_gflop"] / st["dq_dx_ms"] if st["dq_dx_ms"] else None}
     dom = k_fwd if st["dq_fwd_ms"] >= st["dq_dx_ms"] else k_dx
+    absmax_desc = ("double-quantised absmax: 8-bit codes + float32 scale per 256 blocks" if args.absmax == "dq8"
+                   else "float32 absmax")
     out = {
         "metric": METRIC,
         "value": round(T * args.steps / elapsed, 2),
@@ -234,10 +239,11 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": (f"8B-shaped streamed QLoRA SFT step: 32 layers (hidden 4096, 32/8 heads x 128, "
-                                f"SwiGLU 14336), NF4 block-64 fp32-absmax store in pinned host memory streamed "
-                                f"through 2 device slots, bf16 embedding + LM head 128256 x 4096 resident, "
-                                f"LoRA r64 alpha16 on 7 linears"),
-                   "global_batch": B, "seq_len": S, "parallelism": "single GPU", "mode": args.mode},
+                                f"SwiGLU 14336), NF4 block-64 store ({absmax_desc}, {store.record_bytes / 1e6:.1f} MB "
+                                f"per layer) in pinned host memory streamed through 2 device slots, bf16 embedding + "
+                                f"LM head 128256 x 4096 resident, LoRA r64 alpha16 on 7 linears"),
+                   "global_batch": B, "seq_len": S, "parallelism": "single GPU", "mode": args.mode,
+                   "absmax": args.absmax},
         "roofline": {"bound": "mfma", "kernel": dom["name"],
                      "achieved": round(dom["tflops"], 2) if dom["tflops"] else None,
                      "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",

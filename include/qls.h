@@ -61,6 +61,9 @@ enum {
 
 enum { QLS_STREAMED = 0, QLS_RESIDENT = 1 };
 
+/* Absmax format of a store (see qls_store_create_fmt). */
+enum { QLS_ABSMAX_F32 = 0, QLS_ABSMAX_DQ8 = 1 };
+
 /* Module order used everywhere (records, LoRA packing): */
 enum { QLS_Q = 0, QLS_K, QLS_V, QLS_O, QLS_GATE, QLS_UP, QLS_DOWN, QLS_NMOD };
 
@@ -105,7 +108,10 @@ typedef struct qls_resident {
 
 /* Read-only view of one layer record in the pinned host store.
  * codes[m]: NF4 codes of module m, numel/2 bytes, element 2k in the high
- * nibble of byte k; absmax[m]: numel/64 float32; norms: bf16 [hidden]. */
+ * nibble of byte k; norms: bf16 [hidden].  QLS_ABSMAX_F32 stores: absmax[m]
+ * numel/64 float32 (absmax_q8 / absmax_scale NULL).  QLS_ABSMAX_DQ8 stores:
+ * absmax_q8[m] numel/64 uint8 and absmax_scale[m] ceil(numel/64/256) float32
+ * (absmax NULL). */
 typedef struct qls_layer_view {
   const uint8_t* codes[QLS_NMOD];
   const float* absmax[QLS_NMOD];
@@ -113,6 +119,9 @@ typedef struct qls_layer_view {
   const uint16_t* norm_mlp;
   const void* record;
   int64_t record_bytes;
+  int32_t absmax_format;
+  const uint8_t* absmax_q8[QLS_NMOD];
+  const float* absmax_scale[QLS_NMOD];
 } qls_layer_view;
 
 typedef struct qls_stats {
@@ -165,6 +174,18 @@ int qls_nf4_quantize(const float* h_w, int64_t n, uint8_t* h_codes, float* h_abs
 int qls_nf4_dequant_dev(const uint8_t* d_codes, const float* d_absmax, int64_t n,
                         uint16_t* d_out, void* stream);
 
+/* Double quantisation of an absmax array ([P2] "Step 2, train": a 3.60 GB
+ * pinned store for 32 layers and 113 MB device buffers, i.e. NF4 codes plus
+ * 8-bit absmax; the format is this library's reading).  Per group of 256
+ * consecutive entries (the last may be shorter): s = float32(max / 255),
+ * q = clamp(rint(float32(a / s)), 0, 255) with ties to even, s = 0 gives q = 0.
+ * h_q8: nblocks bytes; h_scales: ceil(nblocks / 256) float32.  Host only. */
+int qls_nf4_double_quant(const float* h_absmax, int64_t nblocks, uint8_t* h_q8, float* h_scales);
+/* Device decode: d_out[i] = float32(float32(q8[i]) * scales[i / 256]), the
+ * absmax the kernels use for a QLS_ABSMAX_DQ8 store.  Asynchronous on stream. */
+int qls_nf4_absmax_expand_dev(const uint8_t* d_q8, const float* d_scales, int64_t nblocks,
+                              float* d_out, void* stream);
+
 /* ---------------------------------------------------------------- one QLoRA linear
  * y = bf16( x W^T + s * u B^T ),  u = bf16( x A^T ),  s = alpha / r,
  * with W the dequantised NF4 weight [N x K].  x bf16 [T x K]; A bf16 [r x K];
@@ -187,9 +208,13 @@ int qls_linear_bwd(const uint8_t* d_codes, const float* d_absmax, int N, int K,
                    float* d_dx, float* d_dA, float* d_dB, void* d_ws, void* stream);
 
 /* ---------------------------------------------------------------- sizes */
-/* Bytes of one layer record: 7 code blobs, 7 absmax arrays, 2 bf16 norms,
- * each 256-byte aligned. */
+/* Bytes of one layer record: the 7 code blobs, the absmax data (QLS_ABSMAX_F32:
+ * 7 float32 arrays; QLS_ABSMAX_DQ8: 7 uint8 arrays then 7 float32 scale
+ * arrays), 2 bf16 norms, each region 256-byte aligned.  The _fmt form takes the
+ * format; the plain form is QLS_ABSMAX_F32.  At the 8B shape: 122,699,776 B
+ * (F32) and 112,529,408 B (DQ8). */
 int64_t qls_layer_record_bytes(const qls_model_cfg* cfg);
+int64_t qls_layer_record_bytes_fmt(const qls_model_cfg* cfg, int absmax_format);
 /* Length of the packed LoRA vector: layer-major, modules q,k,v,o,gate,up,down,
  * each A [r x in] row-major then B [out x r] row-major. */
 int64_t qls_lora_numel(const qls_model_cfg* cfg);
@@ -202,13 +227,20 @@ int64_t qls_lora_numel(const qls_model_cfg* cfg);
  * creation fails with QLS_ENOPIN.  The store owns its host memory and must
  * outlive every session created over it. */
 int qls_store_create(const qls_model_cfg* cfg, uint64_t max_pinned_bytes, qls_store** out);
+/* Same, with the absmax format: QLS_ABSMAX_F32 (qls_store_create) or
+ * QLS_ABSMAX_DQ8 (absmax double-quantised when a layer is set; the session
+ * decodes it on the device when a record arrives, before the layer's first
+ * kernel).  Errors as qls_store_create, plus QLS_EINVAL for an unknown format. */
+int qls_store_create_fmt(const qls_model_cfg* cfg, int absmax_format, uint64_t max_pinned_bytes,
+                         qls_store** out);
 /* Quantise and pack one layer.  w[m]: float32 [out x in] of module m; norms
  * bf16 [hidden].  Inputs are borrowed for the call.  n_threads as for
  * qls_nf4_quantize.  Errors: QLS_EINVAL (layer out of range / NULL). */
 int qls_store_set_layer_fp32(qls_store* st, int layer, const float* const h_w[QLS_NMOD],
                              const uint16_t* h_norm_attn, const uint16_t* h_norm_mlp,
                              int n_threads);
-/* Pack a layer that is already quantised (codes / absmax as in qls_nf4_quantize). */
+/* Pack a layer that is already quantised (codes / absmax as in qls_nf4_quantize;
+ * a QLS_ABSMAX_DQ8 store double-quantises the absmax as it packs). */
 int qls_store_set_layer_nf4(qls_store* st, int layer, const uint8_t* const h_codes[QLS_NMOD],
                             const float* const h_absmax[QLS_NMOD],
                             const uint16_t* h_norm_attn, const uint16_t* h_norm_mlp);

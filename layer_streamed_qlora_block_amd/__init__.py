@@ -20,6 +20,7 @@ _lib = C.CDLL(LIB_PATH)
 
 QLS_OK, QLS_EINVAL, QLS_ENOMEM, QLS_ENOPIN, QLS_EHIP, QLS_ESTATE, QLS_EUNSUPPORTED = 0, -1, -2, -3, -4, -5, -6
 QLS_STREAMED, QLS_RESIDENT = 0, 1
+QLS_ABSMAX_F32, QLS_ABSMAX_DQ8 = 0, 1
 NMOD = 7
 MODULES = ("q", "k", "v", "o", "gate", "up", "down")
 DBG_POISON_ON_RELEASE, DBG_COPY_DELAY, DBG_COMPUTE_DELAY, DBG_NO_REUSE = 1, 2, 4, 8
@@ -49,7 +50,9 @@ class Resident(C.Structure):
 
 class LayerView(C.Structure):
     _fields_ = [("codes", C.c_void_p * NMOD), ("absmax", C.c_void_p * NMOD), ("norm_attn", C.c_void_p),
-                ("norm_mlp", C.c_void_p), ("record", C.c_void_p), ("record_bytes", C.c_int64)]
+                ("norm_mlp", C.c_void_p), ("record", C.c_void_p), ("record_bytes", C.c_int64),
+                ("absmax_format", C.c_int32), ("absmax_q8", C.c_void_p * NMOD),
+                ("absmax_scale", C.c_void_p * NMOD)]
 
 
 class Stats(C.Structure):
@@ -73,12 +76,16 @@ _SIG = {
     "qls_nf4_codebook": (_I, [_P]),
     "qls_nf4_quantize": (_I, [_P, _I64, _P, _P, _I]),
     "qls_nf4_dequant_dev": (_I, [_P, _P, _I64, _P, _P]),
+    "qls_nf4_double_quant": (_I, [_P, _I64, _P, _P]),
+    "qls_nf4_absmax_expand_dev": (_I, [_P, _P, _I64, _P, _P]),
     "qls_linear_ws_bytes": (_I64, [_I, _I, _I, _I]),
     "qls_linear_fwd": (_I, [_P, _P, _I, _I, _P, _I, _P, _P, _I, _F, _P, _P, _P, _P]),
     "qls_linear_bwd": (_I, [_P, _P, _I, _I, _P, _P, _P, _I, _P, _P, _I, _F, _P, _P, _P, _P, _P]),
     "qls_layer_record_bytes": (_I64, [C.POINTER(ModelCfg)]),
+    "qls_layer_record_bytes_fmt": (_I64, [C.POINTER(ModelCfg), _I]),
     "qls_lora_numel": (_I64, [C.POINTER(ModelCfg)]),
     "qls_store_create": (_I, [C.POINTER(ModelCfg), C.c_uint64, C.POINTER(_P)]),
+    "qls_store_create_fmt": (_I, [C.POINTER(ModelCfg), _I, C.c_uint64, C.POINTER(_P)]),
     "qls_store_set_layer_fp32": (_I, [_P, _I, _P * NMOD, _P, _P, _I]),
     "qls_store_set_layer_nf4": (_I, [_P, _I, _P * NMOD, _P * NMOD, _P, _P]),
     "qls_store_layer_view": (_I, [_P, _I, C.POINTER(LayerView)]),
@@ -160,6 +167,19 @@ def qls_nf4_dequant_dev(d_codes, d_absmax, n, d_out, stream=None):
     _check(_lib.qls_nf4_dequant_dev(_ptr(d_codes), _ptr(d_absmax), n, _ptr(d_out), _stream(stream)))
 
 
+def qls_nf4_double_quant(absmax):
+    import numpy as np
+    a = np.ascontiguousarray(absmax, dtype=np.float32).reshape(-1)
+    q8 = np.empty(a.size, np.uint8)
+    scales = np.empty(-(-a.size // 256), np.float32)
+    _check(_lib.qls_nf4_double_quant(a.ctypes.data, a.size, q8.ctypes.data, scales.ctypes.data))
+    return q8, scales
+
+
+def qls_nf4_absmax_expand_dev(d_q8, d_scales, nblocks, d_out, stream=None):
+    _check(_lib.qls_nf4_absmax_expand_dev(_ptr(d_q8), _ptr(d_scales), nblocks, _ptr(d_out), _stream(stream)))
+
+
 def qls_linear_ws_bytes(T, N, K, r) -> int:
     return _check(_lib.qls_linear_ws_bytes(T, N, K, r))
 
@@ -178,6 +198,10 @@ def qls_layer_record_bytes(mc: ModelCfg) -> int:
     return _check(_lib.qls_layer_record_bytes(C.byref(mc)))
 
 
+def qls_layer_record_bytes_fmt(mc: ModelCfg, absmax_format: int) -> int:
+    return _check(_lib.qls_layer_record_bytes_fmt(C.byref(mc), absmax_format))
+
+
 def qls_lora_numel(mc: ModelCfg) -> int:
     return _check(_lib.qls_lora_numel(C.byref(mc)))
 
@@ -185,6 +209,12 @@ def qls_lora_numel(mc: ModelCfg) -> int:
 def qls_store_create(mc: ModelCfg, max_pinned_bytes: int = 0):
     h = _P()
     _check(_lib.qls_store_create(C.byref(mc), max_pinned_bytes, C.byref(h)))
+    return h
+
+
+def qls_store_create_fmt(mc: ModelCfg, absmax_format: int, max_pinned_bytes: int = 0):
+    h = _P()
+    _check(_lib.qls_store_create_fmt(C.byref(mc), absmax_format, max_pinned_bytes, C.byref(h)))
     return h
 
 

@@ -33,6 +33,15 @@ int qls_nf4_dequant_dev(const uint8_t* d_codes, const float* d_absmax, int64_t n
   return QLS_OK;
 }
 
+int qls_nf4_absmax_expand_dev(const uint8_t* d_q8, const float* d_scales, int64_t nblocks, float* d_out,
+                              void* stream) {
+  if (!d_q8 || !d_scales || !d_out) return fail(QLS_EINVAL, "NULL buffer");
+  if (nblocks < 0) return fail(QLS_EINVAL, "nblocks must be non-negative");
+  absmax_expand_flat_launch(d_q8, d_scales, nblocks, d_out, (hipStream_t)stream);
+  QLS_HIP(hipGetLastError());
+  return QLS_OK;
+}
+
 int64_t qls_linear_ws_bytes(int T, int N, int K, int r) {
   if (T <= 0 || N <= 0 || K <= 0 || r <= 0) return fail(QLS_EINVAL, "sizes must be positive");
   return linear_ws_bytes(T, N, K, r);

@@ -41,16 +41,34 @@ struct Shape {
 };
 bool make_shape(const qls_model_cfg* c, Shape* out, std::string* why);
 
-// One layer record: all code blobs back to back (module order), then all
-// absmax arrays back to back, then the two bf16 norms; regions 256-B aligned.
-// Back-to-back blobs make q|k|v and gate|up single row-major NF4 matrices.
+// One layer record: all code blobs back to back (module order), then the
+// absmax data, then the two bf16 norms; regions 256-B aligned.  Back-to-back
+// blobs make q|k|v and gate|up single row-major NF4 matrices.
+//   QLS_ABSMAX_F32: all float32 absmax arrays back to back (absmax_off).
+//   QLS_ABSMAX_DQ8: all 8-bit absmax codes back to back (q8_off), then all
+//   float32 group scales back to back (scale_off, one per 256 blocks of a
+//   module).  The session expands them into float32 arrays laid out as
+//   exp_off (back to back, the F32 layout shifted to 0) before a layer's use.
 struct RecordLayout {
+  int fmt;
   int64_t code_off[QLS_NMOD];
-  int64_t absmax_off[QLS_NMOD];
+  int64_t absmax_off[QLS_NMOD];            // F32 only
+  int64_t q8_off[QLS_NMOD], scale_off[QLS_NMOD];   // DQ8 only
+  int64_t exp_off[QLS_NMOD];               // float32 absmax, relative (both formats)
+  int64_t nblocks;                          // absmax entries of the layer
+  int64_t block_start[QLS_NMOD + 1];        // first absmax index of each module
+  int64_t scale_start[QLS_NMOD];            // first group scale of each module
   int64_t norm_attn_off, norm_mlp_off;
   int64_t bytes;
 };
-RecordLayout record_layout(const Shape& sh);
+RecordLayout record_layout(const Shape& sh, int fmt);
+// Second-level absmax quantisation (host, float32 IEEE, no contraction).
+void nf4_double_quant_host(const float* absmax, int64_t nb, uint8_t* q8, float* scales);
+// Device expansion of one layer's DQ8 absmax into float32 (layout exp_off).
+int absmax_expand_launch(const uint8_t* rec, const RecordLayout& lay, float* out, hipStream_t st);
+// Device expansion of one array: out[i] = float32(q8[i] * scales[i / 256]).
+int absmax_expand_flat_launch(const uint8_t* q8, const float* scales, int64_t nb, float* out,
+                              hipStream_t st);
 
 // Offsets (elements) of each module's A and B in the packed float32 LoRA
 // vector, per layer, plus the per-layer stride.

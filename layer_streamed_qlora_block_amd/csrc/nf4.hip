@@ -52,6 +52,28 @@ __global__ void __launch_bounds__(256) nf4_dequant_kernel(const uint32_t* __rest
                  pack2_bf16(v[6], v[7])};
 }
 
+// Double-quantised absmax decode: out[i] = float32(q8[i] * s[group]), one
+// IEEE float32 multiply.  The layer form walks the seven modules of a record:
+// the 8-bit codes and the expanded floats are back to back over the layer, the
+// group scales restart their 256-block grouping at each module.
+struct ExpandArgs {
+  const uint8_t* q8;             // the layer's 8-bit codes (module order, back to back)
+  const float* scales;           // the layer's group scales (module order, back to back)
+  int64_t block_start[QLS_NMOD + 1];
+  int64_t scale_start[QLS_NMOD];
+  float* out;
+};
+
+__global__ void __launch_bounds__(256) absmax_expand_kernel(ExpandArgs a) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= a.block_start[QLS_NMOD]) return;
+  int m = 0;
+#pragma unroll
+  for (int j = 1; j < QLS_NMOD; ++j) m += i >= a.block_start[j];
+  const int64_t local = i - a.block_start[m];
+  a.out[i] = (float)a.q8[i] * a.scales[a.scale_start[m] + local / 256];
+}
+
 std::once_flag g_cb_once;
 float* g_cb_dev = nullptr;
 int g_cb_err = 0;
@@ -95,5 +117,29 @@ int nf4_dequant_launch(const uint8_t* codes, const float* absmax, int64_t n, uin
   hipLaunchKernelGGL(nf4_dequant_kernel, dim3((unsigned)ceil_div64(n8, 256)), dim3(256), 0, st,
                      reinterpret_cast<const uint32_t*>(codes), absmax, n8,
                      reinterpret_cast<u32x4*>(out), cb);
+  return 0;
+}
+
+int absmax_expand_launch(const uint8_t* rec, const RecordLayout& lay, float* out, hipStream_t st) {
+  ExpandArgs a{};
+  a.q8 = rec + lay.q8_off[0];
+  a.scales = reinterpret_cast<const float*>(rec + lay.scale_off[0]);
+  for (int m = 0; m <= QLS_NMOD; ++m) a.block_start[m] = lay.block_start[m];
+  for (int m = 0; m < QLS_NMOD; ++m) a.scale_start[m] = lay.scale_start[m];
+  a.out = out;
+  if (lay.nblocks == 0) return 0;
+  hipLaunchKernelGGL(absmax_expand_kernel, dim3((unsigned)ceil_div64(lay.nblocks, 256)), dim3(256), 0, st, a);
+  return 0;
+}
+
+int absmax_expand_flat_launch(const uint8_t* q8, const float* scales, int64_t nb, float* out,
+                              hipStream_t st) {
+  ExpandArgs a{};
+  a.q8 = q8;
+  a.scales = scales;
+  for (int m = 1; m <= QLS_NMOD; ++m) a.block_start[m] = nb;   // one module holds everything
+  a.out = out;
+  if (nb == 0) return 0;
+  hipLaunchKernelGGL(absmax_expand_kernel, dim3((unsigned)ceil_div64(nb, 256)), dim3(256), 0, st, a);
   return 0;
 }

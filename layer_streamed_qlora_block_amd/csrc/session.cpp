@@ -37,6 +37,7 @@ struct Plan {
   int64_t g, dh, dn, dyb, dgu, dattn, dqf, dkf, dvf, dqkv, du, xo;
   int64_t lbf, hf, stats, lse_t, tgt_logit, logp, logp_ref, roww, tgt, ids, dlog, dhf, part;
   int64_t xref0, xref1, scal, rope;
+  int64_t amax;   // two float32 absmax expansions (double-quantised stores only)
   int64_t total;
 };
 
@@ -108,6 +109,7 @@ Plan make_plan(const Shape& sh, const RecordLayout& lay, const qls_run_cfg& run,
   p.xref1 = take(T * d * 2);
   p.scal = take(64);
   p.rope = take((int64_t)z.Smax * (sh.c.head_dim / 2) * 2 * 4);
+  p.amax = take(lay.fmt == QLS_ABSMAX_DQ8 ? 2 * lay.nblocks * 4 : 0);
   p.total = off;
   return p;
 }
@@ -146,6 +148,11 @@ struct qls_session {
   qls_resident res;
   hipEvent_t copied[2] = {}, released[2] = {};
   int slot_layer[2] = {-1, -1};
+  // Double-quantised stores: expansion buffer e = layer & 1 holds the float32
+  // absmax of exp_layer[e], decoded from copy number exp_gen[e] of its slot.
+  int64_t slot_gen[2] = {0, 0};
+  int exp_layer[2] = {-1, -1};
+  int64_t exp_gen[2] = {-1, -1};
   uint32_t dbg = 0;
   int delay_us = 0;
   int64_t wall_khz = 100000;
@@ -171,6 +178,7 @@ struct qls_session {
   }
 
   template <class T> T* at(int64_t off) const { return reinterpret_cast<T*>(ws + off); }
+  float* amax_buf(int l) const { return at<float>(p.amax) + (int64_t)(l & 1) * lay.nblocks; }
   uint16_t* ck(int l) const { return at<uint16_t>(p.ckpt) + (int64_t)l * z.Tm * sh.c.hidden; }
   uint16_t* lw(int l) const { return at<uint16_t>(p.lbf) + (int64_t)l * ll.per_layer; }
 
@@ -206,6 +214,7 @@ int prefetch(qls_session* S, int layer) {
   if (S->timing) { QLS_HIP(hipEventRecord(te.b, S->ps)); S->copy_ev.push_back(te); }
   QLS_HIP(hipEventRecord(S->copied[s], S->ps));
   S->slot_layer[s] = layer;
+  S->slot_gen[s] += 1;
   S->loads += 1;
   S->h2d += S->lay.bytes;
   return QLS_OK;
@@ -222,6 +231,18 @@ int acquire(qls_session* S, int layer, const uint8_t** rec, TimedEv* te) {
     }
     QLS_HIP(hipStreamWaitEvent(S->cs, S->copied[s], 0));
     *rec = S->at<uint8_t>(S->p.slots) + s * S->lay.bytes;
+  }
+  if (S->lay.fmt == QLS_ABSMAX_DQ8) {
+    // Decode the 8-bit absmax of this record once per arrival, on the compute
+    // stream (ordered after the copy fence and before the layer's kernels).
+    const int e = layer & 1;
+    const int64_t gen = S->run.mode == QLS_RESIDENT ? 0 : S->slot_gen[e];
+    if (S->exp_layer[e] != layer || S->exp_gen[e] != gen) {
+      if (absmax_expand_launch(*rec, S->lay, S->amax_buf(layer), S->cs))
+        return fail(QLS_EHIP, "absmax expansion launch failed");
+      S->exp_layer[e] = layer;
+      S->exp_gen[e] = gen;
+    }
   }
   if (S->timing) { te->a = S->next_ev(); te->b = S->next_ev(); QLS_HIP(hipEventRecord(te->a, S->cs)); }
   return QLS_OK;
@@ -249,11 +270,15 @@ struct W {
   const uint16_t* nm;
 };
 
-W weights(const qls_session* S, const uint8_t* rec) {
+// The layer's codes and norms in its record; its float32 absmax in the record
+// (F32 store) or in the expansion buffer acquire() decoded it into (DQ8 store).
+W weights(const qls_session* S, const uint8_t* rec, int layer) {
   W w{};
+  const bool dq = S->lay.fmt == QLS_ABSMAX_DQ8;
   for (int m = 0; m < QLS_NMOD; ++m) {
     w.code[m] = rec + S->lay.code_off[m];
-    w.amax[m] = reinterpret_cast<const float*>(rec + S->lay.absmax_off[m]);
+    w.amax[m] = dq ? S->amax_buf(layer) + S->lay.exp_off[m] / 4
+                   : reinterpret_cast<const float*>(rec + S->lay.absmax_off[m]);
   }
   w.na = reinterpret_cast<const uint16_t*>(rec + S->lay.norm_attn_off);
   w.nm = reinterpret_cast<const uint16_t*>(rec + S->lay.norm_mlp_off);
@@ -266,7 +291,7 @@ int fwd_layer(qls_session* S, int l, const uint8_t* rec, const uint16_t* x, uint
               int T, int B, int Sq) {
   const Shape& sh = S->sh;
   const int d = sh.c.hidden, I = sh.c.intermediate, r = sh.c.lora_r;
-  const W w = weights(S, rec);
+  const W w = weights(S, rec, l);
   const uint16_t* lw = S->lw(l);
   hipStream_t st = S->cs;
   uint16_t* n1 = S->at<uint16_t>(S->p.n1);
@@ -334,7 +359,7 @@ int bwd_layer(qls_session* S, int l, const uint8_t* rec, const uint16_t* x, floa
   const Shape& sh = S->sh;
   const int d = sh.c.hidden, I = sh.c.intermediate, r = sh.c.lora_r;
   const float s = sh.s;
-  const W w = weights(S, rec);
+  const W w = weights(S, rec, l);
   const uint16_t* lw = S->lw(l);
   hipStream_t st = S->cs;
   float* gl = grads + (int64_t)l * S->ll.per_layer;

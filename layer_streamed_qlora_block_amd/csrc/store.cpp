@@ -15,7 +15,7 @@
 
 struct qls_store {
   Shape sh;
-  RecordLayout lay;
+  RecordLayout lay;   // lay.fmt: QLS_ABSMAX_F32 or QLS_ABSMAX_DQ8
   uint8_t* host = nullptr;          // n_layers * lay.bytes, hipHostMalloc
   std::vector<char> ready;
 };
@@ -49,13 +49,32 @@ bool make_shape(const qls_model_cfg* c, Shape* o, std::string* why) {
   return true;
 }
 
-RecordLayout record_layout(const Shape& sh) {
+RecordLayout record_layout(const Shape& sh, int fmt) {
   RecordLayout L{};
+  L.fmt = fmt;
   int64_t off = 0;
   for (int m = 0; m < QLS_NMOD; ++m) { L.code_off[m] = off; off += sh.numel[m] / 2; }
   off = align_up(off, 256);
-  for (int m = 0; m < QLS_NMOD; ++m) { L.absmax_off[m] = off; off += sh.numel[m] / 64 * 4; }
-  off = align_up(off, 256);
+  int64_t e = 0, b = 0, g = 0;
+  for (int m = 0; m < QLS_NMOD; ++m) {
+    L.exp_off[m] = e;
+    L.block_start[m] = b;
+    L.scale_start[m] = g;
+    e += sh.numel[m] / 64 * 4;
+    b += sh.numel[m] / 64;
+    g += cdiv(sh.numel[m] / 64, 256);
+  }
+  L.block_start[QLS_NMOD] = b;
+  L.nblocks = b;
+  if (fmt == QLS_ABSMAX_DQ8) {
+    for (int m = 0; m < QLS_NMOD; ++m) L.q8_off[m] = off + L.block_start[m];
+    off = align_up(off + b, 256);
+    for (int m = 0; m < QLS_NMOD; ++m) L.scale_off[m] = off + 4 * L.scale_start[m];
+    off = align_up(off + 4 * g, 256);
+  } else {
+    for (int m = 0; m < QLS_NMOD; ++m) L.absmax_off[m] = off + L.exp_off[m];
+    off = align_up(off + e, 256);
+  }
   L.norm_attn_off = off; off = align_up(off + 2LL * sh.c.hidden, 256);
   L.norm_mlp_off = off; off = align_up(off + 2LL * sh.c.hidden, 256);
   L.bytes = off;
@@ -104,6 +123,23 @@ static void quantize_blocks(const float* w, int64_t b0, int64_t b1, uint8_t* cod
   }
 }
 
+// Second level: per group of 256 absmax values s = f32(max / 255), q =
+// clamp(rint(f32(a / s)), 0, 255) (round half to even), s = 0 -> q = 0.
+void nf4_double_quant_host(const float* a, int64_t nb, uint8_t* q8, float* scales) {
+  for (int64_t g0 = 0, gi = 0; g0 < nb; g0 += 256, ++gi) {
+    const int64_t g1 = std::min<int64_t>(nb, g0 + 256);
+    float c = 0.f;
+    for (int64_t i = g0; i < g1; ++i) c = std::max(c, a[i]);
+    const float sc = c / 255.0f;
+    scales[gi] = sc;
+    for (int64_t i = g0; i < g1; ++i) {
+      if (!(sc > 0.f)) { q8[i] = 0; continue; }
+      const float x = std::nearbyint(a[i] / sc);   // default rounding: nearest, ties to even
+      q8[i] = (uint8_t)std::min(255.f, std::max(0.f, x));
+    }
+  }
+}
+
 void nf4_quantize_host(const float* w, int64_t n, uint8_t* codes, float* absmax, int n_threads) {
   float cb[16];
   nf4_codebook_host(cb);
@@ -122,11 +158,17 @@ void nf4_quantize_host(const float* w, int64_t n, uint8_t* codes, float* absmax,
 // ---------------------------------------------------------------- C ABI
 extern "C" {
 
-int64_t qls_layer_record_bytes(const qls_model_cfg* cfg) {
+int64_t qls_layer_record_bytes_fmt(const qls_model_cfg* cfg, int absmax_format) {
   Shape sh;
   std::string why;
   if (!make_shape(cfg, &sh, &why)) return fail(QLS_EINVAL, why);
-  return record_layout(sh).bytes;
+  if (absmax_format != QLS_ABSMAX_F32 && absmax_format != QLS_ABSMAX_DQ8)
+    return fail(QLS_EINVAL, "absmax_format must be QLS_ABSMAX_F32 or QLS_ABSMAX_DQ8");
+  return record_layout(sh, absmax_format).bytes;
+}
+
+int64_t qls_layer_record_bytes(const qls_model_cfg* cfg) {
+  return qls_layer_record_bytes_fmt(cfg, QLS_ABSMAX_F32);
 }
 
 int64_t qls_lora_numel(const qls_model_cfg* cfg) {
@@ -149,16 +191,26 @@ int qls_nf4_quantize(const float* w, int64_t n, uint8_t* codes, float* absmax, i
   return QLS_OK;
 }
 
-int qls_store_create(const qls_model_cfg* cfg, uint64_t max_pinned_bytes, qls_store** out) {
+int qls_nf4_double_quant(const float* absmax, int64_t nblocks, uint8_t* q8, float* scales) {
+  if (!absmax || !q8 || !scales) return fail(QLS_EINVAL, "NULL buffer");
+  if (nblocks < 0) return fail(QLS_EINVAL, "nblocks must be non-negative");
+  nf4_double_quant_host(absmax, nblocks, q8, scales);
+  return QLS_OK;
+}
+
+int qls_store_create_fmt(const qls_model_cfg* cfg, int absmax_format, uint64_t max_pinned_bytes,
+                         qls_store** out) {
   if (!out) return fail(QLS_EINVAL, "out is NULL");
   *out = nullptr;
   Shape sh;
   std::string why;
   if (!make_shape(cfg, &sh, &why)) return fail(QLS_EINVAL, why);
+  if (absmax_format != QLS_ABSMAX_F32 && absmax_format != QLS_ABSMAX_DQ8)
+    return fail(QLS_EINVAL, "absmax_format must be QLS_ABSMAX_F32 or QLS_ABSMAX_DQ8");
   auto* st = new (std::nothrow) qls_store;
   if (!st) return fail(QLS_ENOMEM, "host allocation failed");
   st->sh = sh;
-  st->lay = record_layout(sh);
+  st->lay = record_layout(sh, absmax_format);
   const uint64_t total = (uint64_t)st->lay.bytes * (uint64_t)cfg->n_layers;
   if (max_pinned_bytes && total > max_pinned_bytes) {
     delete st;
@@ -175,6 +227,20 @@ int qls_store_create(const qls_model_cfg* cfg, uint64_t max_pinned_bytes, qls_st
   return QLS_OK;
 }
 
+int qls_store_create(const qls_model_cfg* cfg, uint64_t max_pinned_bytes, qls_store** out) {
+  return qls_store_create_fmt(cfg, QLS_ABSMAX_F32, max_pinned_bytes, out);
+}
+
+// Write module m's absmax into the record in the store's format.
+static void put_absmax(qls_store* st, uint8_t* rec, int m, const float* absmax) {
+  const int64_t nb = st->sh.numel[m] / 64;
+  if (st->lay.fmt == QLS_ABSMAX_DQ8)
+    nf4_double_quant_host(absmax, nb, rec + st->lay.q8_off[m],
+                          reinterpret_cast<float*>(rec + st->lay.scale_off[m]));
+  else
+    std::memcpy(rec + st->lay.absmax_off[m], absmax, nb * 4);
+}
+
 static int set_norms(qls_store* st, int layer, const uint16_t* na, const uint16_t* nm) {
   uint8_t* rec = st->host + (int64_t)layer * st->lay.bytes;
   std::memcpy(rec + st->lay.norm_attn_off, na, 2 * (size_t)st->sh.c.hidden);
@@ -189,9 +255,17 @@ int qls_store_set_layer_fp32(qls_store* st, int layer, const float* const w[QLS_
   for (int m = 0; m < QLS_NMOD; ++m)
     if (!w[m]) return fail(QLS_EINVAL, "NULL weight");
   uint8_t* rec = st->host + (int64_t)layer * st->lay.bytes;
-  for (int m = 0; m < QLS_NMOD; ++m)
-    nf4_quantize_host(w[m], st->sh.numel[m], rec + st->lay.code_off[m],
-                      reinterpret_cast<float*>(rec + st->lay.absmax_off[m]), n_threads);
+  std::vector<float> amax;
+  for (int m = 0; m < QLS_NMOD; ++m) {
+    if (st->lay.fmt == QLS_ABSMAX_F32) {
+      nf4_quantize_host(w[m], st->sh.numel[m], rec + st->lay.code_off[m],
+                        reinterpret_cast<float*>(rec + st->lay.absmax_off[m]), n_threads);
+    } else {
+      amax.resize(st->sh.numel[m] / 64);
+      nf4_quantize_host(w[m], st->sh.numel[m], rec + st->lay.code_off[m], amax.data(), n_threads);
+      put_absmax(st, rec, m, amax.data());
+    }
+  }
   set_norms(st, layer, na, nm);
   st->ready[layer] = 1;
   return QLS_OK;
@@ -206,7 +280,7 @@ int qls_store_set_layer_nf4(qls_store* st, int layer, const uint8_t* const codes
   for (int m = 0; m < QLS_NMOD; ++m) {
     if (!codes[m] || !absmax[m]) return fail(QLS_EINVAL, "NULL module buffer");
     std::memcpy(rec + st->lay.code_off[m], codes[m], st->sh.numel[m] / 2);
-    std::memcpy(rec + st->lay.absmax_off[m], absmax[m], st->sh.numel[m] / 64 * 4);
+    put_absmax(st, rec, m, absmax[m]);
   }
   set_norms(st, layer, na, nm);
   st->ready[layer] = 1;
@@ -217,9 +291,13 @@ int qls_store_layer_view(const qls_store* st, int layer, qls_layer_view* out) {
   if (!st || !out) return fail(QLS_EINVAL, "NULL argument");
   if (layer < 0 || layer >= st->sh.c.n_layers) return fail(QLS_EINVAL, "layer out of range");
   const uint8_t* rec = st->host + (int64_t)layer * st->lay.bytes;
+  const bool dq = st->lay.fmt == QLS_ABSMAX_DQ8;
+  out->absmax_format = st->lay.fmt;
   for (int m = 0; m < QLS_NMOD; ++m) {
     out->codes[m] = rec + st->lay.code_off[m];
-    out->absmax[m] = reinterpret_cast<const float*>(rec + st->lay.absmax_off[m]);
+    out->absmax[m] = dq ? nullptr : reinterpret_cast<const float*>(rec + st->lay.absmax_off[m]);
+    out->absmax_q8[m] = dq ? rec + st->lay.q8_off[m] : nullptr;
+    out->absmax_scale[m] = dq ? reinterpret_cast<const float*>(rec + st->lay.scale_off[m]) : nullptr;
   }
   out->norm_attn = reinterpret_cast<const uint16_t*>(rec + st->lay.norm_attn_off);
   out->norm_mlp = reinterpret_cast<const uint16_t*>(rec + st->lay.norm_mlp_off);

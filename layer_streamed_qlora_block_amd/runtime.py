@@ -11,10 +11,10 @@ import ctypes as C
 import numpy as np
 import torch
 
-from . import (QLS_RESIDENT, QLS_STREAMED, RunCfg, model_cfg, qls_debug_set, qls_dpo_step,
-               qls_layer_fwd_bwd, qls_layer_record_bytes, qls_logprobs, qls_lora_numel,
+from . import (QLS_ABSMAX_DQ8, QLS_ABSMAX_F32, QLS_RESIDENT, QLS_STREAMED, RunCfg, model_cfg, qls_debug_set,
+               qls_dpo_step, qls_layer_fwd_bwd, qls_layer_record_bytes_fmt, qls_logprobs, qls_lora_numel,
                qls_session_checkpoints, qls_session_create, qls_session_destroy, qls_session_reset_stats,
-               qls_session_stats, qls_sft_step, qls_store_create, qls_store_destroy, qls_store_layer_view,
+               qls_session_stats, qls_sft_step, qls_store_create_fmt, qls_store_destroy, qls_store_layer_view,
                qls_store_set_layer_fp32, qls_store_set_layer_nf4, qls_workspace_bytes)
 
 
@@ -23,12 +23,19 @@ def _np_bf16(t: torch.Tensor) -> np.ndarray:
 
 
 class Store:
-    def __init__(self, cfg, max_pinned_bytes: int = 0):
+    """Pinned NF4 layer store.  absmax: "f32" (float32 per 64-block) or "dq8"
+    (8-bit codes + one float32 scale per 256 blocks)."""
+
+    def __init__(self, cfg, max_pinned_bytes: int = 0, absmax: str = "f32"):
+        if absmax not in ("f32", "dq8"):
+            raise ValueError("absmax must be 'f32' or 'dq8'")
         self.cfg = cfg
         self.mc = model_cfg(cfg)
-        self.record_bytes = qls_layer_record_bytes(self.mc)
+        self.absmax = absmax
+        fmt = QLS_ABSMAX_DQ8 if absmax == "dq8" else QLS_ABSMAX_F32
+        self.record_bytes = qls_layer_record_bytes_fmt(self.mc, fmt)
         self.lora_numel = qls_lora_numel(self.mc)
-        self.h = qls_store_create(self.mc, max_pinned_bytes)
+        self.h = qls_store_create_fmt(self.mc, fmt, max_pinned_bytes)
 
     def set_layer_fp32(self, layer, weights, norm_attn, norm_mlp, n_threads: int = 0):
         ws = [np.ascontiguousarray(w, dtype=np.float32) for w in weights]
@@ -41,13 +48,21 @@ class Store:
         qls_store_set_layer_nf4(self.h, layer, cs, am, _np_bf16(norm_attn), _np_bf16(norm_mlp))
 
     def layer(self, layer) -> dict:
-        """Copies of one record's NF4 codes / absmax per module and its norms."""
+        """Copies of one record's NF4 codes and absmax data per module and its
+        norms ("absmax" for f32 stores; "absmax_q8" and "absmax_scale" for dq8)."""
         v = qls_store_layer_view(self.h, layer)
-        out = {"codes": [], "absmax": []}
+        dq = v.absmax_format == QLS_ABSMAX_DQ8
+        out = {"codes": [], "absmax": [], "absmax_q8": [], "absmax_scale": []}
         for m, (_, o, i) in enumerate(self.cfg.module_shapes()):
             n = o * i
+            nb = n // 64
             out["codes"].append(np.ctypeslib.as_array(C.cast(v.codes[m], C.POINTER(C.c_uint8)), (n // 2,)).copy())
-            out["absmax"].append(np.ctypeslib.as_array(C.cast(v.absmax[m], C.POINTER(C.c_float)), (n // 64,)).copy())
+            if dq:
+                out["absmax_q8"].append(np.ctypeslib.as_array(C.cast(v.absmax_q8[m], C.POINTER(C.c_uint8)), (nb,)).copy())
+                out["absmax_scale"].append(np.ctypeslib.as_array(
+                    C.cast(v.absmax_scale[m], C.POINTER(C.c_float)), (-(-nb // 256),)).copy())
+            else:
+                out["absmax"].append(np.ctypeslib.as_array(C.cast(v.absmax[m], C.POINTER(C.c_float)), (nb,)).copy())
         d = self.cfg.d
         out["norm_attn"] = np.ctypeslib.as_array(C.cast(v.norm_attn, C.POINTER(C.c_uint16)), (d,)).copy()
         out["norm_mlp"] = np.ctypeslib.as_array(C.cast(v.norm_mlp, C.POINTER(C.c_uint16)), (d,)).copy()

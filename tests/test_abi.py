@@ -84,3 +84,25 @@ def test_error_paths(q):
     q.qls_session_destroy(None)
     with pytest.raises(q.QlsError):
         q.qls_linear_ws_bytes(0, 16, 16, 8)
+
+
+@pytest.mark.parametrize("nb,seed", [(256, 1), (1000, 2), (3, 3), (4096 * 7 + 5, 4)])
+def test_double_quant_bitwise_equals_oracle(q, nb, seed):
+    rng = np.random.default_rng(seed)
+    a = np.abs(rng.normal(0, 0.02, (nb, 64))).max(axis=1).astype(np.float32)
+    a[: min(nb, 17)] *= np.float32(3.0)            # a few large entries per group
+    if nb > 600:
+        a[256:512] = 0                            # an all-zero group
+    q8, s = q.qls_nf4_double_quant(a)
+    q8o, so = nf4.double_quant(a)
+    assert np.array_equal(q8, q8o) and np.array_equal(s.view(np.uint32), so.view(np.uint32))
+
+
+def test_double_quant_record_size(q):
+    mc = q.model_cfg(synth.LLAMA8B)
+    # codes 109,051,904 + 8-bit absmax 3,407,872 + 13,312 group scales + norms
+    assert q.qls_layer_record_bytes_fmt(mc, q.QLS_ABSMAX_DQ8) == 112_529_408
+    assert q.qls_layer_record_bytes_fmt(mc, q.QLS_ABSMAX_F32) == q.qls_layer_record_bytes(mc)
+    with pytest.raises(q.QlsError) as e:
+        q.qls_layer_record_bytes_fmt(mc, 7)
+    assert e.value.code == q.QLS_EINVAL

@@ -41,6 +41,18 @@ def test_dequant_bit_exact(q, shape, seed):
     assert np.array_equal(_dequant_gpu(q, codes, absmax), nf4.dequant_bits(codes, absmax))
 
 
+def test_absmax_expand_bit_exact(q):
+    """Device decode of double-quantised absmax equals the oracle's float32(q * s)."""
+    rng = np.random.default_rng(9)
+    a = np.abs(rng.normal(0, 0.02, (70000, 64))).max(axis=1).astype(np.float32)
+    a[256:512] = 0
+    q8, sc = nf4.double_quant(a)
+    out = torch.empty(a.size, dtype=torch.float32, device="cuda")
+    q.qls_nf4_absmax_expand_dev(dev(q8), dev(sc), a.size, out)
+    torch.cuda.synchronize()
+    assert np.array_equal(out.cpu().numpy().view(np.uint32), nf4.dq_absmax(q8, sc).view(np.uint32))
+
+
 def test_dequant_edge_scales(q):
     rng = np.random.default_rng(9)
     codes = rng.integers(0, 256, 32 * 64, dtype=np.uint8)

@@ -10,7 +10,9 @@
   * adapters-disabled log-probs equal the fused DPO reference, bit for bit;
   * layer-load counts: 2L - 2 per SFT step, 3L - 2 for a separate reference
     sweep plus a policy step (page "Soup ... radar note", section "In detail":
-    1.52x for DPO at 32 layers).
+    1.52x for DPO at 32 layers);
+  * the same parity and streamed == resident checks on a store with
+    double-quantised absmax (8-bit codes + one float32 scale per 256 blocks).
 """
 import numpy as np
 import pytest
@@ -31,14 +33,14 @@ def q():
     return q
 
 
-def _setup(q, cfg, perturbed=True):
-    store = q.Store(cfg)
+def _setup(q, cfg, perturbed=True, absmax="f32"):
+    store = q.Store(cfg, absmax=absmax)
     layers = []
     for l in range(cfg.L):
         ws = synth.base_layer(cfg, l)
         na, nm = synth.layer_norms(cfg, l, perturbed)
         store.set_layer_fp32(l, ws, na, nm)
-        layers.append(om.dequant_layer(cfg, ws, na.float().numpy(), nm.float().numpy()))
+        layers.append(om.dequant_layer(cfg, ws, na.float().numpy(), nm.float().numpy(), absmax=absmax))
     emb, lm, fn = synth.embedding(cfg), synth.lm_head(cfg), synth.final_norm(cfg, perturbed)
     model = om.Model(cfg, layers, emb.float().numpy(), lm.float().numpy(), fn.float().numpy())
     return store, model, (emb.cuda(), lm.cuda(), fn.cuda())
@@ -248,3 +250,62 @@ def test_workspace_too_small_is_rejected(q, tiny):
     with pytest.raises(q.QlsError) as e:
         q.qls_session_create(store.h, run, ws, need - 256, s, s, *res)
     assert e.value.code == q.QLS_ENOMEM
+
+
+# ---------------------------------------------------------------- double-quantised absmax store
+@pytest.fixture(scope="module")
+def tiny_dq(q):
+    cfg = synth.TINY
+    store, model, res = _setup(q, cfg, absmax="dq8")
+    return cfg, store, model, res
+
+
+def test_dq_store_holds_the_oracle_double_quant(q, tiny_dq):
+    from oracle import nf4
+    cfg, store, _, _ = tiny_dq
+    assert store.record_bytes < q.qls_layer_record_bytes(q.model_cfg(cfg))
+    rec = store.layer(1)
+    for m, w in enumerate(synth.base_layer(cfg, 1)):
+        codes, amax = nf4.quantize(w)
+        q8, sc = nf4.double_quant(amax)
+        assert np.array_equal(rec["codes"][m], codes)
+        assert np.array_equal(rec["absmax_q8"][m], q8)
+        assert np.array_equal(rec["absmax_scale"][m].view(np.uint32), sc.view(np.uint32))
+
+
+def test_dq_sft_matches_oracle(q, tiny_dq):
+    cfg, store, model, res = tiny_dq
+    ids = synth.token_ids(cfg, 1, 64)
+    lora = synth.lora_init(cfg)
+    sess = q.Session(store, *res, max_tokens=64, max_seq=64)
+    hl, loss, grads = _run_sft(q, sess, cfg, ids, lora)
+    ol, og, _ = om.sft_step(cfg, PM, model, lora, ids)
+    print(f"dq8 loss gpu={hl:.7f} oracle={ol:.7f}", flush=True)
+    assert abs(hl - ol) <= 1e-3 * abs(ol)
+    r, c = report("dq8 grads", grads.cpu().numpy(), _flat_oracle_grads(cfg, og))
+    assert r <= 1e-2 and c >= 0.999
+    sess.close()
+
+
+def test_dq_streamed_equals_resident_bitwise(q):
+    cfg = _deep_cfg()
+    store, _, res = _setup(q, cfg, absmax="dq8")
+    ids = synth.token_ids(cfg, 1, 64, seed=3)
+    lora = synth.lora_init(cfg, b_std=0.01)
+    out = {}
+    for name, mode, flags in [("resident", q.QLS_RESIDENT, 0), ("streamed", q.QLS_STREAMED, 0),
+                              ("poison", q.QLS_STREAMED, q.DBG_POISON_ON_RELEASE),
+                              ("no-reuse", q.QLS_STREAMED, q.DBG_NO_REUSE)]:
+        print(f"dq8 run {name}", flush=True)
+        sess = q.Session(store, *res, max_tokens=64, max_seq=64, mode=mode)
+        sess.debug(flags)
+        for _ in range(2):                        # the second step reuses slots and expansions
+            hl, loss, grads = _run_sft(q, sess, cfg, ids, lora)
+        out[name] = (bits(loss), bits(grads), bits(sess.checkpoints(64)))
+        st = sess.stats()
+        if mode == q.QLS_STREAMED:
+            assert st["h2d_bytes"] == st["layer_loads"] * store.record_bytes
+        sess.close()
+    for name in ("streamed", "poison", "no-reuse"):
+        for a, b in zip(out[name], out["resident"]):
+            assert np.array_equal(a, b), name
