@@ -26,6 +26,9 @@ Pins (what the oracle is checked against, in ``tests/test_oracle_*.py``):
                        attention / cross-entropy, B = 0 identities, the
                        adapters-disabled reference pass, the DPO ln 2 closed
                        form.
+  optim.adamw_step  -- torch.optim.AdamW in float64 over several steps (with and
+                       without weight decay), the step-1 closed form, mirror
+                       precision within float32 rounding of float64.
   model loss value  -- parity unpinned beyond the above: the pages print no
                        worked loss or gradient.
 """
