@@ -207,6 +207,24 @@ int qls_linear_bwd(const uint8_t* d_codes, const float* d_absmax, int N, int K,
                    const uint16_t* d_A, const uint16_t* d_B, int r, float alpha,
                    float* d_dx, float* d_dA, float* d_dB, void* d_ws, void* stream);
 
+/* ---------------------------------------------------------------- optimizer
+ * AdamW (decoupled weight decay) on n float32 parameters, in place, at step
+ * `step` (1-based): the training loop around qls_sft_step / qls_dpo_step.  The
+ * pages train at lr 2e-5 ([P2] "Step 1, the config") and compare 20 streamed
+ * with 20 resident steps ([P3] "The gotchas nobody's mentioning yet"); they
+ * name no optimizer.  With b1 = beta1, b2 = beta2, float32 arithmetic, each
+ * operation rounded on its own:
+ *   p <- p * (1 - lr wd);  m <- b1 m + (1 - b1) g;  v <- b2 v + (1 - b2) g^2;
+ *   p <- p - (lr / (1 - b1^step)) * m / (sqrt(v) / sqrt(1 - b2^step) + eps)
+ * with every constant (1 - lr wd, b1, 1 - b1, b2, 1 - b2, lr / (1 - b1^step),
+ * 1 / sqrt(1 - b2^step), eps) formed in double on the host from the double
+ * hyper-parameters and rounded once to float32.  m and
+ * v start at zero (caller-owned, same length as the parameters).  Errors:
+ * QLS_EINVAL (NULL, n < 0, step < 1, betas outside [0, 1), eps <= 0).
+ * Asynchronous on stream. */
+int qls_adamw_step(float* d_params, const float* d_grads, float* d_m, float* d_v, int64_t n, int step,
+                   double lr, double beta1, double beta2, double eps, double weight_decay, void* stream);
+
 /* ---------------------------------------------------------------- sizes */
 /* Bytes of one layer record: the 7 code blobs, the absmax data (QLS_ABSMAX_F32:
  * 7 float32 arrays; QLS_ABSMAX_DQ8: 7 uint8 arrays then 7 float32 scale

@@ -78,6 +78,8 @@ _SIG = {
     "qls_nf4_dequant_dev": (_I, [_P, _P, _I64, _P, _P]),
     "qls_nf4_double_quant": (_I, [_P, _I64, _P, _P]),
     "qls_nf4_absmax_expand_dev": (_I, [_P, _P, _I64, _P, _P]),
+    "qls_adamw_step": (_I, [_P, _P, _P, _P, _I64, _I, C.c_double, C.c_double, C.c_double, C.c_double,
+                            C.c_double, _P]),
     "qls_linear_ws_bytes": (_I64, [_I, _I, _I, _I]),
     "qls_linear_fwd": (_I, [_P, _P, _I, _I, _P, _I, _P, _P, _I, _F, _P, _P, _P, _P]),
     "qls_linear_bwd": (_I, [_P, _P, _I, _I, _P, _P, _P, _I, _P, _P, _I, _F, _P, _P, _P, _P, _P]),
@@ -178,6 +180,12 @@ def qls_nf4_double_quant(absmax):
 
 def qls_nf4_absmax_expand_dev(d_q8, d_scales, nblocks, d_out, stream=None):
     _check(_lib.qls_nf4_absmax_expand_dev(_ptr(d_q8), _ptr(d_scales), nblocks, _ptr(d_out), _stream(stream)))
+
+
+def qls_adamw_step(params, grads, m, v, step, lr, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.0,
+                   stream=None):
+    _check(_lib.qls_adamw_step(_ptr(params), _ptr(grads), _ptr(m), _ptr(v), params.numel(), step, lr, beta1,
+                               beta2, eps, weight_decay, _stream(stream)))
 
 
 def qls_linear_ws_bytes(T, N, K, r) -> int:
@@ -303,4 +311,4 @@ def qls_debug_set(sess, flags, delay_us=0):
     _check(_lib.qls_debug_set(sess, flags, delay_us))
 
 
-from .runtime import Session, Store  # noqa: E402  (torch-facing convenience objects)
+from .runtime import AdamW, Session, Store  # noqa: E402  (torch-facing convenience objects)

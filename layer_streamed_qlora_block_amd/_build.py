@@ -3,7 +3,8 @@
 Every HIP translation unit is compiled with packed-fp32 instructions disabled
 (the compiler otherwise forms v_pk_* float ops on its own).  The host
 quantiser is compiled with floating-point contraction off so its float32
-decisions match their IEEE definition.  The large-tile GEMM unit raises the
+decisions match their IEEE definition, and so is the optimizer unit, whose
+float32 update must round every operation on its own.  The large-tile GEMM unit raises the
 full-unroll limit so its epilogue loops over the accumulator blocks unroll
 completely and the accumulators stay in registers.
 """
@@ -28,6 +29,7 @@ COMMON = ["-O3", "-fPIC", "-std=c++17", "-Wall", "-Wno-unused-function",
 DEVICE = ["-x", "hip", f"--offload-arch={ARCH}", "-Xclang", "-target-feature",
           "-Xclang", "-packed-fp32-ops", "-fno-gpu-rdc"]
 PER_FILE = {"store.cpp": ["-ffp-contract=off"],
+            "optim.hip": ["-ffp-contract=off"],
             "gemm_big.hip": ["-mllvm", "-pragma-unroll-threshold=200000"]}
 
 

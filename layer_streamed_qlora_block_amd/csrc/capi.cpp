@@ -42,6 +42,17 @@ int qls_nf4_absmax_expand_dev(const uint8_t* d_q8, const float* d_scales, int64_
   return QLS_OK;
 }
 
+int qls_adamw_step(float* d_params, const float* d_grads, float* d_m, float* d_v, int64_t n, int step,
+                   double lr, double beta1, double beta2, double eps, double weight_decay, void* stream) {
+  if (!d_params || !d_grads || !d_m || !d_v) return fail(QLS_EINVAL, "NULL buffer");
+  if (n < 0 || step < 1) return fail(QLS_EINVAL, "n must be >= 0 and step >= 1");
+  if (!(beta1 >= 0.0 && beta1 < 1.0) || !(beta2 >= 0.0 && beta2 < 1.0) || !(eps > 0.0))
+    return fail(QLS_EINVAL, "betas must be in [0, 1) and eps positive");
+  adamw_update(d_params, d_grads, d_m, d_v, n, step, lr, beta1, beta2, eps, weight_decay, (hipStream_t)stream);
+  QLS_HIP(hipGetLastError());
+  return QLS_OK;
+}
+
 int64_t qls_linear_ws_bytes(int T, int N, int K, int r) {
   if (T <= 0 || N <= 0 || K <= 0 || r <= 0) return fail(QLS_EINVAL, "sizes must be positive");
   return linear_ws_bytes(T, N, K, r);

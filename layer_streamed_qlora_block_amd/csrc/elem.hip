@@ -2,6 +2,8 @@
 // cross-entropy reductions and the DPO head.  All are row- or element-parallel
 // with 16-byte accesses where the layout allows; reductions use a fixed order
 // so repeated runs give identical bits.
+#include <cmath>
+
 #include "common.h"
 #include "ops.h"
 

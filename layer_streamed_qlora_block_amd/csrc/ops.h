@@ -95,5 +95,8 @@ void sft_weights_loss(const float* logp, const int32_t* tgt, int T, int N, float
 void seq_logp(const float* logp, int B, int S, int prompt_len, float* seq, float* tok, hipStream_t st);
 void dpo_loss(const float* logp_pol, const float* logp_ref, int S, int prompt_len, float beta,
               float* w, float* loss, float* aux, hipStream_t st);
+// AdamW update of n float32 parameters at step t (1-based), in place.
+void adamw_update(float* p, const float* g, float* m, float* v, int64_t n, int t, double lr, double b1,
+                  double b2, double eps, double wd, hipStream_t st);
 // Bounded spin of `ticks` wall-clock ticks (test hook).
 void spin_delay(int64_t ticks, hipStream_t st);

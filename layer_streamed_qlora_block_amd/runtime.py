@@ -12,7 +12,7 @@ import numpy as np
 import torch
 
 from . import (QLS_ABSMAX_DQ8, QLS_ABSMAX_F32, QLS_RESIDENT, QLS_STREAMED, RunCfg, model_cfg, qls_debug_set,
-               qls_dpo_step, qls_layer_fwd_bwd, qls_layer_record_bytes_fmt, qls_logprobs, qls_lora_numel,
+               qls_adamw_step, qls_dpo_step, qls_layer_fwd_bwd, qls_layer_record_bytes_fmt, qls_logprobs, qls_lora_numel,
                qls_session_checkpoints, qls_session_create, qls_session_destroy, qls_session_reset_stats,
                qls_session_stats, qls_sft_step, qls_store_create_fmt, qls_store_destroy, qls_store_layer_view,
                qls_store_set_layer_fp32, qls_store_set_layer_nf4, qls_workspace_bytes)
@@ -166,3 +166,24 @@ class Session:
 
 
 __all__ = ["Store", "Session", "QLS_STREAMED", "QLS_RESIDENT"]
+
+
+class AdamW:
+    """AdamW on the packed float32 LoRA vector (qls_adamw_step), moments in
+    device memory, issued on torch's current stream (after the step's kernels,
+    which the session orders before it)."""
+
+    def __init__(self, params: torch.Tensor, lr: float = 2e-5, betas=(0.9, 0.999), eps: float = 1e-8,
+                 weight_decay: float = 0.0):
+        if params.dtype != torch.float32 or not params.is_cuda or not params.is_contiguous():
+            raise ValueError("params must be a contiguous float32 CUDA tensor")
+        self.p = params
+        self.m = torch.zeros_like(params)
+        self.v = torch.zeros_like(params)
+        self.lr, self.betas, self.eps, self.wd = lr, betas, eps, weight_decay
+        self.t = 0
+
+    def step(self, grads: torch.Tensor):
+        self.t += 1
+        qls_adamw_step(self.p, grads, self.m, self.v, self.t, self.lr, self.betas[0], self.betas[1], self.eps,
+                       self.wd, stream=torch.cuda.current_stream())
