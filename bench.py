@@ -145,6 +145,8 @@ def main():
                     help="store format: double-quantised absmax (112.5 MB per 8B layer, the pages' store) "
                          "or float32 absmax (122.7 MB)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--optimizer", choices=["adamw", "none"], default="adamw",
+                    help="update the LoRA vector with AdamW (lr 2e-5, the pages' config) inside every timed step")
     ap.add_argument("--dpo", action="store_true", help="also time DPO steps (2 x seq, shared 128-token prompt)")
     ap.add_argument("--threads", type=int, default=min(16, os.cpu_count() or 1))
     ap.add_argument("--copy-probe-mib", type=int, default=0,
@@ -193,8 +195,15 @@ def main():
     print(f"[bench] session ready ({sess.ws_bytes / 1e9:.2f} GB workspace), setup "
           f"{time.perf_counter() - t_setup:.1f} s", file=sys.stderr, flush=True)
 
-    for _ in range(args.warmup):
+    opt = q.AdamW(lora, lr=2e-5) if args.optimizer == "adamw" else None
+
+    def train_step():
         sess.sft_step(ids, lora, grads, loss)
+        if opt is not None:
+            opt.step(grads)
+
+    for _ in range(args.warmup):
+        train_step()
     torch.cuda.synchronize()
     sess.reset_stats()
     torch.cuda.synchronize()
@@ -203,7 +212,7 @@ def main():
     t0 = time.perf_counter()
     sampler.start()   # samples the clock while the timed steps run
     for i in range(args.steps):
-        sess.sft_step(ids, lora, grads, loss)
+        train_step()
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     sampler.join()
@@ -243,7 +252,7 @@ def main():
                                 f"per layer) in pinned host memory streamed through 2 device slots, bf16 embedding + "
                                 f"LM head 128256 x 4096 resident, LoRA r64 alpha16 on 7 linears"),
                    "global_batch": B, "seq_len": S, "parallelism": "single GPU", "mode": args.mode,
-                   "absmax": args.absmax},
+                   "absmax": args.absmax, "optimizer": (None if opt is None else "AdamW lr 2e-5 on the LoRA vector")},
         "roofline": {"bound": "mfma", "kernel": dom["name"],
                      "achieved": round(dom["tflops"], 2) if dom["tflops"] else None,
                      "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
