@@ -8,13 +8,16 @@
 // tile (4 x 2 MFMA blocks, 128 accumulators per lane), so the other wave on
 // the SIMD can issue while one waits on LDS or a barrier.  The k-loop runs in
 // steps of 64 (one NF4 block along K for NT): global loads run two steps
-// ahead through two register stages; each step dequantises the NF4 tile of
-// the next step (bf16 = RNE(float32(cb[c] * absmax)), one 2 KB LDS table that
-// maps a code byte to its two codebook values) into the other of two LDS
-// stages while the MFMAs consume the current one.  LDS rows are padded to 72
-// bf16 so the 16-byte fragment reads of 16 consecutive rows hit distinct
-// banks.  The epilogue goes through LDS, one 128-row half at a time, so
-// residual loads and output stores are 16 bytes per lane and row-contiguous.
+// ahead: the activation tile goes straight from global memory into LDS
+// (buffer_load ... lds, 16 bytes per lane), the NF4 codes through two register
+// stages.  Each step dequantises the NF4 tile of the next step (bf16 =
+// RNE(float32(cb[c] * absmax)), one 2 KB LDS table that maps a code byte to its
+// two codebook values) into the other of two LDS stages while the MFMAs
+// consume the current one.  Activation tiles are unpadded 128-byte rows whose
+// 16-byte chunks are XOR-swizzled by row; weight tiles are padded to 72 bf16
+// per row (NT) or chunk-swizzled (NN), so fragment reads are free of bank
+// conflicts.  The epilogue goes through LDS, 32 rows at a time, so residual
+// loads and output stores are 16 bytes per lane and row-contiguous.
 #include "common.h"
 #include "gemm.h"
 
@@ -22,10 +25,11 @@ namespace {
 
 constexpr int NT = 512;
 constexpr int BM = 256, BN = 256, BK = 64, PITCH = BK + 8;
-constexpr int TILE = BM * PITCH;     // bf16 elements of one operand tile
-constexpr int STAGE = 2 * TILE;      // A tile then B tile
-constexpr int TP = BN + 4;           // fp32 pitch of the staged epilogue tile
-static_assert(128 * TP * 4 <= 2 * STAGE * 2, "epilogue half-tile must fit the stages");
+constexpr int ATILE = BM * BK;      // bf16 elements of an activation tile (unpadded rows)
+constexpr int TILE = BN * PITCH;     // bf16 elements of a weight tile
+constexpr int TP = BN + 4;           // fp32 pitch of the staged epilogue rows
+constexpr int EROWS = 32;            // epilogue rows staged at a time (through weight stage 0)
+static_assert(EROWS * TP * 4 <= TILE * 2, "epilogue rows must fit a weight stage");
 
 QLS_DEV __amdgpu_buffer_rsrc_t rsrc(const void* p, int64_t bytes) {
   const int n = bytes <= 0 ? 0 : (bytes > 0x7fffffffLL ? 0x7fffffff : (int)bytes);
@@ -39,6 +43,12 @@ QLS_DEV uint32_t ld32(__amdgpu_buffer_rsrc_t r, uint32_t v, uint32_t s) {
 }
 QLS_DEV float sigm(float x) { return 1.f / (1.f + __expf(-x)); }
 
+// Activation tile: 16-byte chunk c of row r sits at chunk c ^ a_swz(r).  Eight
+// consecutive rows (the 128-byte bank span) and sixteen consecutive rows with
+// the same parity both map one chunk index to distinct chunks.
+QLS_DEV int a_swz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
+QLS_DEV int a_pos(int r, int k) { return r * BK + 8 * ((k >> 3) ^ a_swz(r)) + (k & 7); }
+
 // NN B tile: each thread dequantises 4 contraction rows x 8 columns.  Column
 // group cg (8 columns) and row quad kq of thread t are interleaved so that a
 // half-wave covers 8 column groups x 4 row quads, and the 16-byte chunks of
@@ -50,25 +60,36 @@ QLS_DEV int nn_swz(int n) { return 2 * ((n >> 4) & 3); }
 // Element offset of contraction index k (multiple of 4) in LDS row n of an NN B tile.
 QLS_DEV int nn_pos(int n, int k) { return n * PITCH + 8 * ((k >> 3) ^ nn_swz(n)) + (k & 7); }
 
-// One register stage of global data: the thread's A slice (row t/2, 32
-// contraction values) and its B codes (NT: 32 codes of one W row + absmax;
-// NN: 4 W rows x 8 columns + 4 absmax).
+// One register stage of NF4 data: NT: 32 codes of one W row + absmax; NN:
+// 4 W rows x 8 columns + 4 absmax.  kLoads: the VMEM instructions of a stage.
 template <int BL> struct Stage;
-template <> struct Stage<B_NF4_NT> { u32x4 a[4]; u32x4 q; float s; };
-template <> struct Stage<B_NF4_NN> { u32x4 a[4]; uint32_t q[4]; float s[4]; };
+template <> struct Stage<B_NF4_NT> { u32x4 q; float s; static constexpr int kLoads = 2; };
+template <> struct Stage<B_NF4_NN> { uint32_t q[4]; float s[4]; static constexpr int kLoads = 8; };
+
+// Wait until at most n vector-memory operations are outstanding and every LDS
+// operation is done (gfx9 s_waitcnt encoding: vmcnt bits 3:0 and 15:14,
+// expcnt 6:4 left at its maximum, lgkmcnt 11:8 = 0).
+template <int N>
+QLS_DEV void wait_vm_lds() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | ((N >> 4) << 14));
+}
 
 template <int BL>
 struct Big {
   const GemmArgs& g;
-  uint16_t* smem;
+  uint16_t* sA[2];
+  uint16_t* sB[2];
   const float2* lut2;
   int t, lane, wm, wn, m0, n0;
   __amdgpu_buffer_rsrc_t ra, rq, rs;
-  uint32_t va, vq, vs;
+  uint32_t vdma[4], vq, vs;
   f32x16 acc[4][2];
 
-  QLS_DEV Big(const GemmArgs& g_, uint16_t* smem_, const float2* lut2_, int m0_, int n0_)
-      : g(g_), smem(smem_), lut2(lut2_), m0(m0_), n0(n0_) {
+  QLS_DEV Big(const GemmArgs& g_, uint16_t* a0, uint16_t* a1, uint16_t* b0, uint16_t* b1,
+              const float2* lut2_, int m0_, int n0_)
+      : g(g_), lut2(lut2_), m0(m0_), n0(n0_) {
+    sA[0] = a0; sA[1] = a1; sB[0] = b0; sB[1] = b1;
     t = threadIdx.x;
     lane = t & 63;
     const int wave = t >> 6;
@@ -79,8 +100,14 @@ struct Big {
 #pragma unroll
       for (int j = 0; j < 2; ++j) acc[i][j] = f32x16{};
     // A rows m0.. through a resource that ends at row M (rows past it read 0).
+    // DMA: wave w, instruction j fills LDS rows 8(4w+j) .. +7 (1 KB); lane l
+    // lands in row +l/8, chunk slot l%8, which holds chunk (l%8) ^ a_swz(row).
     ra = rsrc(g.A + (int64_t)m0 * g.lda, (int64_t)(g.M - m0) * g.lda * 2);
-    va = (uint32_t)(((t >> 1) * g.lda + 32 * (t & 1)) * 2);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int r = 8 * (4 * (t >> 6) + j) + (lane >> 3);
+      vdma[j] = (uint32_t)((r * g.lda + 8 * ((lane & 7) ^ a_swz(r))) * 2);
+    }
     if constexpr (BL == B_NF4_NT) {
       // W rows n0..: codes row n at n * ldq / 2, absmax at n * ldq / 64.
       rq = rsrc(g.Bq + (int64_t)n0 * g.ldq / 2, (int64_t)(g.N - n0) * g.ldq / 2);
@@ -98,9 +125,16 @@ struct Big {
     }
   }
 
-  QLS_DEV void load(Stage<BL>& r, int k0) {
+  // Activation tile k0 .. k0+64 straight into LDS.
+  QLS_DEV void dma(uint16_t* s, int k0) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) r.a[j] = ld128(ra, va + 16 * j, (uint32_t)k0 * 2);
+    for (int j = 0; j < 4; ++j)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          ra, (__attribute__((address_space(3))) void*)(s + (4 * (t >> 6) + j) * 512), 16, vdma[j],
+          (uint32_t)k0 * 2, 0, 0);
+  }
+
+  QLS_DEV void load(Stage<BL>& r, int k0) {
     if constexpr (BL == B_NF4_NT) {
       r.q = ld128(rq, vq, (uint32_t)k0 / 2);
       r.s = __uint_as_float(ld32(rs, vs, (uint32_t)k0 / 16));
@@ -113,11 +147,9 @@ struct Big {
     }
   }
 
-  // Dequantise and write one register stage into LDS stage (sA, sB).
-  QLS_DEV void store(const Stage<BL>& r, uint16_t* sA, uint16_t* sB) const {
+  // Dequantise one register stage into weight stage sB.
+  QLS_DEV void store(const Stage<BL>& r, uint16_t* sB) const {
     const int row = t >> 1, half = t & 1;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) *reinterpret_cast<u32x4*>(sA + row * PITCH + 32 * half + 8 * j) = r.a[j];
     if constexpr (BL == B_NF4_NT) {
 #pragma unroll
       for (int w = 0; w < 4; ++w) {
@@ -154,7 +186,7 @@ struct Big {
       u32x4 a[4], b[2];
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        a[i] = *reinterpret_cast<const u32x4*>(sA + (wm * 128 + 32 * i + (lane & 31)) * PITCH + kofs);
+        a[i] = *reinterpret_cast<const u32x4*>(sA + a_pos(wm * 128 + 32 * i + (lane & 31), kofs));
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
         const int n = wn * 64 + 32 * j + (lane & 31);
@@ -172,16 +204,19 @@ struct Big {
 
   // ---- LoRA contraction into the accumulator (before the base product).
   // Plain guarded loads: it runs once per tile.
-  // Rows m0.. of P (row-major, ld), contraction columns [k0, k0+64) of [0, K):
-  QLS_DEV void stage_rows(uint16_t* s, const uint16_t* p, int64_t ld, int rlo, int rhi, int r0, int k0, int K) const {
+  // Rows r0.. of P (row-major, ld), contraction columns [k0, k0+64) of [0, K),
+  // rows outside [rlo, rhi) as zero; `swz`: activation layout, else padded.
+  QLS_DEV void stage_rows(uint16_t* s, bool swz, const uint16_t* p, int64_t ld, int rlo, int rhi, int r0,
+                          int k0, int K) const {
     const int row = t >> 1, half = t & 1;
     const int gr = r0 + row;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const int k = k0 + 32 * half + 8 * j;
+      const int kk = 32 * half + 8 * j;
+      const int k = k0 + kk;
       u32x4 v = u32x4{0, 0, 0, 0};
       if (gr >= rlo && gr < rhi && k < K) v = *reinterpret_cast<const u32x4*>(p + (int64_t)gr * ld + k);
-      *reinterpret_cast<u32x4*>(s + row * PITCH + 32 * half + 8 * j) = v;
+      *reinterpret_cast<u32x4*>(s + (swz ? a_pos(row, kk) : row * PITCH + kk)) = v;
     }
   }
   // Columns n0.. of P stored k-major (element (k, n) at p[k * ld + n]),
@@ -207,8 +242,8 @@ struct Big {
   }
 
   QLS_DEV void lora() {
-    uint16_t* sA = smem;
-    uint16_t* sB = smem + TILE;
+    uint16_t* sa = sA[0];
+    uint16_t* sb = sB[0];
     if constexpr (BL == B_NF4_NT) {
       // acc = (s2 / alpha) sum_g U_g B_g^T; B_g is zero outside module g's columns.
       int start = 0;
@@ -217,10 +252,10 @@ struct Big {
         if (end > n0 && start < n0 + BN) {
           const uint16_t* bp = g.modB[gi] - (int64_t)start * g.K2;
           for (int k0 = 0; k0 < g.K2; k0 += BK) {
-            stage_rows(sA, g.A2 + gi * g.K2, g.lda2, 0, g.M, m0, k0, g.K2);
-            stage_rows(sB, bp, g.K2, start, end, n0, k0, g.K2);
+            stage_rows(sa, true, g.A2 + gi * g.K2, g.lda2, 0, g.M, m0, k0, g.K2);
+            stage_rows(sb, false, bp, g.K2, start, end, n0, k0, g.K2);
             __syncthreads();
-            mma(sA, sB);
+            mma(sa, sb);
             __syncthreads();
           }
         }
@@ -234,63 +269,78 @@ struct Big {
     } else {
       // acc = du_cat A_cat, A_cat [K2, N] row-major.
       for (int k0 = 0; k0 < g.K2; k0 += BK) {
-        stage_rows(sA, g.A2, g.lda2, 0, g.M, m0, k0, g.K2);
-        stage_cols(sB, g.B2, g.ldb2, g.N, k0, g.K2);
+        stage_rows(sa, true, g.A2, g.lda2, 0, g.M, m0, k0, g.K2);
+        stage_cols(sb, g.B2, g.ldb2, g.N, k0, g.K2);
         __syncthreads();
-        mma(sA, sB);
+        mma(sa, sb);
         __syncthreads();
       }
     }
   }
 
-  // ---- base product: two register stages, two LDS stages, one barrier per step.
+  // ---- base product: one barrier per step.  Step kt: the MFMAs read stage
+  // kt&1 while the DMA fills the activation tile of kt+1 into the other stage,
+  // the NF4 codes of kt+1 (loaded a step earlier) are dequantised into the
+  // other weight stage and the codes of kt+2 are loaded.  The DMA is issued
+  // before the code loads (a compiler fence keeps the order), so waiting for
+  // all but the newest kLoads vector operations before the barrier covers it.
+  QLS_DEV void half_step(int kt, int nk, int cur, Stage<BL>& rld, const Stage<BL>& rst) {
+    dma(sA[cur ^ 1], min(kt + 1, nk - 1) * BK);
+    asm volatile("" ::: "memory");
+    load(rld, min(kt + 2, nk - 1) * BK);
+    mma(sA[cur], sB[cur]);
+    store(rst, sB[cur ^ 1]);
+    wait_vm_lds<Stage<BL>::kLoads>();
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+  }
+
   QLS_DEV void mainloop() {
     const int nk = g.K / BK;
-    uint16_t* const s0 = smem;
-    uint16_t* const s1 = smem + STAGE;
     Stage<BL> r0, r1;
+    dma(sA[0], 0);
+    asm volatile("" ::: "memory");
     load(r0, 0);
     load(r1, min(1, nk - 1) * BK);
-    store(r0, s0, s0 + TILE);
+    store(r0, sB[0]);
     __syncthreads();
     // Loads past the last step re-read step nk-1 (in bounds, never consumed).
     for (int kt = 0;; kt += 2) {
-      load(r0, min(kt + 2, nk - 1) * BK);
-      mma(s0, s0 + TILE);
-      store(r1, s1, s1 + TILE);
-      __syncthreads();
+      half_step(kt, nk, 0, r0, r1);
       if (kt + 1 >= nk) break;
-      load(r1, min(kt + 3, nk - 1) * BK);
-      mma(s1, s1 + TILE);
-      store(r0, s0, s0 + TILE);
-      __syncthreads();
+      half_step(kt + 1, nk, 1, r1, r0);
       if (kt + 2 >= nk) break;
     }
+    __syncthreads();
   }
 
-  // ---- epilogue through LDS, one 128-row half at a time; 8 columns per thread.
+  // ---- epilogue through LDS (weight stage 0), 32 rows at a time; 8 columns
+  // per thread.  Rows 32h .. 32h+31 are block i = h%4 of the waves with wm = h/4.
   template <int EPI>
   QLS_DEV void epilogue() {
-    float* sT = reinterpret_cast<float*>(smem);
+    float* sT = reinterpret_cast<float*>(sB[0]);
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      if (wm == h) {
+    for (int h = 0; h < BM / EROWS; ++h) {
+      if (wm == (h >> 2)) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < 4; ++i) {
+          if (i != (h & 3)) continue;
 #pragma unroll
           for (int j = 0; j < 2; ++j)
 #pragma unroll
             for (int q = 0; q < 16; ++q) {
-              const int mm = 32 * i + 8 * (q >> 2) + 4 * (lane >> 5) + (q & 3);
+              const int mm = 8 * (q >> 2) + 4 * (lane >> 5) + (q & 3);
               const int nn = wn * 64 + 32 * j + (lane & 31);
               sT[mm * TP + nn] = acc[i][j][q];
             }
+        }
       }
       __syncthreads();
-#pragma unroll 2
-      for (int it = 0; it < 8; ++it) {
+#pragma unroll
+      for (int it = 0; it < EROWS * BN / 8 / NT; ++it) {
         const int rr = (t >> 5) + 16 * it, c8 = 8 * (t & 31);
-        const int m = m0 + 128 * h + rr, n = n0 + c8;
+        const int m = m0 + EROWS * h + rr, n = n0 + c8;
         if (m < g.M && n < g.N) {
           const f32x4 x0 = *reinterpret_cast<const f32x4*>(sT + rr * TP + c8);
           const f32x4 x1 = *reinterpret_cast<const f32x4*>(sT + rr * TP + c8 + 4);
@@ -347,13 +397,18 @@ struct Big {
 template <int BL, int EPI>
 __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2)))
 big_kernel(GemmArgs g, const float* __restrict__ cb) {
-  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * STAGE];
+  // Separate arrays per stage, so the compiler can tell the DMA's target from
+  // the stage the MFMAs read.
+  __shared__ __attribute__((aligned(16))) uint16_t sA0[ATILE];
+  __shared__ __attribute__((aligned(16))) uint16_t sA1[ATILE];
+  __shared__ __attribute__((aligned(16))) uint16_t sB0[TILE];
+  __shared__ __attribute__((aligned(16))) uint16_t sB1[TILE];
   __shared__ __attribute__((aligned(16))) float2 lut2[256];
   const int t = threadIdx.x;
   if (t < 256) lut2[t] = make_float2(cb[t >> 4], cb[t & 15]);   // byte -> (high, low) nibble levels
   const int tiles_n = (g.N + BN - 1) / BN;
   const int m0 = (blockIdx.x / tiles_n) * BM, n0 = (blockIdx.x % tiles_n) * BN;
-  Big<BL> k(g, smem, lut2, m0, n0);
+  Big<BL> k(g, sA0, sA1, sB0, sB1, lut2, m0, n0);
   __syncthreads();
   if ((BL == B_NF4_NT && g.lora == LORA_FWD) || (BL == B_NF4_NN && g.lora == LORA_DX)) k.lora();
   k.mainloop();
