@@ -41,13 +41,16 @@ QLS_DEV void stage_rows(uint16_t* s, const uint16_t* base, int64_t ld, int r0, i
 }
 
 // transposed: s[j][row] (pitch 72) = element (row, j); each thread moves
-// 8 rows x R columns and transposes them in registers.
+// 8 rows x R columns and transposes them in registers.  Column group jg and
+// row group kg are interleaved so that each 8 / 16 consecutive lanes write 16
+// distinct bank quads (a plain jg = t % 32 mapping puts four of them on one).
 template <int HD>
 QLS_DEV void stage_cols(uint16_t* s, const uint16_t* base, int64_t ld, int r0, int S) {
   constexpr int R = HD / 32;
-  constexpr int JG = HD / R;          // 32 column groups
+  static_assert(HD / R == 32, "32 column groups");
   const int t = threadIdx.x;
-  const int jg = t % JG, kg = t / JG; // kg in [0, 8)
+  const int jg = ((t >> 2) & 3) | (((t >> 4) & 7) << 2);   // 0..31
+  const int kg = (t & 3) | ((t >> 7) << 2);                // 0..7
   uint32_t w[8][R / 2];
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
