@@ -2,7 +2,8 @@
 """Benchmark of the streamed QLoRA SFT step on the 8B-shaped stack, one MI355X.
 
 Workload (one step = the whole hot path): 32 Llama-3.1-8B-shaped decoder
-layers held as NF4 (block 64, fp32 absmax) in pinned host memory, streamed one
+layers held as NF4 (block 64; absmax double-quantised by default, ``--absmax
+f32`` for float32 absmax) in pinned host memory, streamed one
 layer ahead through two device slots; resident bf16 embedding and LM head
 (128256 x 4096); LoRA r=64, alpha=16 on the seven linears; batch 1 x seq 512
 (``--seq 4096`` for the long-sequence case); forward sweep, vocabulary-chunked
@@ -31,10 +32,10 @@ sys.path.insert(0, ROOT)
 
 METRIC = "streamed QLoRA SFT tokens/sec (8B-shape, seq 512); % H2D BW and % MFMA peak"
 BF16_PEAK_TFLOPS = 2500.0       # MI355X dense bf16 MFMA
-# HBM bytes per launch of the forward dequant-GEMM, from rocprofv3 FETCH_SIZE /
+# HBM bytes per launch of a dequant-GEMM kernel, from rocprofv3 FETCH_SIZE /
 # WRITE_SIZE passes scaled by a known-size copy (profiles/hbm_traffic_dequant_gemm_8b.md);
-# valid for the kernels they were taken on, keyed by sequence length.
-TRAFFIC_BYTES_PER_LAUNCH = {512: 148.2e6, 4096: 787.5e6}
+# valid only for the kernel code they were taken on, keyed by (kernel, sequence length).
+TRAFFIC_BYTES_PER_LAUNCH = {}
 PCIE_GEN5_X16_GBPS = 64.0       # theoretical per direction
 
 
@@ -225,13 +226,21 @@ def main():
     steps = max(1, st["steps"])
     h2d_ovl = st["h2d_bytes"] / (st["copy_ms"] * 1e-3) / 1e9 if st["copy_ms"] > 0 else None
     h2d_eff = st["h2d_bytes"] / elapsed / 1e9
-    k_fwd = {"name": "dequant-GEMM forward (Y = X W_nf4^T + s U B^T [+ residual])",
-             "launches": st["dq_fwd_launches"], "avg_us": 1e3 * st["dq_fwd_ms"] / max(1, st["dq_fwd_launches"]),
-             "tflops": st["dq_fwd_gflop"] / st["dq_fwd_ms"] if st["dq_fwd_ms"] else None}
-    k_dx = {"name": "dequant-GEMM transposed (dX = dY W_nf4 + du A)",
-            "launches": st["dq_dx_launches"], "avg_us": 1e3 * st["dq_dx_ms"] / max(1, st["dq_dx_launches"]),
-            "tflops": st["dq_dx_gflop"] / st["dq_dx_ms"] if st["dq_dx_ms"] else None}
-    dom = k_fwd if st["dq_fwd_ms"] >= st["dq_dx_ms"] else k_dx
+    kern = {}
+    for key, tag, desc in (("fwd", "dq_fwd", "dequant-GEMM forward (Y = X W_nf4^T + s U B^T [+ residual])"),
+                           ("dx", "dq_dx", "dequant-GEMM transposed (dX = dY W_nf4 + du A)")):
+        big = (st[tag + "_big_ms"], st[tag + "_big_gflop"], st[tag + "_big_launches"])
+        small = (st[tag + "_ms"] - big[0], st[tag + "_gflop"] - big[1], st[tag + "_launches"] - big[2])
+        for tile, (ms, gf, n) in ((256, big), (128, small)):
+            if n <= 0:
+                continue
+            kern[f"dq_{key}_{tile}"] = {"name": f"{desc}, {tile} x {tile} tiles", "launches": n,
+                                        "ms_per_step": round(ms / steps, 3), "avg_us": round(1e3 * ms / n, 2),
+                                        "tflops": round(gf / ms, 2) if ms > 0 else None}
+        kern[f"dq_{key}_splitk_reduce"] = {"ms_per_step": round(st[tag + "_reduce_ms"] / steps, 3)}
+    timed = {k: v for k, v in kern.items() if "launches" in v}
+    dom_key = max(timed, key=lambda k: timed[k]["ms_per_step"])
+    dom = timed[dom_key]
     absmax_desc = ("double-quantised absmax: 8-bit codes + float32 scale per 256 blocks" if args.absmax == "dq8"
                    else "float32 absmax")
     out = {
@@ -254,12 +263,12 @@ def main():
                    "global_batch": B, "seq_len": S, "parallelism": "single GPU", "mode": args.mode,
                    "absmax": args.absmax, "optimizer": (None if opt is None else "AdamW lr 2e-5 on the LoRA vector")},
         "roofline": {"bound": "mfma", "kernel": dom["name"],
-                     "achieved": round(dom["tflops"], 2) if dom["tflops"] else None,
+                     "achieved": dom["tflops"],
                      "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(dom["tflops"] / BF16_PEAK_TFLOPS, 4) if dom["tflops"] else None,
-                     "traffic": (TRAFFIC_BYTES_PER_LAUNCH.get(S) if dom is k_fwd and B == 1 else None),
+                     "traffic": (TRAFFIC_BYTES_PER_LAUNCH.get((dom_key, S)) if B == 1 else None),
                      "traffic_unit": "HBM bytes per launch"},
-        "kernels": {"dq_fwd": k_fwd, "dq_dx": k_dx},
+        "kernels": kern,
         "h2d": {"bytes_per_step": st["h2d_bytes"] // steps, "layer_loads_per_step": st["layer_loads"] / steps,
                 "isolated_GBps": round(iso, 2),
                 "under_overlap_GBps": round(h2d_ovl, 2) if h2d_ovl else None,

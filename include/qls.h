@@ -47,7 +47,7 @@
 extern "C" {
 #endif
 
-#define QLS_ABI_VERSION 1
+#define QLS_ABI_VERSION 2
 
 enum {
   QLS_OK = 0,
@@ -143,6 +143,14 @@ typedef struct qls_stats {
   int64_t dq_fwd_launches;
   double dq_dx_ms, dq_dx_gflop;
   int64_t dq_dx_launches;
+  /* The part of the above taken by the 256 x 256-tile kernels (the rest ran
+   * the 128 x 128-tile kernels), and the summed duration of the split-K
+   * reduce kernels that followed any of the launches (timing on). */
+  double dq_fwd_big_ms, dq_fwd_big_gflop;
+  int64_t dq_fwd_big_launches;
+  double dq_dx_big_ms, dq_dx_big_gflop;
+  int64_t dq_dx_big_launches;
+  double dq_fwd_reduce_ms, dq_dx_reduce_ms;
 } qls_stats;
 
 typedef struct qls_store qls_store;

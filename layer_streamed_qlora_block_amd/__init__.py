@@ -60,7 +60,10 @@ class Stats(C.Structure):
                 ("copy_ms", C.c_double), ("compute_ms", C.c_double), ("overlap_ms", C.c_double),
                 ("step_ms", C.c_double), ("ws_bytes", C.c_int64),
                 ("dq_fwd_ms", C.c_double), ("dq_fwd_gflop", C.c_double), ("dq_fwd_launches", C.c_int64),
-                ("dq_dx_ms", C.c_double), ("dq_dx_gflop", C.c_double), ("dq_dx_launches", C.c_int64)]
+                ("dq_dx_ms", C.c_double), ("dq_dx_gflop", C.c_double), ("dq_dx_launches", C.c_int64),
+                ("dq_fwd_big_ms", C.c_double), ("dq_fwd_big_gflop", C.c_double), ("dq_fwd_big_launches", C.c_int64),
+                ("dq_dx_big_ms", C.c_double), ("dq_dx_big_gflop", C.c_double), ("dq_dx_big_launches", C.c_int64),
+                ("dq_fwd_reduce_ms", C.c_double), ("dq_dx_reduce_ms", C.c_double)]
 
     def as_dict(self):
         return {k: getattr(self, k) for k, _ in self._fields_}

@@ -49,14 +49,18 @@ struct GemmArgs {
 
 // Returns 0, or -1 when the (tile, loaders, epilogue) combination is not built.
 int gemm_launch(const GemmArgs& g, int aload, int bload, int epi, int tile, hipStream_t st);
-// Large-M dequant-GEMMs (256 x 256 tiles, 512 threads): B_NF4_NT with
+// Large dequant-GEMMs (256 x 256 tiles, 512 threads): B_NF4_NT with
 // EPI_BF16 (LORA_FWD allowed) and B_NF4_NN with EPI_F32 / EPI_BF16 (no
-// residual) / EPI_SWIGLU_BWD (LORA_DX allowed); no split-K.  gemm_big_ok
-// checks the shape and alignment conditions; gemm_big_launch returns -1 when
-// they do not hold.
+// residual) / EPI_SWIGLU_BWD (LORA_DX allowed); split-K (ksplit > 1) writes
+// float partials to g.partial (ksplit * M * N floats) and then runs
+// gemm_reduce_epi.  gemm_big_ok checks the shape and alignment conditions;
+// gemm_big_launch returns -1 when they do not hold.
 bool gemm_big_ok(const GemmArgs& g, int bload, int epi);
 int gemm_big_launch(const GemmArgs& g, int bload, int epi, hipStream_t st);
 // out = epilogue(sum_z partial[z]) for split-K: mode 0 -> bf16 alpha*sum, 1 -> f32 alpha*sum.
 void gemm_reduce(const float* partial, int ksplit, int M, int N, float alpha, int mode,
                  void* C, int64_t ldc, hipStream_t st);
 int64_t gemm_partial_elems(int M, int N, int ksplit);
+// Sums the ksplit partials of g (in split order) and applies epilogue epi to g.C
+// (N % 4 == 0).
+void gemm_reduce_epi(const GemmArgs& g, int epi, hipStream_t st);

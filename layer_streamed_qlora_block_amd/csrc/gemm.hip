@@ -814,3 +814,8 @@ void gemm_reduce(const float* partial, int ksplit, int M, int N, float alpha, in
 }
 
 int64_t gemm_partial_elems(int M, int N, int ksplit) { return (int64_t)M * N * ksplit; }
+
+void gemm_reduce_epi(const GemmArgs& g, int epi, hipStream_t st) {
+  const int64_t n = (int64_t)g.M * (g.N / 4);
+  hipLaunchKernelGGL(reduce_epi_kernel, dim3((unsigned)ceil_div64(n, 256)), dim3(256), 0, st, g, epi);
+}

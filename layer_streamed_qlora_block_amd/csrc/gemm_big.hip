@@ -284,10 +284,10 @@ struct Big {
   // other weight stage and the codes of kt+2 are loaded.  The DMA is issued
   // before the code loads (a compiler fence keeps the order), so waiting for
   // all but the newest kLoads vector operations before the barrier covers it.
-  QLS_DEV void half_step(int kt, int nk, int cur, Stage<BL>& rld, const Stage<BL>& rst) {
-    dma(sA[cur ^ 1], min(kt + 1, nk - 1) * BK);
+  QLS_DEV void half_step(int kt, int kb, int nk, int cur, Stage<BL>& rld, const Stage<BL>& rst) {
+    dma(sA[cur ^ 1], (kb + min(kt + 1, nk - 1)) * BK);
     asm volatile("" ::: "memory");
-    load(rld, min(kt + 2, nk - 1) * BK);
+    load(rld, (kb + min(kt + 2, nk - 1)) * BK);
     mma(sA[cur], sB[cur]);
     store(rst, sB[cur ^ 1]);
     wait_vm_lds<Stage<BL>::kLoads>();
@@ -296,20 +296,21 @@ struct Big {
     asm volatile("" ::: "memory");
   }
 
-  QLS_DEV void mainloop() {
-    const int nk = g.K / BK;
+  // Contraction steps [kb, ke) of 64 (a split-K slice, or all of K).
+  QLS_DEV void mainloop(int kb, int ke) {
+    const int nk = ke - kb;
     Stage<BL> r0, r1;
-    dma(sA[0], 0);
+    dma(sA[0], kb * BK);
     asm volatile("" ::: "memory");
-    load(r0, 0);
-    load(r1, min(1, nk - 1) * BK);
+    load(r0, kb * BK);
+    load(r1, (kb + min(1, nk - 1)) * BK);
     store(r0, sB[0]);
     __syncthreads();
-    // Loads past the last step re-read step nk-1 (in bounds, never consumed).
+    // Loads past the last step re-read step ke-1 (in bounds, never consumed).
     for (int kt = 0;; kt += 2) {
-      half_step(kt, nk, 0, r0, r1);
+      half_step(kt, kb, nk, 0, r0, r1);
       if (kt + 1 >= nk) break;
-      half_step(kt + 1, nk, 1, r1, r0);
+      half_step(kt + 1, kb, nk, 1, r1, r0);
       if (kt + 2 >= nk) break;
     }
     __syncthreads();
@@ -317,8 +318,9 @@ struct Big {
 
   // ---- epilogue through LDS (weight stage 0), 32 rows at a time; 8 columns
   // per thread.  Rows 32h .. 32h+31 are block i = h%4 of the waves with wm = h/4.
+  // C / ldc: the output (EPI_F32 also serves the split-K partials).
   template <int EPI>
-  QLS_DEV void epilogue() {
+  QLS_DEV void epilogue(void* C, int64_t ldc) {
     float* sT = reinterpret_cast<float*>(sB[0]);
 #pragma unroll
     for (int h = 0; h < BM / EROWS; ++h) {
@@ -359,9 +361,9 @@ struct Big {
             u32x4 o;
 #pragma unroll
             for (int e = 0; e < 4; ++e) o[e] = pack2_bf16(y[2 * e], y[2 * e + 1]);
-            *reinterpret_cast<u32x4*>(reinterpret_cast<uint16_t*>(g.C) + (int64_t)m * g.ldc + n) = o;
+            *reinterpret_cast<u32x4*>(reinterpret_cast<uint16_t*>(C) + (int64_t)m * ldc + n) = o;
           } else if constexpr (EPI == EPI_F32) {
-            float* c = reinterpret_cast<float*>(g.C) + (int64_t)m * g.ldc + n;
+            float* c = reinterpret_cast<float*>(C) + (int64_t)m * ldc + n;
             *reinterpret_cast<f32x4*>(c) = f32x4{y[0], y[1], y[2], y[3]};
             *reinterpret_cast<f32x4*>(c + 4) = f32x4{y[4], y[5], y[6], y[7]};
           } else if constexpr (EPI == EPI_SWIGLU_BWD) {
@@ -383,7 +385,7 @@ struct Big {
               og[e] = pack2_bf16(dg[0], dg[1]);
               ou[e] = pack2_bf16(du[0], du[1]);
             }
-            uint16_t* out = reinterpret_cast<uint16_t*>(g.C) + (int64_t)m * g.ldc;
+            uint16_t* out = reinterpret_cast<uint16_t*>(C) + (int64_t)m * ldc;
             *reinterpret_cast<u32x4*>(out + n) = og;
             *reinterpret_cast<u32x4*>(out + g.I + n) = ou;
           }
@@ -410,9 +412,16 @@ big_kernel(GemmArgs g, const float* __restrict__ cb) {
   const int m0 = (blockIdx.x / tiles_n) * BM, n0 = (blockIdx.x % tiles_n) * BN;
   Big<BL> k(g, sA0, sA1, sB0, sB1, lut2, m0, n0);
   __syncthreads();
-  if ((BL == B_NF4_NT && g.lora == LORA_FWD) || (BL == B_NF4_NN && g.lora == LORA_DX)) k.lora();
-  k.mainloop();
-  k.template epilogue<EPI>();
+  // Split-K: slice z takes contraction steps [nk z / ks, nk (z+1) / ks), the
+  // LoRA term goes into slice 0 only, and each slice writes alpha * acc as a
+  // float partial that gemm_reduce_epi sums in slice order.
+  const int nk = g.K / BK, ks = g.ksplit > 1 ? g.ksplit : 1, z = blockIdx.z;
+  if (z == 0 && ((BL == B_NF4_NT && g.lora == LORA_FWD) || (BL == B_NF4_NN && g.lora == LORA_DX))) k.lora();
+  k.mainloop(nk * z / ks, nk * (z + 1) / ks);
+  if (ks > 1)
+    k.template epilogue<EPI_F32>(g.partial + (int64_t)z * g.M * g.N, g.N);
+  else
+    k.template epilogue<EPI>(g.C, g.ldc);
 }
 
 }  // namespace
@@ -425,7 +434,8 @@ bool fits31(int64_t bytes) { return bytes < 0x7fffffffLL; }
 }  // namespace
 
 bool gemm_big_ok(const GemmArgs& g, int bload, int epi) {
-  if (g.M <= 0 || g.N <= 0 || g.K <= 0 || g.K % BK || g.ksplit > 1) return false;
+  if (g.M <= 0 || g.N <= 0 || g.K <= 0 || g.K % BK) return false;
+  if (g.ksplit > 1 && (!g.partial || !a16(g.partial) || g.N % 8 || g.ksplit > g.K / BK)) return false;
   if (g.lda % 8 || !a16(g.A) || !fits31((int64_t)g.M * g.lda * 2)) return false;
   if (g.ldq % 64 || !g.Bq || !g.Bs || !a16(g.C)) return false;
   if (bload == B_NF4_NT) {
@@ -461,15 +471,18 @@ int gemm_big_launch(const GemmArgs& g, int bload, int epi, hipStream_t st) {
   if (!gemm_big_ok(g, bload, epi)) return -1;
   const float* cb = nf4_codebook_dev();
   const unsigned tiles = (unsigned)(((g.M + BM - 1) / BM) * ((g.N + BN - 1) / BN));
+  const unsigned ks = g.ksplit > 1 ? (unsigned)g.ksplit : 1u;
+  const dim3 grid(tiles, 1, ks);
   if (g.ev0) (void)hipEventRecord(g.ev0, st);
   if (bload == B_NF4_NT)
-    hipLaunchKernelGGL((big_kernel<B_NF4_NT, EPI_BF16>), dim3(tiles), dim3(NT), 0, st, g, cb);
+    hipLaunchKernelGGL((big_kernel<B_NF4_NT, EPI_BF16>), grid, dim3(NT), 0, st, g, cb);
   else if (epi == EPI_F32)
-    hipLaunchKernelGGL((big_kernel<B_NF4_NN, EPI_F32>), dim3(tiles), dim3(NT), 0, st, g, cb);
+    hipLaunchKernelGGL((big_kernel<B_NF4_NN, EPI_F32>), grid, dim3(NT), 0, st, g, cb);
   else if (epi == EPI_BF16)
-    hipLaunchKernelGGL((big_kernel<B_NF4_NN, EPI_BF16>), dim3(tiles), dim3(NT), 0, st, g, cb);
+    hipLaunchKernelGGL((big_kernel<B_NF4_NN, EPI_BF16>), grid, dim3(NT), 0, st, g, cb);
   else
-    hipLaunchKernelGGL((big_kernel<B_NF4_NN, EPI_SWIGLU_BWD>), dim3(tiles), dim3(NT), 0, st, g, cb);
+    hipLaunchKernelGGL((big_kernel<B_NF4_NN, EPI_SWIGLU_BWD>), grid, dim3(NT), 0, st, g, cb);
   if (g.ev1) (void)hipEventRecord(g.ev1, st);
+  if (ks > 1) gemm_reduce_epi(g, epi, st);
   return 0;
 }

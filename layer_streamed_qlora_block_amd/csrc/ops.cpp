@@ -9,7 +9,7 @@ namespace {
 
 constexpr int kSkinnyTarget = 1024;  // workgroups to aim for with split-K
 constexpr int kMaxSplit = 64;
-constexpr int64_t kBigPartial = 512LL * 128 * 128;   // floats available to a split big GEMM
+constexpr int64_t kBigPartial = 512LL * 4096 * 8;    // floats available to a split big GEMM (64 MB)
 
 // Skinny products (one side is the LoRA rank): each k-tile iteration of a
 // 64 x 64 tile is latency-bound, so the contraction is split into slices of at
@@ -53,10 +53,22 @@ int big_split(int M, int N, int K) {
   return std::max(1, std::min(ks, 16));
 }
 
-// The dequant-GEMMs take the 256 x 256 kernels once there are at least as
-// many such tiles as CUs (no split-K needed to fill the chip); 128 x 128 tiles
-// with split-K otherwise.
-bool use_big(int M, int N) { return cdiv(M, 256) * cdiv(N, 256) >= 256; }
+// One 256 x 256 workgroup (512 threads, ~138 KB of LDS) fills a CU, so a
+// launch of at least 192 of them (one wave over the 256 CUs, >= 75% of them
+// busy) runs the big kernels.  With fewer output tiles the contraction is
+// split into up to 256 / tiles slices of at least 16 steps of 64, partials
+// within kBigPartial; when that still leaves fewer than 192 workgroups the
+// 128 x 128 kernels (several workgroups per CU) take the GEMM.
+GemmPlan plan_nf4(int M, int N, int K, bool can_split) {
+  const int64_t tiles = cdiv(M, 256) * cdiv(N, 256);
+  if (tiles >= 192) return {true, 1};
+  if (can_split) {
+    const int nk = K / 64;
+    for (int ks = (int)std::min<int64_t>(256 / std::max<int64_t>(tiles, 1), nk / 16); ks >= 2; --ks)
+      if (tiles * ks >= 192 && (int64_t)M * N * ks <= kBigPartial) return {true, ks};
+  }
+  return {false, can_split ? big_split(M, N, K) : 1};
+}
 
 int64_t skinny_partial_floats(int64_t max_mn) {
   return std::max<int64_t>({max_mn, (int64_t)kSkinnyTarget * 64 * 64, kBigPartial});
@@ -89,7 +101,7 @@ int skinny_dA(const uint16_t* du, int64_t lddu, int T, int r, const uint16_t* x,
   return skinny(A_COL, du, lddu, B_BF16_NN, x, ldx, r, K, T, 1.f, 1, dA, K, part, st);
 }
 
-int linear_fwd(const LinearFwd& f, hipStream_t st) {
+int linear_fwd(LinearFwd& f, hipStream_t st) {
   const int64_t ldx = f.ldx ? f.ldx : f.K;
   const bool lora = f.A != nullptr && f.r > 0;
   if (lora) {
@@ -112,15 +124,25 @@ int linear_fwd(const LinearFwd& f, hipStream_t st) {
   }
   g.ev0 = f.ev0;
   g.ev1 = f.ev1;
-  if (use_big(f.T, f.N) && gemm_big_ok(g, B_NF4_NT, EPI_BF16))
-    return gemm_big_launch(g, B_NF4_NT, EPI_BF16, st);
   // Split-K needs the workspace for its partials; without one the GEMM runs unsplit.
-  g.ksplit = f.ws ? big_split(f.T, f.N, f.K) : 1;
+  const GemmPlan pl = plan_nf4(f.T, f.N, f.K, f.ws != nullptr);
   g.partial = f.ws;
-  return gemm_launch(g, A_ROW, B_NF4_NT, EPI_BF16, 128, st);
+  int rc;
+  g.ksplit = pl.ksplit;
+  if (pl.big && gemm_big_ok(g, B_NF4_NT, EPI_BF16)) {
+    f.tile = 256;
+    rc = gemm_big_launch(g, B_NF4_NT, EPI_BF16, st);
+  } else {
+    f.tile = 128;
+    g.ksplit = f.ws ? big_split(f.T, f.N, f.K) : 1;
+    rc = gemm_launch(g, A_ROW, B_NF4_NT, EPI_BF16, 128, st);
+  }
+  f.ksplit = g.ksplit;
+  if (!rc && f.ev2 && g.ksplit > 1) (void)hipEventRecord(f.ev2, st);
+  return rc;
 }
 
-int linear_dx(const LinearDx& d, hipStream_t st) {
+int linear_dx(LinearDx& d, hipStream_t st) {
   GemmArgs g{};
   g.M = d.T; g.N = d.Nout; g.K = d.Kc;
   g.A = d.dy; g.lda = d.lddy;
@@ -136,10 +158,19 @@ int linear_dx(const LinearDx& d, hipStream_t st) {
   g.gu = d.gu; g.ldgu = d.ldgu; g.I = d.I;
   g.ev0 = d.ev0;
   g.ev1 = d.ev1;
-  if (use_big(d.T, d.Nout) && gemm_big_ok(g, B_NF4_NN, d.epi)) return gemm_big_launch(g, B_NF4_NN, d.epi, st);
-  if (d.ws) {
-    g.ksplit = big_split(d.T, d.Nout, d.Kc);
-    g.partial = d.ws;
+  const GemmPlan pl = plan_nf4(d.T, d.Nout, d.Kc, d.ws != nullptr);
+  g.partial = d.ws;
+  int rc;
+  g.ksplit = pl.ksplit;
+  if (pl.big && gemm_big_ok(g, B_NF4_NN, d.epi)) {
+    d.tile = 256;
+    rc = gemm_big_launch(g, B_NF4_NN, d.epi, st);
+  } else {
+    d.tile = 128;
+    g.ksplit = d.ws ? big_split(d.T, d.Nout, d.Kc) : 1;
+    rc = gemm_launch(g, A_ROW, B_NF4_NN, d.epi, 128, st);
   }
-  return gemm_launch(g, A_ROW, B_NF4_NN, d.epi, 128, st);
+  d.ksplit = g.ksplit;
+  if (!rc && d.ev2 && g.ksplit > 1) (void)hipEventRecord(d.ev2, st);
+  return rc;
 }

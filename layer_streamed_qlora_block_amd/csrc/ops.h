@@ -18,9 +18,12 @@ struct LinearFwd {
   uint16_t* y; int64_t ldy;
   uint16_t* u;                  // U_cat [T, nmod*r]
   float* ws;                    // split-K partials
-  hipEvent_t ev0, ev1;          // optional: recorded around the dequant-GEMM launch
+  hipEvent_t ev0, ev1;          // optional: recorded around the dequant-GEMM kernel
+  hipEvent_t ev2;               // optional: recorded after its split-K reduce (only if split)
+  int tile;                     // out: 256 or 128, the output tile of the kernel taken
+  int ksplit;                   // out: contraction slices of that kernel (1: no reduce)
 };
-int linear_fwd(const LinearFwd& f, hipStream_t st);
+int linear_fwd(LinearFwd& f, hipStream_t st);
 
 // out = dY W + du_cat A_cat, contraction over W's Kc rows (dY [T, Kc]) and the
 // rc concatenated LoRA ranks; W NF4 with Nout columns.
@@ -32,14 +35,19 @@ struct LinearDx {
   void* out; int64_t ldo; int epi;    // EPI_F32 / EPI_BF16 / EPI_SWIGLU_BWD
   const uint16_t* gu; int64_t ldgu; int I;
   float* ws;                    // split-K partials (nullptr: no split)
-  hipEvent_t ev0, ev1;          // optional: recorded around the launch
+  hipEvent_t ev0, ev1;          // optional: recorded around the dequant-GEMM kernel
+  hipEvent_t ev2;               // optional: recorded after its split-K reduce (only if split)
+  int tile;                     // out: 256 or 128, the output tile of the kernel taken
+  int ksplit;                   // out: contraction slices of that kernel (1: no reduce)
 };
-int linear_dx(const LinearDx& d, hipStream_t st);
+int linear_dx(LinearDx& d, hipStream_t st);
 // Split-K factor for a 128 x 128-tiled GEMM of M x N x K (partials fit in
 // skinny_partial_floats()).
 int big_split(int M, int N, int K);
-// True when an M x N dequant-GEMM takes the 256 x 256 kernels.
-bool use_big(int M, int N);
+// Kernel choice for an M x N x K dequant-GEMM: the 256 x 256 kernels (big)
+// with ksplit contraction slices, or the 128 x 128 ones.
+struct GemmPlan { bool big; int ksplit; };
+GemmPlan plan_nf4(int M, int N, int K, bool can_split);
 
 // Skinny LoRA products (split-K over the long dimension, deterministic reduce).
 // U = bf16(x A^T)                   x [T, K] (ldx), A [n, K]          -> U [T, n] (ldu)

@@ -129,7 +129,8 @@ bool check_run(const Shape& sh, const qls_run_cfg* run, std::string* why) {
 }
 
 struct TimedEv { hipEvent_t a, b; };
-struct TimedK { hipEvent_t a, b; double gflop; };
+// A timed dequant-GEMM: a..b the kernel, b..c its split-K reduce (c null: none).
+struct TimedK { hipEvent_t a, b, c; double gflop; bool big; };
 
 }  // namespace
 
@@ -166,15 +167,21 @@ struct qls_session {
   std::vector<TimedEv> copy_ev, comp_ev, step_ev;
   std::vector<TimedK> kf_ev, kd_ev;
   void clear_timing() { ev_next = 0; copy_ev.clear(); comp_ev.clear(); step_ev.clear(); kf_ev.clear(); kd_ev.clear(); }
-  void tag_fwd(LinearFwd& f, bool lora) {
-    if (!timing) return;
-    f.ev0 = next_ev(); f.ev1 = next_ev();
-    kf_ev.push_back({f.ev0, f.ev1, 2e-9 * f.T * (double)f.N * (f.K + (lora ? f.r : 0))});
+  int run_fwd(LinearFwd& f, bool lora, hipStream_t st) {
+    if (timing) { f.ev0 = next_ev(); f.ev1 = next_ev(); f.ev2 = next_ev(); }
+    const int rc = linear_fwd(f, st);
+    if (timing && !rc)
+      kf_ev.push_back({f.ev0, f.ev1, f.ksplit > 1 ? f.ev2 : nullptr,
+                       2e-9 * f.T * (double)f.N * (f.K + (lora ? f.r : 0)), f.tile == 256});
+    return rc;
   }
-  void tag_dx(LinearDx& d) {
-    if (!timing) return;
-    d.ev0 = next_ev(); d.ev1 = next_ev();
-    kd_ev.push_back({d.ev0, d.ev1, 2e-9 * d.T * (double)d.Nout * (d.Kc + d.rc)});
+  int run_dx(LinearDx& d, hipStream_t st) {
+    if (timing) { d.ev0 = next_ev(); d.ev1 = next_ev(); d.ev2 = next_ev(); }
+    const int rc = linear_dx(d, st);
+    if (timing && !rc)
+      kd_ev.push_back({d.ev0, d.ev1, d.ksplit > 1 ? d.ev2 : nullptr,
+                       2e-9 * d.T * (double)d.Nout * (d.Kc + d.rc), d.tile == 256});
+    return rc;
   }
 
   template <class T> T* at(int64_t off) const { return reinterpret_cast<T*>(ws + off); }
@@ -311,8 +318,7 @@ int fwd_layer(qls_session* S, int l, const uint8_t* rec, const uint16_t* x, uint
   f.nmod = 3; f.mod_end[0] = sh.qd; f.mod_end[1] = sh.qd + sh.kvd; f.mod_end[2] = sh.nqkv;
   f.Bm[0] = lw + S->wb[QLS_Q]; f.Bm[1] = lw + S->wb[QLS_K]; f.Bm[2] = lw + S->wb[QLS_V];
   f.s = sh.s; f.y = qkv; f.ldy = sh.nqkv; f.u = S->at<uint16_t>(S->p.uqkv); f.ws = part;
-  S->tag_fwd(f, lora);
-  QLS_RC(linear_fwd(f, st));
+  QLS_RC(S->run_fwd(f, lora, st));
   rope_fwd(qkv, sh.nqkv, T, Sq, sh.c.n_heads, sh.c.n_kv_heads, sh.c.head_dim, S->at<float>(S->p.rope), st);
   AttnArgs aa{};
   aa.qkv = qkv; aa.ld = sh.nqkv; aa.q_off = 0; aa.k_off = sh.qd; aa.v_off = sh.qd + sh.kvd;
@@ -327,8 +333,7 @@ int fwd_layer(qls_session* S, int l, const uint8_t* rec, const uint16_t* x, uint
   f.A = lora ? lw + S->wa[QLS_O] : nullptr;
   f.nmod = 1; f.mod_end[0] = d; f.Bm[0] = lw + S->wb[QLS_O];
   f.s = sh.s; f.res = x; f.ldres = d; f.y = h; f.ldy = d; f.u = S->at<uint16_t>(S->p.uo); f.ws = part;
-  S->tag_fwd(f, lora);
-  QLS_RC(linear_fwd(f, st));
+  QLS_RC(S->run_fwd(f, lora, st));
 
   rmsnorm_fwd(h, w.nm, sh.c.rms_eps, n2, T, d, st);
   f = LinearFwd{};
@@ -338,8 +343,7 @@ int fwd_layer(qls_session* S, int l, const uint8_t* rec, const uint16_t* x, uint
   f.nmod = 2; f.mod_end[0] = I; f.mod_end[1] = 2 * I;
   f.Bm[0] = lw + S->wb[QLS_GATE]; f.Bm[1] = lw + S->wb[QLS_UP];
   f.s = sh.s; f.y = gu; f.ldy = 2 * I; f.u = S->at<uint16_t>(S->p.ugu); f.ws = part;
-  S->tag_fwd(f, lora);
-  QLS_RC(linear_fwd(f, st));
+  QLS_RC(S->run_fwd(f, lora, st));
   swiglu_fwd(gu, a, T, I, st);
 
   f = LinearFwd{};
@@ -348,8 +352,7 @@ int fwd_layer(qls_session* S, int l, const uint8_t* rec, const uint16_t* x, uint
   f.A = lora ? lw + S->wa[QLS_DOWN] : nullptr;
   f.nmod = 1; f.mod_end[0] = d; f.Bm[0] = lw + S->wb[QLS_DOWN];
   f.s = sh.s; f.res = h; f.ldres = d; f.y = xout; f.ldy = d; f.u = S->at<uint16_t>(S->p.udown); f.ws = part;
-  S->tag_fwd(f, lora);
-  QLS_RC(linear_fwd(f, st));
+  QLS_RC(S->run_fwd(f, lora, st));
   return QLS_OK;
 }
 
@@ -391,8 +394,7 @@ int bwd_layer(qls_session* S, int l, const uint8_t* rec, const uint16_t* x, floa
   x1.du = du; x1.lddu = r; x1.Acat = lw + S->wa[QLS_DOWN]; x1.rc = r;
   x1.out = dgu; x1.ldo = 2 * I; x1.epi = EPI_SWIGLU_BWD; x1.ws = part;
   x1.gu = S->at<uint16_t>(S->p.gu); x1.ldgu = 2 * I; x1.I = I;
-  S->tag_dx(x1);
-  QLS_RC(linear_dx(x1, st));
+  QLS_RC(S->run_dx(x1, st));
 
   // ---- gate / up
   for (int k = 0; k < 2; ++k) {
@@ -406,8 +408,7 @@ int bwd_layer(qls_session* S, int l, const uint8_t* rec, const uint16_t* x, floa
   x2.codes = w.code[QLS_GATE]; x2.absmax = w.amax[QLS_GATE]; x2.ldq = d;
   x2.du = du; x2.lddu = 2 * r; x2.Acat = lw + S->wa[QLS_GATE]; x2.rc = 2 * r;
   x2.out = dn; x2.ldo = d; x2.epi = EPI_F32; x2.ws = part;
-  S->tag_dx(x2);
-  QLS_RC(linear_dx(x2, st));
+  QLS_RC(S->run_dx(x2, st));
   rmsnorm_bwd(h, w.nm, sh.c.rms_eps, dn, g, dh, dyb, T, d, st);
 
   // ---- o projection
@@ -419,8 +420,7 @@ int bwd_layer(qls_session* S, int l, const uint8_t* rec, const uint16_t* x, floa
   x3.codes = w.code[QLS_O]; x3.absmax = w.amax[QLS_O]; x3.ldq = sh.qd;
   x3.du = du; x3.lddu = r; x3.Acat = lw + S->wa[QLS_O]; x3.rc = r;
   x3.out = S->at<uint16_t>(S->p.dattn); x3.ldo = sh.qd; x3.epi = EPI_BF16; x3.ws = part;
-  S->tag_dx(x3);
-  QLS_RC(linear_dx(x3, st));
+  QLS_RC(S->run_dx(x3, st));
 
   // ---- attention + RoPE
   AttnBwdArgs ab{};
@@ -450,8 +450,7 @@ int bwd_layer(qls_session* S, int l, const uint8_t* rec, const uint16_t* x, floa
   x4.codes = w.code[QLS_Q]; x4.absmax = w.amax[QLS_Q]; x4.ldq = d;
   x4.du = du; x4.lddu = 3 * r; x4.Acat = lw + S->wa[QLS_Q]; x4.rc = 3 * r;
   x4.out = dn; x4.ldo = d; x4.epi = EPI_F32; x4.ws = part;
-  S->tag_dx(x4);
-  QLS_RC(linear_dx(x4, st));
+  QLS_RC(S->run_dx(x4, st));
   rmsnorm_bwd(x, w.na, sh.c.rms_eps, dn, dh, g, nullptr, T, d, st);
   return QLS_OK;
 }
@@ -829,8 +828,18 @@ int qls_session_stats(qls_session* S, qls_stats* o) {
     }
     for (auto& e : S->step_ev) o->step_ms += span(e.a, e.b);
     o->step_ms /= (double)S->step_ev.size();
-    for (auto& k : S->kf_ev) { o->dq_fwd_ms += span(k.a, k.b); o->dq_fwd_gflop += k.gflop; }
-    for (auto& k : S->kd_ev) { o->dq_dx_ms += span(k.a, k.b); o->dq_dx_gflop += k.gflop; }
+    for (auto& k : S->kf_ev) {
+      const double ms = span(k.a, k.b);
+      o->dq_fwd_ms += ms; o->dq_fwd_gflop += k.gflop;
+      if (k.c) o->dq_fwd_reduce_ms += span(k.b, k.c);
+      if (k.big) { o->dq_fwd_big_ms += ms; o->dq_fwd_big_gflop += k.gflop; ++o->dq_fwd_big_launches; }
+    }
+    for (auto& k : S->kd_ev) {
+      const double ms = span(k.a, k.b);
+      o->dq_dx_ms += ms; o->dq_dx_gflop += k.gflop;
+      if (k.c) o->dq_dx_reduce_ms += span(k.b, k.c);
+      if (k.big) { o->dq_dx_big_ms += ms; o->dq_dx_big_gflop += k.gflop; ++o->dq_dx_big_launches; }
+    }
     o->dq_fwd_launches = (int64_t)S->kf_ev.size();
     o->dq_dx_launches = (int64_t)S->kd_ev.size();
   }
