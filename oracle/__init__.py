@@ -26,6 +26,13 @@ Pins (what the oracle is checked against, in ``tests/test_oracle_*.py``):
                        attention / cross-entropy, B = 0 identities, the
                        adapters-disabled reference pass, the DPO ln 2 closed
                        form.
+  pref.head         -- closed forms where each sigmoid term is 1/2, ORPO odds
+                       through p / (1 - p), float64 central differences of
+                       every head (KTO with its reference point held).
+  model.pref_step   -- float64 central differences of the step's LoRA
+                       gradients per head, exact cancellation for chosen ==
+                       rejected, the DPO head against the DPO step, KTO at
+                       policy == reference.
   optim.adamw_step  -- torch.optim.AdamW in float64 over several steps (with and
                        without weight decay), the step-1 closed form, mirror
                        precision within float32 rounding of float64.

@@ -405,3 +405,28 @@ def dpo_step(cfg, P, model, lora, chosen, rejected, prompt_len, beta):
     g = head_backward(cfg, P, model, xs[-1], hc, tgt, w.reshape(-1))
     _, grads = backward_sweep(cfg, P, model, lora, xs, g, B, S, tabs)
     return loss, grads, {"pi": pol, "ref": ref, "z": z}
+
+
+def pref_step(cfg, P, model, lora, chosen, rejected, prompt_len, kind, **params):
+    """One preference step of head ``kind`` (oracle.pref) on one (chosen,
+    rejected) pair that shares ids[:prompt_len]: the adapters-disabled
+    reference pass for the heads that use one, the policy pass, the head on the
+    response log-likelihoods, and the backward of -dL/dpi_x spread over each
+    response token's log-probability into the LoRA matrices."""
+    from . import pref
+    ids = np.stack([np.asarray(chosen), np.asarray(rejected)])
+    B, S = ids.shape
+    n = (S - prompt_len, S - prompt_len)
+    ref = (np.zeros(2) if not pref.needs_reference(kind)
+           else seq_logprobs(cfg, P, model, None, ids, prompt_len)[0])
+    xs, tabs = forward_sweep(cfg, P, model, lora, ids)
+    hc = head_forward(cfg, P, model, xs[-1])
+    tgt = targets(ids)
+    lp = row_logp(hc, tgt).reshape(B, S)
+    pol = lp[:, prompt_len - 1:S - 1].astype(np.float64).sum(axis=1)
+    loss, dpi = pref.head(kind, pol, ref, n, **params)
+    w = np.zeros((B, S))
+    w[:, prompt_len - 1:S - 1] = -np.asarray(dpi)[:, None]
+    g = head_backward(cfg, P, model, xs[-1], hc, tgt, w.reshape(-1))
+    _, grads = backward_sweep(cfg, P, model, lora, xs, g, B, S, tabs)
+    return float(loss), grads, {"pi": pol, "ref": np.asarray(ref, dtype=np.float64), "dpi": dpi}
