@@ -148,7 +148,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--optimizer", choices=["adamw", "none"], default="adamw",
                     help="update the LoRA vector with AdamW (lr 2e-5, the pages' config) inside every timed step")
-    ap.add_argument("--dpo", action="store_true", help="also time DPO steps (2 x seq, shared 128-token prompt)")
+    ap.add_argument("--dpo", action="store_true", help="same as --pref dpo")
+    ap.add_argument("--pref", nargs="*", default=[], choices=["dpo", "simpo", "orpo", "kto"],
+                    help="also time preference steps of these heads (2 x seq, shared 128-token prompt)")
     ap.add_argument("--threads", type=int, default=min(16, os.cpu_count() or 1))
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="only copy a device buffer of this many MiB 3 times and exit: the known-size "
@@ -191,7 +193,7 @@ def main():
     loss = torch.empty(1, dtype=torch.float32, device="cuda")
     ids = torch.from_numpy(synth.token_ids(cfg, B, S, seed=41 if S == 512 else 42)).cuda()
     mode = q.QLS_STREAMED if args.mode == "streamed" else q.QLS_RESIDENT
-    max_tokens = max(T, 2 * S) if args.dpo else T
+    max_tokens = max(T, 2 * S) if (args.dpo or args.pref) else T
     sess = q.Session(store, emb, lm, fn, max_tokens=max_tokens, max_seq=S, mode=mode, timing=True)
     print(f"[bench] session ready ({sess.ws_bytes / 1e9:.2f} GB workspace), setup "
           f"{time.perf_counter() - t_setup:.1f} s", file=sys.stderr, flush=True)
@@ -283,21 +285,28 @@ def main():
         "gpu_clock": clock[0],
         "loss": round(loss_v, 5),
     }
-    if args.dpo:
+    kinds = list(dict.fromkeys((["dpo"] if args.dpo else []) + args.pref))
+    if kinds:
         P = 128
         c, r = synth.dpo_pair(cfg, S, P)
         c, r = torch.from_numpy(c).cuda(), torch.from_numpy(r).cuda()
-        sess.dpo_step(c, r, P, 0.1, lora, grads, loss)
-        torch.cuda.synchronize()
-        sess.reset_stats()
-        t0 = time.perf_counter()
-        n = max(1, args.steps // 2)
-        for _ in range(n):
-            sess.dpo_step(c, r, P, 0.1, lora, grads, loss)
-        torch.cuda.synchronize()
-        dt = (time.perf_counter() - t0) / n
-        out["dpo"] = {"ms_per_step": round(1e3 * dt, 3), "tokens_per_s": round(2 * S / dt, 2),
-                      "layer_loads_per_step": sess.stats()["layer_loads"] / n, "loss": float(loss.item())}
+        params = {"dpo": {"beta": 0.1}, "simpo": {"beta": 2.0, "gamma": 1.0}, "orpo": {"lam": 0.1},
+                  "kto": {"beta": 0.1, "lam_d": 1.0, "lam_u": 1.0}}
+        out["pref"] = {}
+        for kind in kinds:
+            sess.pref_step(kind, c, r, P, lora, grads, loss, **params[kind])
+            torch.cuda.synchronize()
+            sess.reset_stats()
+            t0 = time.perf_counter()
+            n = max(1, args.steps // 2)
+            for _ in range(n):
+                sess.pref_step(kind, c, r, P, lora, grads, loss, **params[kind])
+            torch.cuda.synchronize()
+            dt = (time.perf_counter() - t0) / n
+            out["pref"][kind] = {"params": params[kind], "ms_per_step": round(1e3 * dt, 3),
+                                 "tokens_per_s": round(2 * S / dt, 2),
+                                 "layer_loads_per_step": sess.stats()["layer_loads"] / n,
+                                 "loss": float(loss.item())}
     sess.close()
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on a bounded sample", file=sys.stderr, flush=True)

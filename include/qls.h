@@ -313,10 +313,48 @@ int qls_logprobs(qls_session* s, const int32_t* d_ids, int B, int S, int prompt_
  * each resident layer inside the same forward sweep as the policy, so the
  * step streams the stack exactly as an SFT step does.  Loss = softplus(-z),
  * z = beta((pi_c - ref_c) - (pi_r - ref_r)), log-probs summed over the
- * response positions.  d_aux (optional) float32 [4] = pi_c, pi_r, ref_c, ref_r. */
+ * response positions.  d_aux (optional) float32 [4] = pi_c, pi_r, ref_c, ref_r.
+ * Same as qls_pref_step with kind QLS_PREF_DPO. */
 int qls_dpo_step(qls_session* s, const int32_t* d_chosen, const int32_t* d_rejected, int S,
                  int prompt_len, float beta, const float* d_lora, float* d_grads,
                  float* d_loss, float* h_loss, float* d_aux);
+
+/* Preference heads on a (chosen, rejected) pair, after the papers that
+ * define them (the pages name the four methods as running on the layer stream
+ * and give KTO the same adapters-disabled reference as DPO: page "Soup ...
+ * radar note", section "In detail").  With pi_x the response log-likelihood
+ * of sequence x, rho_x the same with the adapters disabled and n = S -
+ * prompt_len response tokens:
+ *   QLS_PREF_DPO    z = beta((pi_c - rho_c) - (pi_r - rho_r)), L = softplus(-z)
+ *   QLS_PREF_SIMPO  z = beta pi_c / n - beta pi_r / n - gamma,  L = softplus(-z)
+ *                   (reference-free)
+ *   QLS_PREF_ORPO   l_x = pi_x / n, lo_x = l_x - log(1 - e^l_x),
+ *                   L = -l_c + lambda softplus(lo_r - lo_c) (reference-free)
+ *   QLS_PREF_KTO    r_x = pi_x - rho_x, z0 = max(0, (r_c + r_r) / 2) held
+ *                   constant, chosen desirable and rejected undesirable:
+ *                   L = (lambda_d (1 - sigmoid(beta (r_c - z0)))
+ *                        + lambda_u (1 - sigmoid(beta (z0 - r_r)))) / 2
+ * Unused fields are ignored; beta > 0 except for ORPO, the lambdas >= 0. */
+enum qls_pref_kind { QLS_PREF_DPO = 0, QLS_PREF_SIMPO = 1, QLS_PREF_ORPO = 2, QLS_PREF_KTO = 3 };
+typedef struct qls_pref_cfg {
+  int32_t kind;     /* qls_pref_kind */
+  float beta;       /* DPO, SimPO, KTO */
+  float gamma;      /* SimPO target margin */
+  float lambda;     /* ORPO odds-ratio weight */
+  float lambda_d;   /* KTO desirable weight */
+  float lambda_u;   /* KTO undesirable weight */
+} qls_pref_cfg;
+
+/* One preference step of head cfg->kind, otherwise as qls_dpo_step: heads
+ * with a reference compute it on each resident layer inside the policy's
+ * forward sweep; the reference-free heads skip it.  Either way the step
+ * streams the stack exactly as an SFT step does.  d_aux (optional) float32
+ * [4] = pi_c, pi_r, rho_c, rho_r (rho = 0 without a reference).  Errors:
+ * QLS_EINVAL for an unknown kind, non-finite parameters, beta <= 0 where beta
+ * is used, a negative weight, or the conditions of qls_dpo_step. */
+int qls_pref_step(qls_session* s, const qls_pref_cfg* cfg, const int32_t* d_chosen,
+                  const int32_t* d_rejected, int S, int prompt_len, const float* d_lora,
+                  float* d_grads, float* d_loss, float* h_loss, float* d_aux);
 
 /* One streamed decoder layer on its own: forward, recomputed forward and
  * backward of layer `layer` for input d_x bf16 [B*S x hidden] and upstream

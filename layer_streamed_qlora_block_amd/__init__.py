@@ -21,6 +21,8 @@ _lib = C.CDLL(LIB_PATH)
 QLS_OK, QLS_EINVAL, QLS_ENOMEM, QLS_ENOPIN, QLS_EHIP, QLS_ESTATE, QLS_EUNSUPPORTED = 0, -1, -2, -3, -4, -5, -6
 QLS_STREAMED, QLS_RESIDENT = 0, 1
 QLS_ABSMAX_F32, QLS_ABSMAX_DQ8 = 0, 1
+QLS_PREF_DPO, QLS_PREF_SIMPO, QLS_PREF_ORPO, QLS_PREF_KTO = 0, 1, 2, 3
+PREF_KINDS = {"dpo": QLS_PREF_DPO, "simpo": QLS_PREF_SIMPO, "orpo": QLS_PREF_ORPO, "kto": QLS_PREF_KTO}
 NMOD = 7
 MODULES = ("q", "k", "v", "o", "gate", "up", "down")
 DBG_POISON_ON_RELEASE, DBG_COPY_DELAY, DBG_COMPUTE_DELAY, DBG_NO_REUSE = 1, 2, 4, 8
@@ -37,6 +39,11 @@ class ModelCfg(C.Structure):
                 ("n_kv_heads", C.c_int32), ("head_dim", C.c_int32), ("intermediate", C.c_int32),
                 ("vocab", C.c_int32), ("rms_eps", C.c_float), ("rope_theta", C.c_float),
                 ("lora_r", C.c_int32), ("lora_alpha", C.c_float)]
+
+
+class PrefCfg(C.Structure):
+    _fields_ = [("kind", C.c_int32), ("beta", C.c_float), ("gamma", C.c_float), ("lambda_", C.c_float),
+                ("lambda_d", C.c_float), ("lambda_u", C.c_float)]
 
 
 class RunCfg(C.Structure):
@@ -101,6 +108,7 @@ _SIG = {
     "qls_sft_step": (_I, [_P, _P, _I, _I, _P, _P, _P, _P]),
     "qls_logprobs": (_I, [_P, _P, _I, _I, _I, _P, _P, _P]),
     "qls_dpo_step": (_I, [_P, _P, _P, _I, _I, _F, _P, _P, _P, _P, _P]),
+    "qls_pref_step": (_I, [_P, C.POINTER(PrefCfg), _P, _P, _I, _I, _P, _P, _P, _P, _P]),
     "qls_layer_fwd_bwd": (_I, [_P, _I, _P, _P, _I, _I, _P, _P, _P, _P]),
     "qls_session_checkpoints": (_I, [_P, C.POINTER(_P), C.POINTER(_I64)]),
     "qls_session_stats": (_I, [_P, C.POINTER(Stats)]),
@@ -286,6 +294,21 @@ def qls_dpo_step(sess, chosen, rejected, S, prompt_len, beta, lora, grads, loss,
     _check(_lib.qls_dpo_step(sess, _ptr(chosen), _ptr(rejected), S, prompt_len, beta, _ptr(lora),
                              _ptr(grads), _ptr(loss), C.byref(hl) if want_host_loss else None, _ptr(aux)))
     return hl.value if want_host_loss else None
+
+
+def qls_pref_step(sess, cfg: PrefCfg, chosen, rejected, S, prompt_len, lora, grads, loss, aux=None,
+                  want_host_loss=False):
+    hl = C.c_float(0.0)
+    _check(_lib.qls_pref_step(sess, C.byref(cfg), _ptr(chosen), _ptr(rejected), S, prompt_len, _ptr(lora),
+                              _ptr(grads), _ptr(loss), C.byref(hl) if want_host_loss else None, _ptr(aux)))
+    return hl.value if want_host_loss else None
+
+
+def pref_cfg(kind: str, beta: float = 0.0, gamma: float = 0.0, lam: float = 0.0, lam_d: float = 1.0,
+             lam_u: float = 1.0) -> PrefCfg:
+    if kind not in PREF_KINDS:
+        raise ValueError(f"kind must be one of {sorted(PREF_KINDS)}")
+    return PrefCfg(PREF_KINDS[kind], beta, gamma, lam, lam_d, lam_u)
 
 
 def qls_layer_fwd_bwd(sess, layer, x, gout, B, S, lora, out, gin, grads):

@@ -257,32 +257,75 @@ __global__ void __launch_bounds__(TB) seq_logp_k(const float* __restrict__ logp,
   if (threadIdx.x == 0) seq[b] = s;
 }
 
-// Sigmoid DPO on one pair (rows [0, S) chosen, [S, 2S) rejected).
-__global__ void __launch_bounds__(TB) dpo_k(const float* __restrict__ lp, const float* __restrict__ lr,
-                                            int S, int P, float beta, float* __restrict__ w,
-                                            float* __restrict__ loss, float* aux) {
+QLS_DEV double sigmoid_d(double a) {
+  if (a >= 0) return 1.0 / (1.0 + exp(-a));
+  const double e = exp(a);
+  return e / (1.0 + e);
+}
+QLS_DEV double softplus_d(double a) { return fmax(a, 0.0) + log1p(exp(-fabs(a))); }
+
+// Preference head on one pair (rows [0, S) chosen, [S, 2S) rejected), one
+// block: sums the response log-likelihoods pi_x (and the reference rho_x when
+// lr is set), evaluates the head in double precision and writes the row
+// weights w_t = -dL/dpi_x on the response rows of sequence x (0 elsewhere).
+//   DPO    z = beta((pi_c - rho_c) - (pi_r - rho_r)),      L = softplus(-z)
+//   SimPO  z = beta pi_c / n - beta pi_r / n - gamma,       L = softplus(-z)
+//   ORPO   l_x = pi_x / n, lo_x = l_x - log(1 - e^l_x),    L = -l_c + lam softplus(lo_r - lo_c)
+//   KTO    r_x = pi_x - rho_x, z0 = max(0, (r_c + r_r)/2) held constant,
+//          L = (lam_d (1 - sig(beta(r_c - z0))) + lam_u (1 - sig(beta(z0 - r_r)))) / 2
+// with n = S - P response tokens per sequence.
+__global__ void __launch_bounds__(TB) pref_k(const float* __restrict__ lp, const float* __restrict__ lr,
+                                             int S, int P, PrefArgs a, float* __restrict__ w,
+                                             float* __restrict__ loss, float* aux) {
   __shared__ float red[4];
+  __shared__ float wsh[2];
   float v[4];
   for (int q = 0; q < 4; ++q) {
     const float* src = (q & 2) ? lr : lp;
     const int b = q & 1;
     float acc = 0.f;
-    for (int t = threadIdx.x; t < S; t += TB)
-      if (t >= P - 1 && t < S - 1) acc += src[(int64_t)b * S + t];
+    if (src)
+      for (int t = threadIdx.x; t < S; t += TB)
+        if (t >= P - 1 && t < S - 1) acc += src[(int64_t)b * S + t];
     v[q] = block_sum(acc, red);
   }
-  // v = pi_c, pi_r, ref_c, ref_r
-  const float z = beta * ((v[0] - v[2]) - (v[1] - v[3]));
-  const float sg = 1.f / (1.f + expf(z));                       // sigmoid(-z)
-  const float wc = beta * sg;                                   // -dL/dpi_c
+  // v = pi_c, pi_r, rho_c, rho_r
+  if (threadIdx.x == 0) {
+    const double pc = v[0], pr = v[1], rc = v[2], rr = v[3], n = (double)(S - P), beta = a.beta;
+    double L = 0, gc = 0, gr = 0;
+    if (a.kind == PREF_DPO || a.kind == PREF_SIMPO) {
+      const double z = a.kind == PREF_DPO ? beta * ((pc - rc) - (pr - rr)) : beta * pc / n - beta * pr / n - a.gamma;
+      const double sg = sigmoid_d(-z);
+      L = softplus_d(-z);
+      gc = -beta * sg;
+      gr = beta * sg;
+      if (a.kind == PREF_SIMPO) { gc /= n; gr /= n; }
+    } else if (a.kind == PREF_ORPO) {
+      const double lc = pc / n, lrn = pr / n;
+      const double qc = -expm1(lc), qr = -expm1(lrn);       // 1 - p_x
+      const double ratio = (lc - log(qc)) - (lrn - log(qr));
+      const double sg = sigmoid_d(-ratio);
+      L = -lc + a.lam * softplus_d(-ratio);
+      gc = (-1.0 - a.lam * sg / qc) / n;
+      gr = (a.lam * sg / qr) / n;
+    } else {
+      const double xc = pc - rc, xr = pr - rr;
+      const double z0 = fmax(0.0, 0.5 * (xc + xr));
+      const double su = sigmoid_d(beta * (xc - z0)), sv = sigmoid_d(beta * (z0 - xr));
+      L = 0.5 * (a.lam_d * (1.0 - su) + a.lam_u * (1.0 - sv));
+      gc = -0.5 * a.lam_d * beta * su * (1.0 - su);
+      gr = 0.5 * a.lam_u * beta * sv * (1.0 - sv);
+    }
+    *loss = (float)L;
+    wsh[0] = (float)(-gc);
+    wsh[1] = (float)(-gr);
+    if (aux) { aux[0] = v[0]; aux[1] = v[1]; aux[2] = v[2]; aux[3] = v[3]; }
+  }
+  __syncthreads();
   for (int t = threadIdx.x; t < 2 * S; t += TB) {
     const int s = t % S;
     const bool resp = s >= P - 1 && s < S - 1;
-    w[t] = resp ? (t < S ? wc : -wc) : 0.f;
-  }
-  if (threadIdx.x == 0) {
-    *loss = z > 0 ? log1pf(expf(-z)) : -z + log1pf(expf(z));   // softplus(-z)
-    if (aux) { aux[0] = v[0]; aux[1] = v[1]; aux[2] = v[2]; aux[3] = v[3]; }
+    w[t] = resp ? wsh[t < S ? 0 : 1] : 0.f;
   }
 }
 
@@ -361,10 +404,9 @@ void sft_weights_loss(const float* logp, const int32_t* tgt, int T, int N, float
 void seq_logp(const float* logp, int B, int S, int prompt_len, float* seq, float* tok, hipStream_t st) {
   hipLaunchKernelGGL(seq_logp_k, dim3(B), dim3(TB), 0, st, logp, S, prompt_len, seq, tok);
 }
-void dpo_loss(const float* logp_pol, const float* logp_ref, int S, int prompt_len, float beta,
-              float* w, float* loss, float* aux, hipStream_t st) {
-  hipLaunchKernelGGL(dpo_k, dim3(1), dim3(TB), 0, st, logp_pol, logp_ref, S, prompt_len, beta, w,
-                     loss, aux);
+void pref_loss(const PrefArgs& a, const float* logp_pol, const float* logp_ref, int S, int prompt_len,
+               float* w, float* loss, float* aux, hipStream_t st) {
+  hipLaunchKernelGGL(pref_k, dim3(1), dim3(TB), 0, st, logp_pol, logp_ref, S, prompt_len, a, w, loss, aux);
 }
 void spin_delay(int64_t ticks, hipStream_t st) {
   if (ticks <= 0) return;

@@ -101,8 +101,14 @@ void ce_targets(const int32_t* ids, int B, int S, int32_t* tgt, hipStream_t st);
 void sft_weights_loss(const float* logp, const int32_t* tgt, int T, int N, float* w, float* loss,
                       hipStream_t st);
 void seq_logp(const float* logp, int B, int S, int prompt_len, float* seq, float* tok, hipStream_t st);
-void dpo_loss(const float* logp_pol, const float* logp_ref, int S, int prompt_len, float beta,
-              float* w, float* loss, float* aux, hipStream_t st);
+// Preference heads (the qls_pref_kind values).
+enum PrefKind { PREF_DPO = 0, PREF_SIMPO = 1, PREF_ORPO = 2, PREF_KTO = 3 };
+struct PrefArgs { int kind; float beta, gamma, lam, lam_d, lam_u; };
+// Loss of head a on the pair's response log-likelihoods (logp_ref NULL for
+// the reference-free heads), row weights w [2S] = -dL/dpi per response row,
+// aux (optional) [4] = pi_c, pi_r, rho_c, rho_r.
+void pref_loss(const PrefArgs& a, const float* logp_pol, const float* logp_ref, int S, int prompt_len,
+               float* w, float* loss, float* aux, hipStream_t st);
 // AdamW update of n float32 parameters at step t (1-based), in place.
 void adamw_update(float* p, const float* g, float* m, float* v, int64_t n, int t, double lr, double b1,
                   double b2, double eps, double wd, hipStream_t st);

@@ -739,12 +739,22 @@ int qls_logprobs(qls_session* S, const int32_t* d_ids, int B, int Sq, int prompt
   return end_step(S, nullptr, nullptr);
 }
 
-int qls_dpo_step(qls_session* S, const int32_t* d_chosen, const int32_t* d_rejected, int Sq, int prompt_len,
-                 float beta, const float* d_lora, float* d_grads, float* d_loss, float* h_loss, float* d_aux) {
-  if (!S || !d_chosen || !d_rejected || !d_lora || !d_grads || !d_loss) return fail(QLS_EINVAL, "NULL argument");
+int qls_pref_step(qls_session* S, const qls_pref_cfg* cfg, const int32_t* d_chosen, const int32_t* d_rejected,
+                  int Sq, int prompt_len, const float* d_lora, float* d_grads, float* d_loss, float* h_loss,
+                  float* d_aux) {
+  if (!S || !cfg || !d_chosen || !d_rejected || !d_lora || !d_grads || !d_loss)
+    return fail(QLS_EINVAL, "NULL argument");
+  if (cfg->kind < QLS_PREF_DPO || cfg->kind > QLS_PREF_KTO) return fail(QLS_EINVAL, "unknown preference kind");
+  const float prm[5] = {cfg->beta, cfg->gamma, cfg->lambda, cfg->lambda_d, cfg->lambda_u};
+  for (float x : prm)
+    if (!std::isfinite(x)) return fail(QLS_EINVAL, "preference parameters must be finite");
+  if (cfg->kind != QLS_PREF_ORPO && !(cfg->beta > 0.f)) return fail(QLS_EINVAL, "beta must be > 0");
+  if (cfg->lambda < 0.f || cfg->lambda_d < 0.f || cfg->lambda_u < 0.f)
+    return fail(QLS_EINVAL, "loss weights must be >= 0");
   int rc = check_tokens(S, 2, Sq);
   if (rc) return rc;
   if (prompt_len < 1 || prompt_len >= Sq) return fail(QLS_EINVAL, "prompt_len must be in [1, S)");
+  const bool ref = cfg->kind == QLS_PREF_DPO || cfg->kind == QLS_PREF_KTO;
   const int B = 2, T = 2 * Sq;
   const Shape& sh = S->sh;
   const int d = sh.c.hidden;
@@ -754,20 +764,33 @@ int qls_dpo_step(qls_session* S, const int32_t* d_chosen, const int32_t* d_rejec
   QLS_HIP(hipMemcpyAsync(ids + Sq, d_rejected, Sq * 4, hipMemcpyDeviceToDevice, S->cs));
   cast_lora(S, d_lora);
   embed_gather(ids, S->res.d_embed, S->ck(0), T, d, sh.c.vocab, S->at<int>(S->p.scal), S->cs);
-  QLS_HIP(hipMemcpyAsync(S->at<uint16_t>(S->p.xref0), S->ck(0), (size_t)T * d * 2, hipMemcpyDeviceToDevice, S->cs));
+  if (ref)
+    QLS_HIP(hipMemcpyAsync(S->at<uint16_t>(S->p.xref0), S->ck(0), (size_t)T * d * 2, hipMemcpyDeviceToDevice,
+                           S->cs));
   ce_targets(ids, B, Sq, S->at<int32_t>(S->p.tgt), S->cs);
-  if ((rc = forward_sweep(S, T, B, Sq, true, true))) return rc;
+  if ((rc = forward_sweep(S, T, B, Sq, true, ref))) return rc;
   const int L = sh.c.n_layers;
-  const uint16_t* xref = S->at<uint16_t>(L & 1 ? S->p.xref1 : S->p.xref0);
-  if ((rc = head_fwd(S, xref, T, S->at<float>(S->p.logp_ref)))) return rc;
+  if (ref) {
+    const uint16_t* xref = S->at<uint16_t>(L & 1 ? S->p.xref1 : S->p.xref0);
+    if ((rc = head_fwd(S, xref, T, S->at<float>(S->p.logp_ref)))) return rc;
+  }
   const uint16_t* xL = S->ck(L);
   if ((rc = head_fwd(S, xL, T, S->at<float>(S->p.logp)))) return rc;
-  dpo_loss(S->at<float>(S->p.logp), S->at<float>(S->p.logp_ref), Sq, prompt_len, beta, S->at<float>(S->p.roww),
-           d_loss, d_aux, S->cs);
+  PrefArgs a{cfg->kind, cfg->beta, cfg->gamma, cfg->lambda, cfg->lambda_d, cfg->lambda_u};
+  pref_loss(a, S->at<float>(S->p.logp), ref ? S->at<float>(S->p.logp_ref) : nullptr, Sq, prompt_len,
+            S->at<float>(S->p.roww), d_loss, d_aux, S->cs);
   if ((rc = head_bwd(S, xL, T))) return rc;
   if ((rc = backward_sweep(S, T, B, Sq, d_grads))) return rc;
   QLS_HIP(hipGetLastError());
   return end_step(S, h_loss, d_loss);
+}
+
+int qls_dpo_step(qls_session* S, const int32_t* d_chosen, const int32_t* d_rejected, int Sq, int prompt_len,
+                 float beta, const float* d_lora, float* d_grads, float* d_loss, float* h_loss, float* d_aux) {
+  qls_pref_cfg c{};
+  c.kind = QLS_PREF_DPO;
+  c.beta = beta;
+  return qls_pref_step(S, &c, d_chosen, d_rejected, Sq, prompt_len, d_lora, d_grads, d_loss, h_loss, d_aux);
 }
 
 int qls_layer_fwd_bwd(qls_session* S, int layer, const uint16_t* d_x, const uint16_t* d_gout, int B, int Sq,

@@ -12,7 +12,7 @@ import numpy as np
 import torch
 
 from . import (QLS_ABSMAX_DQ8, QLS_ABSMAX_F32, QLS_RESIDENT, QLS_STREAMED, RunCfg, model_cfg, qls_debug_set,
-               qls_adamw_step, qls_dpo_step, qls_layer_fwd_bwd, qls_layer_record_bytes_fmt, qls_logprobs, qls_lora_numel,
+               pref_cfg, qls_adamw_step, qls_dpo_step, qls_pref_step, qls_layer_fwd_bwd, qls_layer_record_bytes_fmt, qls_logprobs, qls_lora_numel,
                qls_session_checkpoints, qls_session_create, qls_session_destroy, qls_session_reset_stats,
                qls_session_stats, qls_sft_step, qls_store_create_fmt, qls_store_destroy, qls_store_layer_view,
                qls_store_set_layer_fp32, qls_store_set_layer_nf4, qls_workspace_bytes)
@@ -126,6 +126,19 @@ class Session:
         try:
             return qls_dpo_step(self.h, chosen, rejected, S, prompt_len, beta, lora, grads, loss, aux,
                                 want_host_loss=host_loss)
+        finally:
+            self._exit()
+
+    def pref_step(self, kind, chosen, rejected, prompt_len, lora, grads, loss, aux=None, host_loss=False,
+                  **params):
+        """Preference step of head kind ("dpo", "simpo", "orpo", "kto"); params:
+        beta, gamma, lam, lam_d, lam_u (see qls_pref_step)."""
+        S = chosen.shape[-1]
+        cfg = pref_cfg(kind, **params)
+        self._enter()
+        try:
+            return qls_pref_step(self.h, cfg, chosen, rejected, S, prompt_len, lora, grads, loss, aux,
+                                 want_host_loss=host_loss)
         finally:
             self._exit()
 
