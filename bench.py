@@ -55,8 +55,12 @@ def gpu_clock_mhz():
     return None
 
 
-def build_store(q, synth, cfg, threads, absmax):
-    store = q.Store(cfg, absmax=absmax)
+def build_store(q, synth, cfg, threads, absmax, disk_layers=0, disk_dir=None):
+    if disk_layers > 0:
+        path = os.path.join(disk_dir or os.environ.get("TMPDIR", "/tmp"), f"qls_store_{os.getpid()}.bin")
+        store = q.Store(cfg, absmax=absmax, ram_layers=cfg.L - disk_layers, disk_path=path)
+    else:
+        store = q.Store(cfg, absmax=absmax)
     per = max(1, threads // 4)
 
     def one(l):
@@ -152,6 +156,9 @@ def main():
     ap.add_argument("--pref", nargs="*", default=[], choices=["dpo", "simpo", "orpo", "kto"],
                     help="also time preference steps of these heads (2 x seq, shared 128-token prompt)")
     ap.add_argument("--threads", type=int, default=min(16, os.cpu_count() or 1))
+    ap.add_argument("--disk-layers", type=int, default=0,
+                    help="spill the last N layers of the store to a file (the disk tier)")
+    ap.add_argument("--disk-dir", default=None, help="directory of the disk-tier file (default $TMPDIR or /tmp)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="only copy a device buffer of this many MiB 3 times and exit: the known-size "
                          "reference that scales the FETCH_SIZE / WRITE_SIZE counters")
@@ -182,7 +189,7 @@ def main():
     B, S = args.batch, args.seq
     T = B * S
     t_setup = time.perf_counter()
-    store = build_store(q, synth, cfg, args.threads, args.absmax)
+    store = build_store(q, synth, cfg, args.threads, args.absmax, args.disk_layers, args.disk_dir)
     print(f"[bench] store built: {cfg.L} x {store.record_bytes} B in {time.perf_counter() - t_setup:.1f} s",
           file=sys.stderr, flush=True)
     emb = synth.embedding(cfg, threads=args.threads).cuda()
@@ -263,7 +270,7 @@ def main():
                                 f"per layer) in pinned host memory streamed through 2 device slots, bf16 embedding + "
                                 f"LM head 128256 x 4096 resident, LoRA r64 alpha16 on 7 linears"),
                    "global_batch": B, "seq_len": S, "parallelism": "single GPU", "mode": args.mode,
-                   "absmax": args.absmax, "optimizer": (None if opt is None else "AdamW lr 2e-5 on the LoRA vector")},
+                   "absmax": args.absmax, "disk_layers": args.disk_layers, "optimizer": (None if opt is None else "AdamW lr 2e-5 on the LoRA vector")},
         "roofline": {"bound": "mfma", "kernel": dom["name"],
                      "achieved": dom["tflops"],
                      "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
@@ -281,6 +288,10 @@ def main():
                 "copy_ms_per_step": round(st["copy_ms"] / steps, 3),
                 "copy_overlapped_by_layer_compute": round(st["overlap_ms"] / st["copy_ms"], 4) if st["copy_ms"] else None,
                 "layer_compute_ms_per_step": round(st["compute_ms"] / steps, 3)},
+        "disk": ({"layers_on_disk": args.disk_layers, "reads_per_step": st["disk_reads"] / steps,
+                  "read_GBps": round(st["disk_bytes"] / (st["disk_read_ms"] * 1e-3) / 1e9, 2)
+                  if st["disk_read_ms"] else None,
+                  "host_wait_ms_per_step": round(st["disk_wait_ms"] / steps, 3)} if args.disk_layers else None),
         "peak_hbm_GB": round(torch.cuda.max_memory_allocated() / 1e9, 3),
         "gpu_clock": clock[0],
         "loss": round(loss_v, 5),

@@ -56,7 +56,8 @@ enum {
   QLS_ENOPIN = -3,       /* pinned host allocation failed or exceeds the cap */
   QLS_EHIP = -4,         /* a HIP runtime call failed (message has hipGetErrorString) */
   QLS_ESTATE = -5,       /* object not ready (e.g. a store layer never set) */
-  QLS_EUNSUPPORTED = -6  /* shape outside what the kernels support */
+  QLS_EUNSUPPORTED = -6, /* shape outside what the kernels support */
+  QLS_EIO = -7           /* disk-tier file create / read / write failed */
 };
 
 enum { QLS_STREAMED = 0, QLS_RESIDENT = 1 };
@@ -151,6 +152,11 @@ typedef struct qls_stats {
   double dq_dx_big_ms, dq_dx_big_gflop;
   int64_t dq_dx_big_launches;
   double dq_fwd_reduce_ms, dq_dx_reduce_ms;
+  /* Disk tier (streamed sessions over a tiered store): records read from the
+   * file (read-aheads included), their bytes, the summed read time on the
+   * reader thread and the time the step's host thread waited for a record. */
+  int64_t disk_reads, disk_bytes;
+  double disk_read_ms, disk_wait_ms;
 } qls_stats;
 
 typedef struct qls_store qls_store;
@@ -270,8 +276,31 @@ int qls_store_set_layer_fp32(qls_store* st, int layer, const float* const h_w[QL
 int qls_store_set_layer_nf4(qls_store* st, int layer, const uint8_t* const h_codes[QLS_NMOD],
                             const float* const h_absmax[QLS_NMOD],
                             const uint16_t* h_norm_attn, const uint16_t* h_norm_mlp);
+/* Read-only pointers into one record.  For a disk-tier layer the record is
+ * first read into a store-owned host buffer: the pointers stay valid until
+ * the next view of a disk-tier layer or the store's destruction.  Errors:
+ * QLS_EINVAL, QLS_ESTATE (disk layer never set), QLS_EIO. */
 int qls_store_layer_view(const qls_store* st, int layer, qls_layer_view* out);
-void qls_store_destroy(qls_store* st);   /* NULL-safe */
+void qls_store_destroy(qls_store* st);   /* NULL-safe; removes a disk tier's file */
+
+/* Two-tier store ([P1] "How Soup's layer streaming actually works", item 2,
+ * and its FAQ on an SSD instead of enough RAM: records that do not fit in
+ * pinned host memory spill to an NVMe-backed file, which adds the storage
+ * read rate as a further bound).  Layers [0, ram_layers) are pinned host
+ * records as in qls_store_create_fmt; layers [ram_layers, n_layers) live in
+ * the file `path` (created or truncated, owned by the store, deleted by
+ * qls_store_destroy), one record per 4096-byte-aligned slot, written when the
+ * layer is set.  A streamed session reads a disk layer with O_DIRECT (when the
+ * file system allows it) into one of three pinned staging buffers, from a
+ * thread that reads the next disk layer of the sweep ahead of its request, and
+ * copies it to the device slot from there; a resident session reads every
+ * disk layer once at creation.  Errors: QLS_EINVAL (format, ram_layers
+ * outside [0, n_layers], no path with disk layers), QLS_ENOPIN, QLS_EIO. */
+enum { QLS_TIER_PINNED = 0, QLS_TIER_DISK = 1 };
+int qls_store_create_tiered(const qls_model_cfg* cfg, int absmax_format, int ram_layers,
+                            const char* path, qls_store** out);
+/* QLS_TIER_PINNED or QLS_TIER_DISK for one layer; QLS_EINVAL if out of range. */
+int qls_store_layer_tier(const qls_store* st, int layer);
 
 /* ---------------------------------------------------------------- session
  * Device bytes a session needs: the two slots (or the whole store when

@@ -18,7 +18,8 @@ if not os.path.exists(LIB_PATH):
                       "(hipcc --offload-arch=gfx950); there is no fallback path")
 _lib = C.CDLL(LIB_PATH)
 
-QLS_OK, QLS_EINVAL, QLS_ENOMEM, QLS_ENOPIN, QLS_EHIP, QLS_ESTATE, QLS_EUNSUPPORTED = 0, -1, -2, -3, -4, -5, -6
+QLS_OK, QLS_EINVAL, QLS_ENOMEM, QLS_ENOPIN, QLS_EHIP, QLS_ESTATE, QLS_EUNSUPPORTED, QLS_EIO = 0, -1, -2, -3, -4, -5, -6, -7
+QLS_TIER_PINNED, QLS_TIER_DISK = 0, 1
 QLS_STREAMED, QLS_RESIDENT = 0, 1
 QLS_ABSMAX_F32, QLS_ABSMAX_DQ8 = 0, 1
 QLS_PREF_DPO, QLS_PREF_SIMPO, QLS_PREF_ORPO, QLS_PREF_KTO = 0, 1, 2, 3
@@ -70,7 +71,9 @@ class Stats(C.Structure):
                 ("dq_dx_ms", C.c_double), ("dq_dx_gflop", C.c_double), ("dq_dx_launches", C.c_int64),
                 ("dq_fwd_big_ms", C.c_double), ("dq_fwd_big_gflop", C.c_double), ("dq_fwd_big_launches", C.c_int64),
                 ("dq_dx_big_ms", C.c_double), ("dq_dx_big_gflop", C.c_double), ("dq_dx_big_launches", C.c_int64),
-                ("dq_fwd_reduce_ms", C.c_double), ("dq_dx_reduce_ms", C.c_double)]
+                ("dq_fwd_reduce_ms", C.c_double), ("dq_dx_reduce_ms", C.c_double),
+                ("disk_reads", C.c_int64), ("disk_bytes", C.c_int64), ("disk_read_ms", C.c_double),
+                ("disk_wait_ms", C.c_double)]
 
     def as_dict(self):
         return {k: getattr(self, k) for k, _ in self._fields_}
@@ -98,6 +101,8 @@ _SIG = {
     "qls_lora_numel": (_I64, [C.POINTER(ModelCfg)]),
     "qls_store_create": (_I, [C.POINTER(ModelCfg), C.c_uint64, C.POINTER(_P)]),
     "qls_store_create_fmt": (_I, [C.POINTER(ModelCfg), _I, C.c_uint64, C.POINTER(_P)]),
+    "qls_store_create_tiered": (_I, [_P, _I, _I, C.c_char_p, _P]),
+    "qls_store_layer_tier": (_I, [_P, _I]),
     "qls_store_set_layer_fp32": (_I, [_P, _I, _P * NMOD, _P, _P, _I]),
     "qls_store_set_layer_nf4": (_I, [_P, _I, _P * NMOD, _P * NMOD, _P, _P]),
     "qls_store_layer_view": (_I, [_P, _I, C.POINTER(LayerView)]),
@@ -229,6 +234,16 @@ def qls_store_create(mc: ModelCfg, max_pinned_bytes: int = 0):
     h = _P()
     _check(_lib.qls_store_create(C.byref(mc), max_pinned_bytes, C.byref(h)))
     return h
+
+
+def qls_store_create_tiered(mc: ModelCfg, absmax_format: int, ram_layers: int, path: str):
+    h = _P()
+    _check(_lib.qls_store_create_tiered(C.byref(mc), absmax_format, ram_layers, path.encode(), C.byref(h)))
+    return h
+
+
+def qls_store_layer_tier(store, layer: int) -> int:
+    return _check(_lib.qls_store_layer_tier(store, layer))
 
 
 def qls_store_create_fmt(mc: ModelCfg, absmax_format: int, max_pinned_bytes: int = 0):

@@ -81,5 +81,10 @@ LoraLayout lora_layout(const Shape& sh);
 // Store accessors (store.cpp).
 const Shape& store_shape(const qls_store* st);
 const RecordLayout& store_layout(const qls_store* st);
+// Host record of a pinned layer (nullptr for a disk-tier layer).
 const uint8_t* store_record(const qls_store* st, int layer);
+// Layers [0, store_ram_layers) are pinned; the rest are read from store_disk.
+int store_ram_layers(const qls_store* st);
+class DiskFile;
+const DiskFile* store_disk(const qls_store* st);
 bool store_complete(const qls_store* st, int* missing);

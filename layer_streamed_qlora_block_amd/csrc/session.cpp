@@ -20,10 +20,12 @@
 #include <chrono>
 #include <cmath>
 #include <cstring>
+#include <memory>
 #include <thread>
 #include <vector>
 
 #include "attn.h"
+#include "disk.h"
 #include "gemm.h"
 #include "internal.h"
 #include "ops.h"
@@ -136,6 +138,8 @@ struct TimedK { hipEvent_t a, b, c; double gflop; bool big; };
 
 struct qls_session {
   const qls_store* st = nullptr;
+  int ram_layers = 0;                   // layers [ram_layers, L) come from the disk tier
+  std::unique_ptr<DiskReader> disk;
   Shape sh;
   RecordLayout lay;
   LoraLayout ll;
@@ -206,7 +210,11 @@ void sleep_cb(void* us) {
 }
 
 // ---------------------------------------------------------------- pool
-int prefetch(qls_session* S, int layer) {
+// Enqueue the copy of `layer` into slot layer & 1 on the copy stream, after
+// the slot's release.  A disk-tier layer is first read into a pinned staging
+// buffer (blocking this thread until the read is done); dir = the sweep's
+// direction, for the reader's read-ahead.
+int prefetch(qls_session* S, int layer, int dir) {
   if (S->run.mode == QLS_RESIDENT) return QLS_OK;
   const int s = layer & 1;
   const bool reuse = !(S->dbg & (QLS_DBG_NO_REUSE | QLS_DBG_POISON_ON_RELEASE));
@@ -214,11 +222,18 @@ int prefetch(qls_session* S, int layer) {
   QLS_HIP(hipStreamWaitEvent(S->ps, S->released[s], 0));
   if (S->dbg & QLS_DBG_COPY_DELAY)
     QLS_HIP(hipLaunchHostFunc(S->ps, sleep_cb, (void*)(intptr_t)S->delay_us));
+  const uint8_t* src = store_record(S->st, layer);
+  int buf = -1;
+  if (layer >= S->ram_layers) {
+    src = S->disk->take(layer, dir, &buf);
+    if (!src) return fail(QLS_EIO, S->disk->error());
+  }
   TimedEv te{};
   if (S->timing) { te.a = S->next_ev(); te.b = S->next_ev(); QLS_HIP(hipEventRecord(te.a, S->ps)); }
-  QLS_HIP(hipMemcpyAsync(S->at<uint8_t>(S->p.slots) + s * S->lay.bytes, store_record(S->st, layer),
-                         S->lay.bytes, hipMemcpyHostToDevice, S->ps));
+  QLS_HIP(hipMemcpyAsync(S->at<uint8_t>(S->p.slots) + s * S->lay.bytes, src, S->lay.bytes,
+                         hipMemcpyHostToDevice, S->ps));
   if (S->timing) { QLS_HIP(hipEventRecord(te.b, S->ps)); S->copy_ev.push_back(te); }
+  if (buf >= 0 && S->disk->after_copy(buf, S->ps)) return fail(QLS_EHIP, "hipEventRecord failed");
   QLS_HIP(hipEventRecord(S->copied[s], S->ps));
   S->slot_layer[s] = layer;
   S->slot_gen[s] += 1;
@@ -233,7 +248,7 @@ int acquire(qls_session* S, int layer, const uint8_t** rec, TimedEv* te) {
   } else {
     const int s = layer & 1;
     if (S->slot_layer[s] != layer) {
-      int rc = prefetch(S, layer);
+      int rc = prefetch(S, layer, 1);
       if (rc) return rc;
     }
     QLS_HIP(hipStreamWaitEvent(S->cs, S->copied[s], 0));
@@ -530,8 +545,8 @@ int begin_step(qls_session* S) {
     QLS_HIP(hipEventRecord(S->step_ev.back().a, S->cs));
   }
   QLS_HIP(hipMemsetAsync(S->at<int>(S->p.scal), 0, 64, S->cs));
-  int rc = prefetch(S, 0);
-  if (!rc && S->sh.c.n_layers > 1) rc = prefetch(S, 1);
+  int rc = prefetch(S, 0, 1);
+  if (!rc && S->sh.c.n_layers > 1) rc = prefetch(S, 1, 1);
   return rc;
 }
 
@@ -566,7 +581,7 @@ int forward_sweep(qls_session* S, int T, int B, int Sq, bool lora, bool ref) {
     if (rc) return rc;
     rc = release(S, l, &te);
     if (rc) return rc;
-    if (l + 2 < L && (rc = prefetch(S, l + 2))) return rc;
+    if (l + 2 < L && (rc = prefetch(S, l + 2, 1))) return rc;
   }
   return QLS_OK;
 }
@@ -584,7 +599,7 @@ int backward_sweep(qls_session* S, int T, int B, int Sq, float* grads) {
     if (rc) return rc;
     rc = release(S, l, &te);
     if (rc) return rc;
-    if (l - 2 >= 0 && (rc = prefetch(S, l - 2))) return rc;
+    if (l - 2 >= 0 && (rc = prefetch(S, l - 2, -1))) return rc;
   }
   return QLS_OK;
 }
@@ -675,12 +690,34 @@ int qls_session_create(const qls_store* st, const qls_run_cfg* run, void* d_ws, 
   fill_rope_table(sh, run->max_seq, &tab);
   hipError_t e = hipMemcpy(S->at<float>(S->p.rope), tab.data(), tab.size() * 4, hipMemcpyHostToDevice);
   if (e != hipSuccess) return cleanup(hip_fail(e, "rope table upload"));
+  S->ram_layers = store_ram_layers(st);
+  const DiskFile* df = store_disk(st);
+  if (run->mode == QLS_STREAMED && S->ram_layers < sh.c.n_layers) {
+    S->disk.reset(new (std::nothrow) DiskReader);
+    if (!S->disk || S->disk->init(df, S->ram_layers, sh.c.n_layers, 3, &why))
+      return cleanup(fail(QLS_ENOPIN, S->disk ? why : std::string("host allocation failed")));
+  }
   if (run->mode == QLS_RESIDENT) {
-    for (int l = 0; l < sh.c.n_layers; ++l) {
-      e = hipMemcpy(S->at<uint8_t>(S->p.slots) + (int64_t)l * S->lay.bytes, store_record(st, l), S->lay.bytes,
-                    hipMemcpyHostToDevice);
-      if (e != hipSuccess) return cleanup(hip_fail(e, "resident store upload"));
+    uint8_t* stage = nullptr;
+    if (S->ram_layers < sh.c.n_layers) {
+      e = hipHostMalloc(reinterpret_cast<void**>(&stage), (size_t)df->record_bytes(), hipHostMallocDefault);
+      if (e != hipSuccess || !stage) return cleanup(hip_fail(e, "disk staging buffer"));
     }
+    for (int l = 0; l < sh.c.n_layers && e == hipSuccess; ++l) {
+      const uint8_t* src = store_record(st, l);
+      if (!src) {
+        const int rd = df->read_any(l - S->ram_layers, stage);
+        if (rd) {
+          (void)hipHostFree(stage);
+          return cleanup(fail(QLS_EIO, std::string("disk tier read failed: ") + std::strerror(-rd)));
+        }
+        src = stage;
+      }
+      e = hipMemcpy(S->at<uint8_t>(S->p.slots) + (int64_t)l * S->lay.bytes, src, S->lay.bytes,
+                    hipMemcpyHostToDevice);
+    }
+    if (stage) (void)hipHostFree(stage);
+    if (e != hipSuccess) return cleanup(hip_fail(e, "resident store upload"));
   }
   *out = S;
   return QLS_OK;
@@ -804,7 +841,7 @@ int qls_layer_fwd_bwd(qls_session* S, int layer, const uint16_t* d_x, const uint
     S->step_ev.push_back({S->next_ev(), S->next_ev()});
     QLS_HIP(hipEventRecord(S->step_ev.back().a, S->cs));
   }
-  if ((rc = prefetch(S, layer))) return rc;
+  if ((rc = prefetch(S, layer, 1))) return rc;
   cast_lora(S, d_lora);
   const uint8_t* rec;
   TimedEv te{};
@@ -835,6 +872,13 @@ int qls_session_stats(qls_session* S, qls_stats* o) {
   o->layer_loads = S->loads;
   o->h2d_bytes = S->h2d;
   o->ws_bytes = S->p.total;
+  if (S->disk) {
+    const DiskReader::Stats d = S->disk->stats();
+    o->disk_reads = d.reads;
+    o->disk_bytes = d.bytes;
+    o->disk_read_ms = d.read_ms;
+    o->disk_wait_ms = d.wait_ms;
+  }
   if (S->timing && !S->step_ev.empty()) {
     hipEvent_t t0 = S->step_ev.front().a;
     auto rel = [&](hipEvent_t e) { float ms = 0; (void)hipEventElapsedTime(&ms, t0, e); return (double)ms; };
@@ -864,6 +908,7 @@ int qls_session_stats(qls_session* S, qls_stats* o) {
       if (k.big) { o->dq_dx_big_ms += ms; o->dq_dx_big_gflop += k.gflop; ++o->dq_dx_big_launches; }
     }
     o->dq_fwd_launches = (int64_t)S->kf_ev.size();
+
     o->dq_dx_launches = (int64_t)S->kd_ev.size();
   }
   return QLS_OK;
@@ -875,6 +920,7 @@ int qls_session_reset_stats(qls_session* S) {
   QLS_HIP(hipStreamSynchronize(S->ps));
   S->steps = S->loads = S->h2d = 0;
   S->clear_timing();
+  if (S->disk) S->disk->reset_stats();
   return QLS_OK;
 }
 

@@ -11,12 +11,16 @@
 #include <cstring>
 #include <thread>
 
+#include "disk.h"
 #include "internal.h"
 
 struct qls_store {
   Shape sh;
   RecordLayout lay;   // lay.fmt: QLS_ABSMAX_F32 or QLS_ABSMAX_DQ8
-  uint8_t* host = nullptr;          // n_layers * lay.bytes, hipHostMalloc
+  uint8_t* host = nullptr;          // ram_layers * lay.bytes, hipHostMalloc
+  int ram_layers = 0;               // layers [0, ram_layers) pinned, the rest in `disk`
+  DiskFile disk;
+  mutable std::vector<uint8_t> view; // last disk record handed out by a layer view
   std::vector<char> ready;
 };
 
@@ -222,6 +226,7 @@ int qls_store_create_fmt(const qls_model_cfg* cfg, int absmax_format, uint64_t m
     delete st;
     return fail(QLS_ENOPIN, std::string("hipHostMalloc of the store failed: ") + hipGetErrorString(e));
   }
+  st->ram_layers = cfg->n_layers;
   st->ready.assign(cfg->n_layers, 0);
   *out = st;
   return QLS_OK;
@@ -229,6 +234,61 @@ int qls_store_create_fmt(const qls_model_cfg* cfg, int absmax_format, uint64_t m
 
 int qls_store_create(const qls_model_cfg* cfg, uint64_t max_pinned_bytes, qls_store** out) {
   return qls_store_create_fmt(cfg, QLS_ABSMAX_F32, max_pinned_bytes, out);
+}
+
+int qls_store_create_tiered(const qls_model_cfg* cfg, int absmax_format, int ram_layers, const char* path,
+                            qls_store** out) {
+  if (!out) return fail(QLS_EINVAL, "out is NULL");
+  *out = nullptr;
+  Shape sh;
+  std::string why;
+  if (!make_shape(cfg, &sh, &why)) return fail(QLS_EINVAL, why);
+  if (absmax_format != QLS_ABSMAX_F32 && absmax_format != QLS_ABSMAX_DQ8)
+    return fail(QLS_EINVAL, "absmax_format must be QLS_ABSMAX_F32 or QLS_ABSMAX_DQ8");
+  if (ram_layers < 0 || ram_layers > cfg->n_layers) return fail(QLS_EINVAL, "ram_layers must be in [0, n_layers]");
+  if (ram_layers < cfg->n_layers && (!path || !*path)) return fail(QLS_EINVAL, "disk layers need a file path");
+  auto* st = new (std::nothrow) qls_store;
+  if (!st) return fail(QLS_ENOMEM, "host allocation failed");
+  st->sh = sh;
+  st->lay = record_layout(sh, absmax_format);
+  st->ram_layers = ram_layers;
+  if (ram_layers > 0) {
+    hipError_t e = hipHostMalloc(reinterpret_cast<void**>(&st->host), (size_t)st->lay.bytes * ram_layers,
+                                 hipHostMallocDefault);
+    if (e != hipSuccess || !st->host) {
+      delete st;
+      return fail(QLS_ENOPIN, std::string("hipHostMalloc of the store failed: ") + hipGetErrorString(e));
+    }
+  }
+  if (ram_layers < cfg->n_layers && st->disk.open(path, st->lay.bytes, cfg->n_layers - ram_layers, &why)) {
+    qls_store_destroy(st);
+    return fail(QLS_EIO, why);
+  }
+  st->ready.assign(cfg->n_layers, 0);
+  *out = st;
+  return QLS_OK;
+}
+
+int qls_store_layer_tier(const qls_store* st, int layer) {
+  if (!st) return fail(QLS_EINVAL, "NULL argument");
+  if (layer < 0 || layer >= st->sh.c.n_layers) return fail(QLS_EINVAL, "layer out of range");
+  return layer < st->ram_layers ? QLS_TIER_PINNED : QLS_TIER_DISK;
+}
+
+// Where set_layer_* builds layer's record: in place for a pinned layer, in
+// the caller's buffer (then written to the file) for a disk layer, so layers
+// can be set from several threads at once.
+static uint8_t* record_dst(qls_store* st, int layer, std::vector<uint8_t>* local) {
+  if (layer < st->ram_layers) return st->host + (int64_t)layer * st->lay.bytes;
+  local->assign((size_t)st->lay.bytes, 0);
+  return local->data();
+}
+
+static int record_commit(qls_store* st, int layer, const uint8_t* rec) {
+  if (layer < st->ram_layers) return QLS_OK;
+  const int rc = st->disk.write(layer - st->ram_layers, rec);
+  if (rc) return fail(QLS_EIO, std::string("disk tier write failed: ") + std::strerror(-rc));
+  return QLS_OK;
 }
 
 // Write module m's absmax into the record in the store's format.
@@ -241,8 +301,7 @@ static void put_absmax(qls_store* st, uint8_t* rec, int m, const float* absmax) 
     std::memcpy(rec + st->lay.absmax_off[m], absmax, nb * 4);
 }
 
-static int set_norms(qls_store* st, int layer, const uint16_t* na, const uint16_t* nm) {
-  uint8_t* rec = st->host + (int64_t)layer * st->lay.bytes;
+static int set_norms(qls_store* st, uint8_t* rec, const uint16_t* na, const uint16_t* nm) {
   std::memcpy(rec + st->lay.norm_attn_off, na, 2 * (size_t)st->sh.c.hidden);
   std::memcpy(rec + st->lay.norm_mlp_off, nm, 2 * (size_t)st->sh.c.hidden);
   return QLS_OK;
@@ -254,7 +313,8 @@ int qls_store_set_layer_fp32(qls_store* st, int layer, const float* const w[QLS_
   if (layer < 0 || layer >= st->sh.c.n_layers) return fail(QLS_EINVAL, "layer out of range");
   for (int m = 0; m < QLS_NMOD; ++m)
     if (!w[m]) return fail(QLS_EINVAL, "NULL weight");
-  uint8_t* rec = st->host + (int64_t)layer * st->lay.bytes;
+  std::vector<uint8_t> local;
+  uint8_t* rec = record_dst(st, layer, &local);
   std::vector<float> amax;
   for (int m = 0; m < QLS_NMOD; ++m) {
     if (st->lay.fmt == QLS_ABSMAX_F32) {
@@ -266,7 +326,9 @@ int qls_store_set_layer_fp32(qls_store* st, int layer, const float* const w[QLS_
       put_absmax(st, rec, m, amax.data());
     }
   }
-  set_norms(st, layer, na, nm);
+  set_norms(st, rec, na, nm);
+  const int rc = record_commit(st, layer, rec);
+  if (rc) return rc;
   st->ready[layer] = 1;
   return QLS_OK;
 }
@@ -276,13 +338,17 @@ int qls_store_set_layer_nf4(qls_store* st, int layer, const uint8_t* const codes
                             const uint16_t* nm) {
   if (!st || !codes || !absmax || !na || !nm) return fail(QLS_EINVAL, "NULL argument");
   if (layer < 0 || layer >= st->sh.c.n_layers) return fail(QLS_EINVAL, "layer out of range");
-  uint8_t* rec = st->host + (int64_t)layer * st->lay.bytes;
-  for (int m = 0; m < QLS_NMOD; ++m) {
+  for (int m = 0; m < QLS_NMOD; ++m)
     if (!codes[m] || !absmax[m]) return fail(QLS_EINVAL, "NULL module buffer");
+  std::vector<uint8_t> local;
+  uint8_t* rec = record_dst(st, layer, &local);
+  for (int m = 0; m < QLS_NMOD; ++m) {
     std::memcpy(rec + st->lay.code_off[m], codes[m], st->sh.numel[m] / 2);
     put_absmax(st, rec, m, absmax[m]);
   }
-  set_norms(st, layer, na, nm);
+  set_norms(st, rec, na, nm);
+  const int rc = record_commit(st, layer, rec);
+  if (rc) return rc;
   st->ready[layer] = 1;
   return QLS_OK;
 }
@@ -290,7 +356,16 @@ int qls_store_set_layer_nf4(qls_store* st, int layer, const uint8_t* const codes
 int qls_store_layer_view(const qls_store* st, int layer, qls_layer_view* out) {
   if (!st || !out) return fail(QLS_EINVAL, "NULL argument");
   if (layer < 0 || layer >= st->sh.c.n_layers) return fail(QLS_EINVAL, "layer out of range");
-  const uint8_t* rec = st->host + (int64_t)layer * st->lay.bytes;
+  const uint8_t* rec;
+  if (layer < st->ram_layers) {
+    rec = st->host + (int64_t)layer * st->lay.bytes;
+  } else {
+    if (!st->ready[layer]) return fail(QLS_ESTATE, "layer was never set");
+    st->view.resize((size_t)st->lay.bytes);
+    const int rc = st->disk.read_any(layer - st->ram_layers, st->view.data());
+    if (rc) return fail(QLS_EIO, std::string("disk tier read failed: ") + std::strerror(-rc));
+    rec = st->view.data();
+  }
   const bool dq = st->lay.fmt == QLS_ABSMAX_DQ8;
   out->absmax_format = st->lay.fmt;
   for (int m = 0; m < QLS_NMOD; ++m) {
@@ -318,8 +393,10 @@ void qls_store_destroy(qls_store* st) {
 const Shape& store_shape(const qls_store* st) { return st->sh; }
 const RecordLayout& store_layout(const qls_store* st) { return st->lay; }
 const uint8_t* store_record(const qls_store* st, int layer) {
-  return st->host + (int64_t)layer * st->lay.bytes;
+  return layer < st->ram_layers ? st->host + (int64_t)layer * st->lay.bytes : nullptr;
 }
+int store_ram_layers(const qls_store* st) { return st->ram_layers; }
+const DiskFile* store_disk(const qls_store* st) { return st->disk.is_open() ? &st->disk : nullptr; }
 bool store_complete(const qls_store* st, int* missing) {
   for (int l = 0; l < (int)st->ready.size(); ++l)
     if (!st->ready[l]) { if (missing) *missing = l; return false; }

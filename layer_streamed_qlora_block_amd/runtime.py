@@ -14,7 +14,7 @@ import torch
 from . import (QLS_ABSMAX_DQ8, QLS_ABSMAX_F32, QLS_RESIDENT, QLS_STREAMED, RunCfg, model_cfg, qls_debug_set,
                pref_cfg, qls_adamw_step, qls_dpo_step, qls_pref_step, qls_layer_fwd_bwd, qls_layer_record_bytes_fmt, qls_logprobs, qls_lora_numel,
                qls_session_checkpoints, qls_session_create, qls_session_destroy, qls_session_reset_stats,
-               qls_session_stats, qls_sft_step, qls_store_create_fmt, qls_store_destroy, qls_store_layer_view,
+               qls_session_stats, qls_sft_step, qls_store_create_fmt, qls_store_create_tiered, qls_store_destroy, qls_store_layer_view,
                qls_store_set_layer_fp32, qls_store_set_layer_nf4, qls_workspace_bytes)
 
 
@@ -23,10 +23,12 @@ def _np_bf16(t: torch.Tensor) -> np.ndarray:
 
 
 class Store:
-    """Pinned NF4 layer store.  absmax: "f32" (float32 per 64-block) or "dq8"
-    (8-bit codes + one float32 scale per 256 blocks)."""
+    """NF4 layer store.  absmax: "f32" (float32 per 64-block) or "dq8" (8-bit
+    codes + one float32 scale per 256 blocks).  With disk_path, layers
+    [0, ram_layers) are pinned host records and the rest spill to that file
+    (the disk tier); otherwise every layer is pinned."""
 
-    def __init__(self, cfg, max_pinned_bytes: int = 0, absmax: str = "f32"):
+    def __init__(self, cfg, max_pinned_bytes: int = 0, absmax: str = "f32", ram_layers=None, disk_path=None):
         if absmax not in ("f32", "dq8"):
             raise ValueError("absmax must be 'f32' or 'dq8'")
         self.cfg = cfg
@@ -35,7 +37,12 @@ class Store:
         fmt = QLS_ABSMAX_DQ8 if absmax == "dq8" else QLS_ABSMAX_F32
         self.record_bytes = qls_layer_record_bytes_fmt(self.mc, fmt)
         self.lora_numel = qls_lora_numel(self.mc)
-        self.h = qls_store_create_fmt(self.mc, fmt, max_pinned_bytes)
+        if disk_path is not None:
+            self.ram_layers = cfg.L if ram_layers is None else int(ram_layers)
+            self.h = qls_store_create_tiered(self.mc, fmt, self.ram_layers, str(disk_path))
+        else:
+            self.ram_layers = cfg.L
+            self.h = qls_store_create_fmt(self.mc, fmt, max_pinned_bytes)
 
     def set_layer_fp32(self, layer, weights, norm_attn, norm_mlp, n_threads: int = 0):
         ws = [np.ascontiguousarray(w, dtype=np.float32) for w in weights]
