@@ -71,7 +71,8 @@ enum { QLS_Q = 0, QLS_K, QLS_V, QLS_O, QLS_GATE, QLS_UP, QLS_DOWN, QLS_NMOD };
 /* Llama-style decoder shape plus LoRA hyper-parameters.
  * Linears as (out x in): q (H*hd x d), k and v (KV*hd x d), o (d x H*hd),
  * gate and up (I x d), down (d x I).  LoRA scale s = alpha / r.
- * Supported: head_dim in {64, 128}; n_heads % n_kv_heads == 0; hidden,
+ * Supported: head_dim in {64, 128}; n_heads % n_kv_heads == 0 with at most 8
+ * query heads per kv head; hidden,
  * intermediate and every linear's in/out multiples of 16; lora_r a multiple
  * of 8 in [8, 128]. */
 typedef struct qls_model_cfg {

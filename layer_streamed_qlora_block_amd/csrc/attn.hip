@@ -1,17 +1,24 @@
 // Causal grouped-query attention for gfx950 with v_mfma_f32_16x16x32_bf16.
 //
-// Forward: one workgroup per (64 query rows, query head, sequence); each of
-// the 4 waves owns 16 query rows and walks the key blocks up to the diagonal
-// with an online softmax (running max / sum in fp32).  Scores are formed
-// transposed, S^T = K Q^T, so a lane's accumulator column is its query row:
-// the softmax statistics stay per lane and the probabilities feed the P V
-// product directly as the B operand (the contraction slots of a lane are the
-// keys it already holds).  P is rounded to bf16 for the product; the final
+// Operand tiles (64 rows x head_dim bf16) go from global memory straight into
+// LDS with buffer_load ... lds, double-buffered, in unpadded rows whose
+// 16-byte chunks are XOR-swizzled by row.  Every product reads its operands
+// from row-major tiles: 16-byte fragments where the contraction runs along a
+// row, ds_read_b64_tr_b16 (the transposing LDS read of gfx950) where it runs
+// down a column, so no tile is ever staged transposed.
+//
+// Forward: one workgroup per (32 query rows, kv head, sequence); wave w is the
+// w-th query head of the kv head, so each K / V block is staged once for the
+// heads that share it.  Scores are formed transposed, S^T = K Q^T, so a
+// lane's accumulator column is its query row: the softmax statistics stay per
+// lane (online max / sum in fp32) and the probabilities feed the P V product
+// directly as the B operand.  P is rounded to bf16 for the product; the final
 // division by the fp32 row sum follows it.  The log-sum-exp per row is saved.
 //
 // Backward (no atomics, fixed summation order):
-//   dq kernel  -- per (64 query rows, head): recompute P from the saved LSE,
-//                 dP^T = V dO^T, dS = P (dP - D), dQ = dS K / sqrt(hd).
+//   dq kernel  -- per (32 query rows, kv head) as the forward: recompute P
+//                 from the saved LSE, dP^T = V dO^T, dS = P (dP - D),
+//                 dQ = dS K / sqrt(hd).
 //   dkv kernel -- per (64 keys, query head): loops over the query blocks on
 //                 or below the diagonal, dV_h += P^T dO, dK_h += dS^T Q /
 //                 sqrt(hd), one float partial per query head; the sum over the
@@ -28,163 +35,203 @@ constexpr int BQ = 64;                 // query rows / keys per block
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
-// rows [r0, r0+64) x HD from base[row * ld + j] into s[64][HD + 8]; rows >= S read 0.
-template <int HD>
-QLS_DEV void stage_rows(uint16_t* s, const uint16_t* base, int64_t ld, int r0, int S) {
-  constexpr int CH = HD / 8;
-  for (int c = threadIdx.x; c < BQ * CH; c += NT) {
-    const int row = c / CH, c8 = c % CH;
-    u32x4 v = {0, 0, 0, 0};
-    if (r0 + row < S) v = *reinterpret_cast<const u32x4*>(base + (int64_t)(r0 + row) * ld + 8 * c8);
-    *reinterpret_cast<u32x4*>(s + row * (HD + 8) + 8 * c8) = v;
-  }
-}
-
-// transposed: s[j][row] (pitch 72) = element (row, j); each thread moves
-// 8 rows x R columns and transposes them in registers.  Column group jg and
-// row group kg are interleaved so that each 8 / 16 consecutive lanes write 16
-// distinct bank quads (a plain jg = t % 32 mapping puts four of them on one).
-template <int HD>
-QLS_DEV void stage_cols(uint16_t* s, const uint16_t* base, int64_t ld, int r0, int S) {
-  constexpr int R = HD / 32;
-  static_assert(HD / R == 32, "32 column groups");
-  const int t = threadIdx.x;
-  const int jg = ((t >> 2) & 3) | (((t >> 4) & 7) << 2);   // 0..31
-  const int kg = (t & 3) | ((t >> 7) << 2);                // 0..7
-  uint32_t w[8][R / 2];
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int row = r0 + 8 * kg + i;
-    if (row < S) {
-      const uint16_t* src = base + (int64_t)row * ld + R * jg;
-      if constexpr (R == 4) {
-        const u32x2 x = *reinterpret_cast<const u32x2*>(src);
-        w[i][0] = x.x;
-        w[i][1] = x.y;
-      } else {
-        w[i][0] = *reinterpret_cast<const uint32_t*>(src);
-      }
-    } else {
-#pragma unroll
-      for (int c = 0; c < R / 2; ++c) w[i][c] = 0;
-    }
-  }
-#pragma unroll
-  for (int c = 0; c < R; ++c) {
-    const int sh = 16 * (c & 1);
-    u32x4 d;
-#pragma unroll
-    for (int q = 0; q < 4; ++q)
-      d[q] = ((w[2 * q][c >> 1] >> sh) & 0xFFFFu) | (((w[2 * q + 1][c >> 1] >> sh) & 0xFFFFu) << 16);
-    *reinterpret_cast<u32x4*>(s + (R * jg + c) * (BQ + 8) + 8 * kg) = d;
-  }
-}
-
-// 8 bf16 contraction slots {base+4g..+3, base+16+4g..+3} of row `row` of a
-// transposed tile (pitch 72): matches the key/query order of a 16x16 C block pair.
-QLS_DEV u32x4 read_pair(const uint16_t* s, int row, int base, int g4) {
-  const u32x2 a = *reinterpret_cast<const u32x2*>(s + row * (BQ + 8) + base + 4 * g4);
-  const u32x2 b = *reinterpret_cast<const u32x2*>(s + row * (BQ + 8) + base + 16 + 4 * g4);
-  return u32x4{a.x, a.y, b.x, b.y};
-}
-
 QLS_DEV u32x4 pack8(const f32x4& a, const f32x4& b) {
   return u32x4{pack2_bf16(a[0], a[1]), pack2_bf16(a[2], a[3]), pack2_bf16(b[0], b[1]),
                pack2_bf16(b[2], b[3])};
 }
 
+// ---- Unpadded swizzled tiles, filled by LDS-DMA.
+// A tile is 64 rows x HD bf16 with rows of HD*2 bytes; the 16-byte chunk c of
+// row r sits at chunk c ^ tswz(r).  The key makes the 16-byte fragment reads
+// of 16 consecutive rows and the 8-byte transpose reads of 8 consecutive rows
+// (two chunks each) land on distinct banks for HD = 128.
 template <int HD>
-__global__ void __launch_bounds__(NT) attn_fwd_k(AttnArgs a) {
-  __shared__ __attribute__((aligned(16))) uint16_t sK[BQ * (HD + 8)];
-  __shared__ __attribute__((aligned(16))) uint16_t sVt[HD * (BQ + 8)];
-  const int nqb = (a.S + BQ - 1) / BQ;
+QLS_DEV int tswz(int r) { return ((2 * (r & 7)) | ((r >> 3) & 1)) & (HD / 8 - 1); }
+template <int HD>
+QLS_DEV int tpos(int r, int col) { return r * HD + 8 * ((col >> 3) ^ tswz<HD>(r)) + (col & 7); }
+
+// Rows [r0, r0 + 64) of a [S x ld] operand (columns [0, HD) at base) into a
+// tile: one 16-byte DMA per lane, 1 KB per instruction, the instructions of
+// the tile spread over the workgroup's nw waves.  Rows at or past S read 0
+// (the resource ends at row S).
+template <int HD>
+QLS_DEV void dma_tile(uint16_t* tile, const uint16_t* base, int64_t ld, int r0, int S, int wave, int nw, int lane) {
+  constexpr int CH = HD / 8, RPI = 64 / CH, NI = 64 / RPI;   // chunks per row, rows and instructions per tile
+  const int64_t rows = S - r0 > 0 ? S - r0 : 0;
+  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(base + (int64_t)r0 * ld), (short)0,
+      (int)(rows * ld * 2 > 0x7fffffffLL ? 0x7fffffffLL : rows * ld * 2), 0x00020000);
+  for (int i = wave; i < NI; i += nw) {
+    const int r = RPI * i + lane / CH;
+    const int c = (lane % CH) ^ tswz<HD>(r);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)(tile + i * 512), 16,
+                                             (uint32_t)((r * ld + 8 * c) * 2), 0, 0, 0);
+  }
+}
+
+// 16-byte MFMA fragment: row r, columns [col, col + 8).
+template <int HD>
+QLS_DEV u32x4 frag(const uint16_t* tile, int r, int col) {
+  return *reinterpret_cast<const u32x4*>(tile + tpos<HD>(r, col));
+}
+
+// Transposed fragment from a row-major tile with ds_read_b64_tr_b16: within
+// each 16-lane group, lane j receives element i from the lane 4i + j/4 of
+// its group, element j % 4 of that lane's 8-byte read.  A lane of group g4
+// reading row kb + c16/4, columns col0 + 4 (c16 % 4) therefore returns
+// tile[kb + i][col0 + c16], i = 0..3.  Two reads give the 8 contraction
+// slots {k0 + 4 g4 + 0..3, k0 + 16 + 4 g4 + 0..3} of column col0 + c16.
+template <int HD>
+QLS_DEV u32x4 frag_t(const uint16_t* tile, int k0, int col0, int g4, int c16) {
+  typedef short v4s __attribute__((ext_vector_type(4)));
+  const int r = k0 + 4 * g4 + (c16 >> 2), col = col0 + 4 * (c16 & 3);
+  const v4s a = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) v4s*)(tile + tpos<HD>(r, col)));
+  const v4s b = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) v4s*)(tile + tpos<HD>(r + 16, col)));
+  const u32x2 x = __builtin_bit_cast(u32x2, a), y = __builtin_bit_cast(u32x2, b);
+  return u32x4{x.x, x.y, y.x, y.y};
+}
+
+QLS_DEV void wait_dma() {
+  __builtin_amdgcn_s_waitcnt(0 | (7 << 4) | (0 << 8) | (0 << 14));   // vmcnt(0) lgkmcnt(0)
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// Forward, one workgroup per (32 query rows, kv head, sequence): wave w is
+// query head kv * G + w (the G heads that share the kv head), so each K / V
+// block is staged once for all of them.  Key blocks of 64 are double-buffered
+// in LDS by DMA; a wave's 32 rows are two 16-row groups that share every K
+// and V fragment it reads.
+template <int HD>
+__global__ void __launch_bounds__(512) attn_fwd_k(AttnArgs a) {
+  __shared__ __attribute__((aligned(16))) uint16_t sK0[64 * HD];
+  __shared__ __attribute__((aligned(16))) uint16_t sK1[64 * HD];
+  __shared__ __attribute__((aligned(16))) uint16_t sV0[64 * HD];
+  __shared__ __attribute__((aligned(16))) uint16_t sV1[64 * HD];
+  const int G = a.H / a.KV;
+  const int nqb = (a.S + 31) / 32;
   const int qb = nqb - 1 - (int)blockIdx.x;       // long rows first
-  const int h = blockIdx.y, b = blockIdx.z;
-  const int g = h / (a.H / a.KV);
+  const int g = blockIdx.y, b = blockIdx.z;
   const int t = threadIdx.x, lane = t & 63, w = t >> 6, g4 = lane >> 4, c16 = lane & 15;
-  const int q0 = qb * BQ;
-  const int myq = q0 + 16 * w + c16;
+  const int h = g * G + w;
+  const int q0 = qb * 32;
   const int64_t tb = (int64_t)b * a.S;
   const uint16_t* Q = a.qkv + tb * a.ld + a.q_off + (int64_t)h * HD;
   const uint16_t* K = a.qkv + tb * a.ld + a.k_off + (int64_t)g * HD;
   const uint16_t* V = a.qkv + tb * a.ld + a.v_off + (int64_t)g * HD;
+  const int nkb = min((q0 + 31) / 64 + 1, (a.S + 63) / 64);
 
-  u32x4 qf[HD / 32];
+  dma_tile<HD>(sK0, K, a.ld, 0, a.S, w, G, lane);
+  dma_tile<HD>(sV0, V, a.ld, 0, a.S, w, G, lane);
+
+  int myq[2];
+  u32x4 qf[2][HD / 32];
 #pragma unroll
-  for (int s = 0; s < HD / 32; ++s)
-    qf[s] = myq < a.S ? *reinterpret_cast<const u32x4*>(Q + (int64_t)myq * a.ld + 32 * s + 8 * g4)
-                      : u32x4{0, 0, 0, 0};
-  f32x4 o[HD / 16];
+  for (int qg = 0; qg < 2; ++qg) {
+    myq[qg] = q0 + 16 * qg + c16;
 #pragma unroll
-  for (int i = 0; i < HD / 16; ++i) o[i] = f32x4{0, 0, 0, 0};
-  float m_run = -INFINITY, l_run = 0.f;
+    for (int s = 0; s < HD / 32; ++s)
+      qf[qg][s] = myq[qg] < a.S ? *reinterpret_cast<const u32x4*>(Q + (int64_t)myq[qg] * a.ld + 32 * s + 8 * g4)
+                                : u32x4{0, 0, 0, 0};
+  }
+  f32x4 o[2][HD / 16];
+#pragma unroll
+  for (int qg = 0; qg < 2; ++qg)
+#pragma unroll
+    for (int i = 0; i < HD / 16; ++i) o[qg][i] = f32x4{0, 0, 0, 0};
+  float m_run[2] = {-INFINITY, -INFINITY}, l_run[2] = {0.f, 0.f};
   const float c = a.scale * kLog2e;
 
-  for (int kb = 0; kb <= qb; ++kb) {
-    const int k0 = kb * BQ;
-    stage_rows<HD>(sK, K, a.ld, k0, a.S);
-    stage_cols<HD>(sVt, V, a.ld, k0, a.S);
-    __syncthreads();
-    f32x4 sc[4];
+  auto block = [&](const uint16_t* sK, const uint16_t* sV, int k0) {
+    f32x4 sc[2][4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      sc[j] = f32x4{0, 0, 0, 0};
+      sc[0][j] = f32x4{0, 0, 0, 0};
+      sc[1][j] = f32x4{0, 0, 0, 0};
 #pragma unroll
       for (int s = 0; s < HD / 32; ++s) {
-        const u32x4 ka = *reinterpret_cast<const u32x4*>(sK + (16 * j + c16) * (HD + 8) + 32 * s + 8 * g4);
-        sc[j] = mfma16(ka, qf[s], sc[j]);
+        const u32x4 ka = frag<HD>(sK, 16 * j + c16, 32 * s + 8 * g4);
+        sc[0][j] = mfma16(ka, qf[0][s], sc[0][j]);
+        sc[1][j] = mfma16(ka, qf[1][s], sc[1][j]);
       }
     }
-    float mloc = -INFINITY;
+    u32x4 pf[2][2];
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int qg = 0; qg < 2; ++qg) {
+      float mloc = -INFINITY;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int key = k0 + 16 * j + 4 * g4 + i;
-        const float x = (key <= myq && key < a.S) ? sc[j][i] * c : -INFINITY;
-        sc[j][i] = x;
-        mloc = fmaxf(mloc, x);
-      }
-    mloc = fmaxf(mloc, __shfl_xor(mloc, 16, 64));
-    mloc = fmaxf(mloc, __shfl_xor(mloc, 32, 64));
-    const float m_new = fmaxf(m_run, mloc);
-    const float m_use = m_new == -INFINITY ? 0.f : m_new;
-    const float alpha = exp2f(m_run - m_use);
-    float ls = 0.f;
+      for (int j = 0; j < 4; ++j)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+        for (int i = 0; i < 4; ++i) {
+          const int key = k0 + 16 * j + 4 * g4 + i;
+          const float x = (key <= myq[qg] && key < a.S) ? sc[qg][j][i] * c : -INFINITY;
+          sc[qg][j][i] = x;
+          mloc = fmaxf(mloc, x);
+        }
+      mloc = fmaxf(mloc, __shfl_xor(mloc, 16, 64));
+      mloc = fmaxf(mloc, __shfl_xor(mloc, 32, 64));
+      const float m_new = fmaxf(m_run[qg], mloc);
+      const float m_use = m_new == -INFINITY ? 0.f : m_new;
+      const float alpha = exp2f(m_run[qg] - m_use);
+      float ls = 0.f;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float p = exp2f(sc[j][i] - m_use);
-        sc[j][i] = p;
-        ls += p;
-      }
-    l_run = l_run * alpha + ls;
-    m_run = m_new;
+      for (int j = 0; j < 4; ++j)
 #pragma unroll
-    for (int i = 0; i < HD / 16; ++i) o[i] *= alpha;
+        for (int i = 0; i < 4; ++i) {
+          const float p = exp2f(sc[qg][j][i] - m_use);
+          sc[qg][j][i] = p;
+          ls += p;
+        }
+      l_run[qg] = l_run[qg] * alpha + ls;
+      m_run[qg] = m_new;
 #pragma unroll
-    for (int tt = 0; tt < 2; ++tt) {
-      const u32x4 pf = pack8(sc[2 * tt], sc[2 * tt + 1]);
+      for (int i = 0; i < HD / 16; ++i) o[qg][i] *= alpha;
+      pf[qg][0] = pack8(sc[qg][0], sc[qg][1]);
+      pf[qg][1] = pack8(sc[qg][2], sc[qg][3]);
+    }
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
       for (int hb = 0; hb < HD / 16; ++hb) {
-        const u32x4 va = read_pair(sVt, 16 * hb + c16, 32 * tt, g4);
-        o[hb] = mfma16(va, pf, o[hb]);
+        const u32x4 va = frag_t<HD>(sV, 32 * tt, 16 * hb, g4, c16);
+        o[0][hb] = mfma16(va, pf[0][tt], o[0][hb]);
+        o[1][hb] = mfma16(va, pf[1][tt], o[1][hb]);
       }
+  };
+
+  for (int kb = 0; kb < nkb; kb += 2) {
+    wait_dma();                                       // block kb in stage 0; stage 1 free
+    if (kb + 1 < nkb) {
+      dma_tile<HD>(sK1, K, a.ld, 64 * (kb + 1), a.S, w, G, lane);
+      dma_tile<HD>(sV1, V, a.ld, 64 * (kb + 1), a.S, w, G, lane);
     }
-    __syncthreads();
+    block(sK0, sV0, 64 * kb);
+    if (kb + 1 >= nkb) break;
+    wait_dma();                                       // block kb+1 in stage 1; stage 0 free
+    if (kb + 2 < nkb) {
+      dma_tile<HD>(sK0, K, a.ld, 64 * (kb + 2), a.S, w, G, lane);
+      dma_tile<HD>(sV0, V, a.ld, 64 * (kb + 2), a.S, w, G, lane);
+    }
+    block(sK1, sV1, 64 * (kb + 1));
   }
-  float lt = l_run + __shfl_xor(l_run, 16, 64);
-  lt += __shfl_xor(lt, 32, 64);
-  if (myq < a.S) {
-    const float inv = 1.f / lt;
-    uint16_t* O = a.out + (tb + myq) * a.ldo + (int64_t)h * HD;
 #pragma unroll
-    for (int hb = 0; hb < HD / 16; ++hb) {
-      const u32x2 v = {pack2_bf16(o[hb][0] * inv, o[hb][1] * inv), pack2_bf16(o[hb][2] * inv, o[hb][3] * inv)};
-      *reinterpret_cast<u32x2*>(O + 16 * hb + 4 * g4) = v;
+  for (int qg = 0; qg < 2; ++qg) {
+    float lt = l_run[qg] + __shfl_xor(l_run[qg], 16, 64);
+    lt += __shfl_xor(lt, 32, 64);
+    if (myq[qg] < a.S) {
+      const float inv = 1.f / lt;
+      uint16_t* O = a.out + (tb + myq[qg]) * a.ldo + (int64_t)h * HD;
+#pragma unroll
+      for (int hb = 0; hb < HD / 16; ++hb) {
+        const u32x2 v = {pack2_bf16(o[qg][hb][0] * inv, o[qg][hb][1] * inv),
+                         pack2_bf16(o[qg][hb][2] * inv, o[qg][hb][3] * inv)};
+        *reinterpret_cast<u32x2*>(O + 16 * hb + 4 * g4) = v;
+      }
+      if (g4 == 0) a.lse[((int64_t)b * a.H + h) * a.S + myq[qg]] = m_run[qg] * kLn2 + logf(lt);
     }
-    if (g4 == 0) a.lse[((int64_t)b * a.H + h) * a.S + myq] = m_run * kLn2 + logf(lt);
   }
 }
 
@@ -206,92 +253,139 @@ __global__ void attn_pre_k(const uint16_t* __restrict__ dO, const uint16_t* __re
   }
 }
 
+// dQ, one workgroup per (32 query rows, kv head, sequence), wave w = query head
+// kv * G + w; K and V blocks of 64 keys double-buffered by DMA and shared by
+// the G heads.  Per block: S^T = K Q^T and dP^T = V dO^T from row fragments,
+// P from the saved LSE, dS = P (dP - D), dQ += dS K with K read transposed.
 template <int HD>
-__global__ void __launch_bounds__(NT) attn_dq_k(AttnBwdArgs a) {
-  __shared__ __attribute__((aligned(16))) uint16_t sK[BQ * (HD + 8)];
-  __shared__ __attribute__((aligned(16))) uint16_t sV[BQ * (HD + 8)];
-  __shared__ __attribute__((aligned(16))) uint16_t sKt[HD * (BQ + 8)];
-  const int nqb = (a.S + BQ - 1) / BQ;
+__global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) attn_dq_k(AttnBwdArgs a) {
+  __shared__ __attribute__((aligned(16))) uint16_t sK0[64 * HD];
+  __shared__ __attribute__((aligned(16))) uint16_t sK1[64 * HD];
+  __shared__ __attribute__((aligned(16))) uint16_t sV0[64 * HD];
+  __shared__ __attribute__((aligned(16))) uint16_t sV1[64 * HD];
+  const int G = a.H / a.KV;
+  const int nqb = (a.S + 31) / 32;
   const int qb = nqb - 1 - (int)blockIdx.x;
-  const int h = blockIdx.y, b = blockIdx.z;
-  const int g = h / (a.H / a.KV);
+  const int g = blockIdx.y, b = blockIdx.z;
   const int t = threadIdx.x, lane = t & 63, w = t >> 6, g4 = lane >> 4, c16 = lane & 15;
-  const int q0 = qb * BQ;
-  const int myq = q0 + 16 * w + c16;
+  const int h = g * G + w;
+  const int q0 = qb * 32;
   const int64_t tb = (int64_t)b * a.S;
   const uint16_t* Q = a.qkv + tb * a.ld + a.q_off + (int64_t)h * HD;
   const uint16_t* K = a.qkv + tb * a.ld + a.k_off + (int64_t)g * HD;
   const uint16_t* V = a.qkv + tb * a.ld + a.v_off + (int64_t)g * HD;
   const uint16_t* dO = a.dO + tb * a.lddo + (int64_t)h * HD;
+  const int nkb = min((q0 + 31) / 64 + 1, (a.S + 63) / 64);
 
-  u32x4 qf[HD / 32], df[HD / 32];
+  dma_tile<HD>(sK0, K, a.ld, 0, a.S, w, G, lane);
+  dma_tile<HD>(sV0, V, a.ld, 0, a.S, w, G, lane);
+
+  int myq[2];
+  float lse2[2], Dq[2];
+  u32x4 qf[2][HD / 32], df[2][HD / 32];
 #pragma unroll
-  for (int s = 0; s < HD / 32; ++s) {
-    const bool ok = myq < a.S;
-    qf[s] = ok ? *reinterpret_cast<const u32x4*>(Q + (int64_t)myq * a.ld + 32 * s + 8 * g4) : u32x4{0, 0, 0, 0};
-    df[s] = ok ? *reinterpret_cast<const u32x4*>(dO + (int64_t)myq * a.lddo + 32 * s + 8 * g4) : u32x4{0, 0, 0, 0};
+  for (int qg = 0; qg < 2; ++qg) {
+    myq[qg] = q0 + 16 * qg + c16;
+    const bool ok = myq[qg] < a.S;
+#pragma unroll
+    for (int s = 0; s < HD / 32; ++s) {
+      qf[qg][s] = ok ? *reinterpret_cast<const u32x4*>(Q + (int64_t)myq[qg] * a.ld + 32 * s + 8 * g4) : u32x4{0, 0, 0, 0};
+      df[qg][s] = ok ? *reinterpret_cast<const u32x4*>(dO + (int64_t)myq[qg] * a.lddo + 32 * s + 8 * g4) : u32x4{0, 0, 0, 0};
+    }
+    const int64_t rid = ((int64_t)b * a.H + h) * a.S + myq[qg];
+    lse2[qg] = ok ? a.lse[rid] * kLog2e : 0.f;
+    Dq[qg] = ok ? a.D[rid] : 0.f;
   }
-  const int64_t row_id = ((int64_t)b * a.H + h) * a.S + myq;
-  const float lse2 = myq < a.S ? a.lse[row_id] * kLog2e : 0.f;
-  const float Dq = myq < a.S ? a.D[row_id] : 0.f;
   const float c = a.scale * kLog2e;
-  f32x4 dq[HD / 16];
+  f32x4 dq[2][HD / 16];
 #pragma unroll
-  for (int i = 0; i < HD / 16; ++i) dq[i] = f32x4{0, 0, 0, 0};
+  for (int qg = 0; qg < 2; ++qg)
+#pragma unroll
+    for (int i = 0; i < HD / 16; ++i) dq[qg][i] = f32x4{0, 0, 0, 0};
 
-  for (int kb = 0; kb <= qb; ++kb) {
-    const int k0 = kb * BQ;
-    stage_rows<HD>(sK, K, a.ld, k0, a.S);
-    stage_rows<HD>(sV, V, a.ld, k0, a.S);
-    stage_cols<HD>(sKt, K, a.ld, k0, a.S);
-    __syncthreads();
-    f32x4 sc[4], dp[4];
+  auto block = [&](const uint16_t* sK, const uint16_t* sV, int k0) {
+    f32x4 sc[2][4], dp[2][4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      sc[j] = f32x4{0, 0, 0, 0};
-      dp[j] = f32x4{0, 0, 0, 0};
+#pragma unroll
+      for (int qg = 0; qg < 2; ++qg) { sc[qg][j] = f32x4{0, 0, 0, 0}; dp[qg][j] = f32x4{0, 0, 0, 0}; }
 #pragma unroll
       for (int s = 0; s < HD / 32; ++s) {
-        const int off = (16 * j + c16) * (HD + 8) + 32 * s + 8 * g4;
-        sc[j] = mfma16(*reinterpret_cast<const u32x4*>(sK + off), qf[s], sc[j]);
-        dp[j] = mfma16(*reinterpret_cast<const u32x4*>(sV + off), df[s], dp[j]);
+        const u32x4 ka = frag<HD>(sK, 16 * j + c16, 32 * s + 8 * g4);
+        const u32x4 va = frag<HD>(sV, 16 * j + c16, 32 * s + 8 * g4);
+#pragma unroll
+        for (int qg = 0; qg < 2; ++qg) {
+          sc[qg][j] = mfma16(ka, qf[qg][s], sc[qg][j]);
+          dp[qg][j] = mfma16(va, df[qg][s], dp[qg][j]);
+        }
       }
     }
+    u32x4 dsf[2][2];
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int qg = 0; qg < 2; ++qg) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int key = k0 + 16 * j + 4 * g4 + i;
-        const float p = (key <= myq && key < a.S && myq < a.S) ? exp2f(sc[j][i] * c - lse2) : 0.f;
-        sc[j][i] = p * (dp[j][i] - Dq);     // dS (rounded to bf16 below)
-      }
+      for (int j = 0; j < 4; ++j)
 #pragma unroll
-    for (int tt = 0; tt < 2; ++tt) {
-      const u32x4 dsf = pack8(sc[2 * tt], sc[2 * tt + 1]);
-#pragma unroll
-      for (int hb = 0; hb < HD / 16; ++hb)
-        dq[hb] = mfma16(dsf, read_pair(sKt, 16 * hb + c16, 32 * tt, g4), dq[hb]);
+        for (int i = 0; i < 4; ++i) {
+          const int key = k0 + 16 * j + 4 * g4 + i;
+          const float p = (key <= myq[qg] && key < a.S && myq[qg] < a.S) ? exp2f(sc[qg][j][i] * c - lse2[qg]) : 0.f;
+          sc[qg][j][i] = p * (dp[qg][j][i] - Dq[qg]);     // dS (rounded to bf16 below)
+        }
+      dsf[qg][0] = pack8(sc[qg][0], sc[qg][1]);
+      dsf[qg][1] = pack8(sc[qg][2], sc[qg][3]);
     }
-    __syncthreads();
-  }
-  // dq[hb][i] = dQ[q0 + 16w + 4 g4 + i][16 hb + c16]
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int q = q0 + 16 * w + 4 * g4 + i;
-    if (q >= a.S) continue;
-    float* dst = a.dq + (tb + q) * a.lddq + (int64_t)h * HD;
+    for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
-    for (int hb = 0; hb < HD / 16; ++hb) dst[16 * hb + c16] = dq[hb][i] * a.scale;
+      for (int hb = 0; hb < HD / 16; ++hb) {
+        const u32x4 kt = frag_t<HD>(sK, 32 * tt, 16 * hb, g4, c16);
+        dq[0][hb] = mfma16(dsf[0][tt], kt, dq[0][hb]);
+        dq[1][hb] = mfma16(dsf[1][tt], kt, dq[1][hb]);
+      }
+  };
+
+  for (int kb = 0; kb < nkb; kb += 2) {
+    wait_dma();
+    if (kb + 1 < nkb) {
+      dma_tile<HD>(sK1, K, a.ld, 64 * (kb + 1), a.S, w, G, lane);
+      dma_tile<HD>(sV1, V, a.ld, 64 * (kb + 1), a.S, w, G, lane);
+    }
+    block(sK0, sV0, 64 * kb);
+    if (kb + 1 >= nkb) break;
+    wait_dma();
+    if (kb + 2 < nkb) {
+      dma_tile<HD>(sK0, K, a.ld, 64 * (kb + 2), a.S, w, G, lane);
+      dma_tile<HD>(sV0, V, a.ld, 64 * (kb + 2), a.S, w, G, lane);
+    }
+    block(sK1, sV1, 64 * (kb + 1));
   }
+  // dq[qg][hb][i] = dQ[q0 + 16 qg + 4 g4 + i][16 hb + c16]
+#pragma unroll
+  for (int qg = 0; qg < 2; ++qg)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int q = q0 + 16 * qg + 4 * g4 + i;
+      if (q >= a.S) continue;
+      float* dst = a.dq + (tb + q) * a.lddq + (int64_t)h * HD;
+#pragma unroll
+      for (int hb = 0; hb < HD / 16; ++hb) dst[16 * hb + c16] = dq[qg][hb][i] * a.scale;
+    }
 }
 
+// dK, dV: one workgroup per (64 keys, query head, sequence), wave w owns keys
+// k0 + 16 w .. + 15 and walks the query blocks on or below the diagonal; Q and
+// dO blocks of 64 rows double-buffered by DMA (with their LSE and D values),
+// read as row fragments for S = Q K^T, dP = dO V^T and transposed for
+// dV += P^T dO and dK += dS^T Q.  One float partial per query head; the sum
+// over the heads that share a kv head is taken in head order by the RoPE
+// backward that consumes dK and dV.
 template <int HD>
-__global__ void __launch_bounds__(NT) attn_dkv_k(AttnBwdArgs a) {
-  __shared__ __attribute__((aligned(16))) uint16_t sQ[BQ * (HD + 8)];
-  __shared__ __attribute__((aligned(16))) uint16_t sdO[BQ * (HD + 8)];
-  __shared__ __attribute__((aligned(16))) uint16_t sQt[HD * (BQ + 8)];
-  __shared__ __attribute__((aligned(16))) uint16_t sdOt[HD * (BQ + 8)];
-  __shared__ float sL[BQ], sD[BQ];
+__global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2))) attn_dkv_k(AttnBwdArgs a) {
+  __shared__ __attribute__((aligned(16))) uint16_t sQ0[64 * HD];
+  __shared__ __attribute__((aligned(16))) uint16_t sQ1[64 * HD];
+  __shared__ __attribute__((aligned(16))) uint16_t sO0[64 * HD];
+  __shared__ __attribute__((aligned(16))) uint16_t sO1[64 * HD];
+  __shared__ float sL[2][64], sD[2][64];
   const int nqb = (a.S + BQ - 1) / BQ;
   const int kb = (int)blockIdx.x;
   const int h = blockIdx.y, b = blockIdx.z;
@@ -302,6 +396,21 @@ __global__ void __launch_bounds__(NT) attn_dkv_k(AttnBwdArgs a) {
   const int64_t tb = (int64_t)b * a.S;
   const uint16_t* K = a.qkv + tb * a.ld + a.k_off + (int64_t)g * HD;
   const uint16_t* V = a.qkv + tb * a.ld + a.v_off + (int64_t)g * HD;
+  const uint16_t* Q = a.qkv + tb * a.ld + a.q_off + (int64_t)h * HD;
+  const uint16_t* dO = a.dO + tb * a.lddo + (int64_t)h * HD;
+  const int64_t rid0 = ((int64_t)b * a.H + h) * a.S;
+
+  auto stage = [&](uint16_t* sq, uint16_t* so, int st, int q0) {
+    dma_tile<HD>(sq, Q, a.ld, q0, a.S, w, NT / 64, lane);
+    dma_tile<HD>(so, dO, a.lddo, q0, a.S, w, NT / 64, lane);
+    if (t < BQ) {
+      const int q = q0 + t;
+      sL[st][t] = q < a.S ? a.lse[rid0 + q] * kLog2e : 0.f;
+      sD[st][t] = q < a.S ? a.D[rid0 + q] : 0.f;
+    }
+  };
+  stage(sQ0, sO0, 0, k0);
+
   u32x4 kf[HD / 32], vf[HD / 32];
 #pragma unroll
   for (int s = 0; s < HD / 32; ++s) {
@@ -314,57 +423,49 @@ __global__ void __launch_bounds__(NT) attn_dkv_k(AttnBwdArgs a) {
 #pragma unroll
   for (int i = 0; i < HD / 16; ++i) { dk[i] = f32x4{0, 0, 0, 0}; dv[i] = f32x4{0, 0, 0, 0}; }
 
-  {
-    const uint16_t* Q = a.qkv + tb * a.ld + a.q_off + (int64_t)h * HD;
-    const uint16_t* dO = a.dO + tb * a.lddo + (int64_t)h * HD;
-    for (int qb = kb; qb < nqb; ++qb) {
-      const int q0 = qb * BQ;
-      stage_rows<HD>(sQ, Q, a.ld, q0, a.S);
-      stage_rows<HD>(sdO, dO, a.lddo, q0, a.S);
-      stage_cols<HD>(sQt, Q, a.ld, q0, a.S);
-      stage_cols<HD>(sdOt, dO, a.lddo, q0, a.S);
-      if (t < BQ) {
-        const int q = q0 + t;
-        const int64_t rid = ((int64_t)b * a.H + h) * a.S + q;
-        sL[t] = q < a.S ? a.lse[rid] * kLog2e : 0.f;
-        sD[t] = q < a.S ? a.D[rid] : 0.f;
+  auto block = [&](const uint16_t* sq, const uint16_t* so, int st, int q0) {
+    f32x4 sc[4], dp[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      sc[j] = f32x4{0, 0, 0, 0};
+      dp[j] = f32x4{0, 0, 0, 0};
+#pragma unroll
+      for (int s = 0; s < HD / 32; ++s) {
+        sc[j] = mfma16(frag<HD>(sq, 16 * j + c16, 32 * s + 8 * g4), kf[s], sc[j]);
+        dp[j] = mfma16(frag<HD>(so, 16 * j + c16, 32 * s + 8 * g4), vf[s], dp[j]);
       }
-      __syncthreads();
-      f32x4 sc[4], dp[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        sc[j] = f32x4{0, 0, 0, 0};
-        dp[j] = f32x4{0, 0, 0, 0};
-#pragma unroll
-        for (int s = 0; s < HD / 32; ++s) {
-          const int off = (16 * j + c16) * (HD + 8) + 32 * s + 8 * g4;
-          sc[j] = mfma16(*reinterpret_cast<const u32x4*>(sQ + off), kf[s], sc[j]);
-          dp[j] = mfma16(*reinterpret_cast<const u32x4*>(sdO + off), vf[s], dp[j]);
-        }
-      }
-      // sc[j][i] = S[q = q0 + 16j + 4g4 + i][key = myk]
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int ql = 16 * j + 4 * g4 + i;
-          const int q = q0 + ql;
-          const float p = (myk <= q && q < a.S && myk < a.S) ? exp2f(sc[j][i] * c - sL[ql]) : 0.f;
-          sc[j][i] = p;
-          dp[j][i] = p * (dp[j][i] - sD[ql]);
-        }
-#pragma unroll
-      for (int tt = 0; tt < 2; ++tt) {
-        const u32x4 pf = pack8(sc[2 * tt], sc[2 * tt + 1]);
-        const u32x4 dsf = pack8(dp[2 * tt], dp[2 * tt + 1]);
-#pragma unroll
-        for (int hb = 0; hb < HD / 16; ++hb) {
-          dv[hb] = mfma16(pf, read_pair(sdOt, 16 * hb + c16, 32 * tt, g4), dv[hb]);
-          dk[hb] = mfma16(dsf, read_pair(sQt, 16 * hb + c16, 32 * tt, g4), dk[hb]);
-        }
-      }
-      __syncthreads();
     }
+    // sc[j][i] = S[q = q0 + 16j + 4g4 + i][key = myk]
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int ql = 16 * j + 4 * g4 + i;
+        const int q = q0 + ql;
+        const float p = (myk <= q && q < a.S && myk < a.S) ? exp2f(sc[j][i] * c - sL[st][ql]) : 0.f;
+        sc[j][i] = p;
+        dp[j][i] = p * (dp[j][i] - sD[st][ql]);
+      }
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) {
+      const u32x4 pf = pack8(sc[2 * tt], sc[2 * tt + 1]);
+      const u32x4 dsf = pack8(dp[2 * tt], dp[2 * tt + 1]);
+#pragma unroll
+      for (int hb = 0; hb < HD / 16; ++hb) {
+        dv[hb] = mfma16(pf, frag_t<HD>(so, 32 * tt, 16 * hb, g4, c16), dv[hb]);
+        dk[hb] = mfma16(dsf, frag_t<HD>(sq, 32 * tt, 16 * hb, g4, c16), dk[hb]);
+      }
+    }
+  };
+
+  for (int qb = kb; qb < nqb; qb += 2) {
+    wait_dma();
+    if (qb + 1 < nqb) stage(sQ1, sO1, 1, BQ * (qb + 1));
+    block(sQ0, sO0, 0, BQ * qb);
+    if (qb + 1 >= nqb) break;
+    wait_dma();
+    if (qb + 2 < nqb) stage(sQ0, sO0, 0, BQ * (qb + 2));
+    block(sQ1, sO1, 1, BQ * (qb + 1));
   }
   // dk[hb][i] = this query head's share of dK[key = k0 + 16w + 4g4 + i][16hb + c16]
 #pragma unroll
@@ -383,10 +484,14 @@ __global__ void __launch_bounds__(NT) attn_dkv_k(AttnBwdArgs a) {
 
 }  // namespace
 
+// Heads per kv head the kernels take: one wave each, up to 8 per workgroup.
+static bool group_ok(int H, int KV) { return KV > 0 && H % KV == 0 && H / KV <= 8; }
+
 int attn_fwd(const AttnArgs& a, int B, hipStream_t st) {
-  const dim3 grid((a.S + BQ - 1) / BQ, a.H, B);
-  if (a.hd == 128) hipLaunchKernelGGL(attn_fwd_k<128>, grid, dim3(NT), 0, st, a);
-  else if (a.hd == 64) hipLaunchKernelGGL(attn_fwd_k<64>, grid, dim3(NT), 0, st, a);
+  if (!group_ok(a.H, a.KV) || a.ld % 8 || a.q_off % 8 || a.k_off % 8 || a.v_off % 8) return -1;
+  const dim3 grid((a.S + 31) / 32, a.KV, B), block(64 * (a.H / a.KV));
+  if (a.hd == 128) hipLaunchKernelGGL(attn_fwd_k<128>, grid, block, 0, st, a);
+  else if (a.hd == 64) hipLaunchKernelGGL(attn_fwd_k<64>, grid, block, 0, st, a);
   else return -1;
   return 0;
 }
@@ -394,16 +499,17 @@ int attn_fwd(const AttnArgs& a, int B, hipStream_t st) {
 int attn_bwd(const AttnBwdArgs& a, int B, hipStream_t st) {
   const int T = B * a.S;
   const int64_t waves = (int64_t)T * a.H;
-  const dim3 gq((a.S + BQ - 1) / BQ, a.H, B), gk((a.S + BQ - 1) / BQ, a.H, B);
+  if (!group_ok(a.H, a.KV) || a.ld % 8 || a.lddo % 8 || a.q_off % 8 || a.k_off % 8 || a.v_off % 8) return -1;
+  const dim3 gq((a.S + 31) / 32, a.KV, B), gk((a.S + BQ - 1) / BQ, a.H, B), bq(64 * (a.H / a.KV));
   if (a.hd == 128) {
     hipLaunchKernelGGL(attn_pre_k<128>, dim3((unsigned)ceil_div64(waves * 64, 256)), dim3(256), 0, st,
                        a.dO, a.O, a.lddo, a.S, a.H, T, a.D);
-    hipLaunchKernelGGL(attn_dq_k<128>, gq, dim3(NT), 0, st, a);
+    hipLaunchKernelGGL(attn_dq_k<128>, gq, bq, 0, st, a);
     hipLaunchKernelGGL(attn_dkv_k<128>, gk, dim3(NT), 0, st, a);
   } else if (a.hd == 64) {
     hipLaunchKernelGGL(attn_pre_k<64>, dim3((unsigned)ceil_div64(waves * 64, 256)), dim3(256), 0, st,
                        a.dO, a.O, a.lddo, a.S, a.H, T, a.D);
-    hipLaunchKernelGGL(attn_dq_k<64>, gq, dim3(NT), 0, st, a);
+    hipLaunchKernelGGL(attn_dq_k<64>, gq, bq, 0, st, a);
     hipLaunchKernelGGL(attn_dkv_k<64>, gk, dim3(NT), 0, st, a);
   } else {
     return -1;

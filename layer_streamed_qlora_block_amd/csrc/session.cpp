@@ -123,6 +123,7 @@ bool check_run(const Shape& sh, const qls_run_cfg* run, std::string* why) {
   if (run->max_tokens <= 0 || run->max_seq < 2) return bad("max_tokens must be > 0 and max_seq >= 2");
   const qls_model_cfg& c = sh.c;
   if (c.head_dim != 64 && c.head_dim != 128) return bad("head_dim must be 64 or 128");
+  if (c.n_heads / c.n_kv_heads > 8) return bad("at most 8 query heads per kv head");
   if (c.hidden % 16 || c.intermediate % 16 || sh.qd % 16 || sh.kvd % 16)
     return bad("hidden, intermediate and head widths must be multiples of 16");
   if (c.lora_r % 8 || c.lora_r > 128) return bad("lora_r must be a multiple of 8 up to 128");
