@@ -174,8 +174,8 @@ def main():
         print(json.dumps({"copy_probe_bytes": n, "copies": 3}))
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU: this build streams the layer store into a single MI355X; "
-              "runs on more than one GPU are not part of it", file=sys.stderr)
+        print("bench.py measures one GPU: the layer store streams into a single MI355X; "
+              "runs on more than one GPU are not implemented", file=sys.stderr)
         sys.exit(2)
     import threading
 

@@ -222,6 +222,26 @@ int qls_linear_bwd(const uint8_t* d_codes, const float* d_absmax, int N, int K,
                    const uint16_t* d_A, const uint16_t* d_B, int r, float alpha,
                    float* d_dx, float* d_dA, float* d_dB, void* d_ws, void* stream);
 
+/* Causal grouped-query attention of one decoder layer on its own (the
+ * attention inside qls_sft_step; [P2] "The number, and exactly what it means"
+ * fixes the Llama-3.1-8B attention shape).  qkv bf16 [B*S x (H + 2 KV) hd]:
+ * per token the H query heads, then the KV key heads, then the KV value heads,
+ * hd each; query head h reads kv head h / (H / KV); scores q k^T / sqrt(hd)
+ * over keys j <= i of the same sequence.  Forward: out bf16 [B*S x H hd],
+ * lse float32 [B x H x S] (natural log-sum-exp of each score row).  Backward
+ * from dout bf16 [B*S x H hd] (out and lse from the forward): dq float32
+ * [B*S x H hd], dk and dv float32 [B*S x KV hd], each the sum over the query
+ * heads of its kv head, in head order.  d_ws: qls_attention_ws_bytes(B, S, H,
+ * hd) bytes of scratch.  hd in {64, 128}, H a multiple of KV and at most 8 KV;
+ * QLS_EUNSUPPORTED otherwise, QLS_EINVAL for NULL buffers or sizes <= 0.
+ * Asynchronous on `stream`. */
+int64_t qls_attention_ws_bytes(int B, int S, int H, int hd);
+int qls_attention_fwd(const uint16_t* d_qkv, int B, int S, int H, int KV, int hd, uint16_t* d_out,
+                      float* d_lse, void* stream);
+int qls_attention_bwd(const uint16_t* d_qkv, const uint16_t* d_out, const uint16_t* d_dout,
+                      const float* d_lse, int B, int S, int H, int KV, int hd, float* d_dq,
+                      float* d_dk, float* d_dv, void* d_ws, void* stream);
+
 /* ---------------------------------------------------------------- optimizer
  * AdamW (decoupled weight decay) on n float32 parameters, in place, at step
  * `step` (1-based): the training loop around qls_sft_step / qls_dpo_step.  The

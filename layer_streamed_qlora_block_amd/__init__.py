@@ -93,6 +93,9 @@ _SIG = {
     "qls_nf4_absmax_expand_dev": (_I, [_P, _P, _I64, _P, _P]),
     "qls_adamw_step": (_I, [_P, _P, _P, _P, _I64, _I, C.c_double, C.c_double, C.c_double, C.c_double,
                             C.c_double, _P]),
+    "qls_attention_ws_bytes": (_I64, [_I, _I, _I, _I]),
+    "qls_attention_fwd": (_I, [_P, _I, _I, _I, _I, _I, _P, _P, _P]),
+    "qls_attention_bwd": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P]),
     "qls_linear_ws_bytes": (_I64, [_I, _I, _I, _I]),
     "qls_linear_fwd": (_I, [_P, _P, _I, _I, _P, _I, _P, _P, _I, _F, _P, _P, _P, _P]),
     "qls_linear_bwd": (_I, [_P, _P, _I, _I, _P, _P, _P, _I, _P, _P, _I, _F, _P, _P, _P, _P, _P]),
@@ -202,6 +205,19 @@ def qls_adamw_step(params, grads, m, v, step, lr, beta1=0.9, beta2=0.999, eps=1e
                    stream=None):
     _check(_lib.qls_adamw_step(_ptr(params), _ptr(grads), _ptr(m), _ptr(v), params.numel(), step, lr, beta1,
                                beta2, eps, weight_decay, _stream(stream)))
+
+
+def qls_attention_ws_bytes(B, S, H, hd) -> int:
+    return _check(_lib.qls_attention_ws_bytes(B, S, H, hd))
+
+
+def qls_attention_fwd(qkv, B, S, H, KV, hd, out, lse, stream=None):
+    _check(_lib.qls_attention_fwd(_ptr(qkv), B, S, H, KV, hd, _ptr(out), _ptr(lse), _stream(stream)))
+
+
+def qls_attention_bwd(qkv, out, dout, lse, B, S, H, KV, hd, dq, dk, dv, ws, stream=None):
+    _check(_lib.qls_attention_bwd(_ptr(qkv), _ptr(out), _ptr(dout), _ptr(lse), B, S, H, KV, hd, _ptr(dq),
+                                  _ptr(dk), _ptr(dv), _ptr(ws), _stream(stream)))
 
 
 def qls_linear_ws_bytes(T, N, K, r) -> int:

@@ -29,3 +29,6 @@ struct AttnBwdArgs {
   float* dk; float* dv; int64_t lddkv;
 };
 int attn_bwd(const AttnBwdArgs& a, int B, hipStream_t st);
+// dK / dV of each kv head from the per-query-head partials of attn_bwd:
+// out [T, KV*hd] = the sum, in head order, of the H/KV partials in part [T, H*hd].
+void attn_group_sum(const float* part, float* out, int T, int H, int KV, int hd, hipStream_t st);

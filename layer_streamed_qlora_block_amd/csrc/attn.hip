@@ -482,7 +482,27 @@ __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2)))
   }
 }
 
+// out[t][g hd + j] = sum over i < G, in order, of part[t][(g G + i) hd + j].
+__global__ void group_sum_k(const float* __restrict__ part, float* __restrict__ out, int64_t n, int H, int KV,
+                            int hd) {
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= n) return;
+  const int kvd = KV * hd, G = H / KV;
+  const int64_t t = idx / kvd;
+  const int e = (int)(idx % kvd), g = e / hd, j = e % hd;
+  const float* src = part + t * (int64_t)H * hd + (int64_t)g * G * hd + j;
+  float acc = 0.f;
+  for (int i = 0; i < G; ++i) acc += src[(int64_t)i * hd];
+  out[idx] = acc;
+}
+
 }  // namespace
+
+void attn_group_sum(const float* part, float* out, int T, int H, int KV, int hd, hipStream_t st) {
+  const int64_t n = (int64_t)T * KV * hd;
+  if (n <= 0) return;
+  hipLaunchKernelGGL(group_sum_k, dim3((unsigned)ceil_div64(n, 256)), dim3(256), 0, st, part, out, n, H, KV, hd);
+}
 
 // Heads per kv head the kernels take: one wave each, up to 8 per workgroup.
 static bool group_ok(int H, int KV) { return KV > 0 && H % KV == 0 && H / KV <= 8; }

@@ -1,7 +1,10 @@
-// C ABI: error plumbing, the NF4 dequant hook and the one-linear entry points.
+// C ABI: error plumbing, the NF4 dequant hook, the one-linear and the
+// attention entry points.
 #include <algorithm>
+#include <cmath>
 #include <string>
 
+#include "attn.h"
 #include "gemm.h"
 #include "internal.h"
 #include "ops.h"
@@ -76,6 +79,56 @@ int qls_linear_fwd(const uint8_t* codes, const float* absmax, int N, int K, cons
   f.ws = reinterpret_cast<float*>(ws);
   int rc = linear_fwd(f, (hipStream_t)stream);
   if (rc) return fail(QLS_EHIP, "kernel combination not built");
+  QLS_HIP(hipGetLastError());
+  return QLS_OK;
+}
+
+int64_t qls_attention_ws_bytes(int B, int S, int H, int hd) {
+  if (B <= 0 || S <= 0 || H <= 0 || hd <= 0) return fail(QLS_EINVAL, "sizes must be positive");
+  const int64_t T = (int64_t)B * S;
+  return align_up((int64_t)B * H * S * 4, 256) + 2 * align_up(T * H * hd * 4, 256);
+}
+
+static int attn_check(int B, int S, int H, int KV, int hd) {
+  if (B <= 0 || S <= 0 || H <= 0 || KV <= 0) return fail(QLS_EINVAL, "sizes must be positive");
+  if (hd != 64 && hd != 128) return fail(QLS_EUNSUPPORTED, "head_dim must be 64 or 128");
+  if (H % KV || H / KV > 8) return fail(QLS_EUNSUPPORTED, "n_heads must be a multiple of n_kv_heads, at most 8 times it");
+  return QLS_OK;
+}
+
+int qls_attention_fwd(const uint16_t* qkv, int B, int S, int H, int KV, int hd, uint16_t* out, float* lse,
+                      void* stream) {
+  if (!qkv || !out || !lse) return fail(QLS_EINVAL, "NULL buffer");
+  int rc = attn_check(B, S, H, KV, hd);
+  if (rc) return rc;
+  AttnArgs a{};
+  a.qkv = qkv; a.ld = (int64_t)(H + 2 * KV) * hd; a.q_off = 0; a.k_off = H * hd; a.v_off = (H + KV) * hd;
+  a.S = S; a.H = H; a.KV = KV; a.hd = hd; a.scale = 1.f / std::sqrt((float)hd);
+  a.out = out; a.ldo = (int64_t)H * hd; a.lse = lse;
+  if (attn_fwd(a, B, (hipStream_t)stream)) return fail(QLS_EUNSUPPORTED, "attention shape not supported");
+  QLS_HIP(hipGetLastError());
+  return QLS_OK;
+}
+
+int qls_attention_bwd(const uint16_t* qkv, const uint16_t* out, const uint16_t* dout, const float* lse, int B,
+                      int S, int H, int KV, int hd, float* dq, float* dk, float* dv, void* ws, void* stream) {
+  if (!qkv || !out || !dout || !lse || !dq || !dk || !dv || !ws) return fail(QLS_EINVAL, "NULL buffer");
+  int rc = attn_check(B, S, H, KV, hd);
+  if (rc) return rc;
+  hipStream_t st = (hipStream_t)stream;
+  const int64_t T = (int64_t)B * S;
+  char* w = reinterpret_cast<char*>(ws);
+  float* D = reinterpret_cast<float*>(w);
+  float* pk = reinterpret_cast<float*>(w + align_up((int64_t)B * H * S * 4, 256));
+  float* pv = reinterpret_cast<float*>(w + align_up((int64_t)B * H * S * 4, 256) + align_up(T * H * hd * 4, 256));
+  AttnBwdArgs a{};
+  a.qkv = qkv; a.ld = (int64_t)(H + 2 * KV) * hd; a.q_off = 0; a.k_off = H * hd; a.v_off = (H + KV) * hd;
+  a.S = S; a.H = H; a.KV = KV; a.hd = hd; a.scale = 1.f / std::sqrt((float)hd);
+  a.dO = dout; a.O = out; a.lddo = (int64_t)H * hd; a.lse = lse; a.D = D;
+  a.dq = dq; a.lddq = (int64_t)H * hd; a.dk = pk; a.dv = pv; a.lddkv = (int64_t)H * hd;
+  if (attn_bwd(a, B, st)) return fail(QLS_EUNSUPPORTED, "attention shape not supported");
+  attn_group_sum(pk, dk, (int)T, H, KV, hd, st);
+  attn_group_sum(pv, dv, (int)T, H, KV, hd, st);
   QLS_HIP(hipGetLastError());
   return QLS_OK;
 }

@@ -5,7 +5,7 @@ The pages train with a learning rate of 2e-5 for 3 epochs (page "Fine tune an
 propose 20 streamed against 20 resident steps with matching loss curves as the
 practical check (page "Fine-Tune an 8B Model on a 4GB Laptop GPU: Hands-On
 Guide", section "The gotchas nobody's mentioning yet").  They do not name the
-optimizer; this build takes AdamW with decoupled weight decay (the usual LoRA
+optimizer; the reading taken here is AdamW with decoupled weight decay (the usual LoRA
 fine-tuning optimizer), betas (0.9, 0.999), eps 1e-8, weight decay 0 unless
 given, applied to every A and B entry of the packed float32 LoRA vector:
 
