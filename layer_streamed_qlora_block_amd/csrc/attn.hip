@@ -42,11 +42,14 @@ QLS_DEV u32x4 pack8(const f32x4& a, const f32x4& b) {
 
 // ---- Unpadded swizzled tiles, filled by LDS-DMA.
 // A tile is 64 rows x HD bf16 with rows of HD*2 bytes; the 16-byte chunk c of
-// row r sits at chunk c ^ tswz(r).  The key makes the 16-byte fragment reads
-// of 16 consecutive rows and the 8-byte transpose reads of 8 consecutive rows
-// (two chunks each) land on distinct banks for HD = 128.
+// row r sits at chunk c ^ tswz(r).  LDS serves 128 bytes (32 banks) per pass:
+// 8 lanes of a 16-byte read, 16 lanes of an 8-byte read, and a chunk's banks
+// are fixed by its index mod 8.  The key permutes the low three chunk bits so
+// that the 16-byte fragment reads of 8 consecutive rows (one chunk index) and
+// the 8-byte transpose reads of 4 consecutive rows (two adjacent chunks each)
+// cover all 32 banks once.
 template <int HD>
-QLS_DEV int tswz(int r) { return ((2 * (r & 7)) | ((r >> 3) & 1)) & (HD / 8 - 1); }
+QLS_DEV int tswz(int r) { return (2 * (r & 3)) | ((r >> 2) & 1); }
 template <int HD>
 QLS_DEV int tpos(int r, int col) { return r * HD + 8 * ((col >> 3) ^ tswz<HD>(r)) + (col & 7); }
 
