@@ -388,7 +388,8 @@ __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2)))
   __shared__ __attribute__((aligned(16))) uint16_t sQ1[64 * HD];
   __shared__ __attribute__((aligned(16))) uint16_t sO0[64 * HD];
   __shared__ __attribute__((aligned(16))) uint16_t sO1[64 * HD];
-  __shared__ float sL[2][64], sD[2][64];
+  __shared__ __attribute__((aligned(16))) float sL[2][64];
+  __shared__ __attribute__((aligned(16))) float sD[2][64];
   const int nqb = (a.S + BQ - 1) / BQ;
   const int kb = (int)blockIdx.x;
   const int h = blockIdx.y, b = blockIdx.z;
@@ -440,15 +441,17 @@ __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2)))
     }
     // sc[j][i] = S[q = q0 + 16j + 4g4 + i][key = myk]
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < 4; ++j) {
+      const f32x4 l4 = *reinterpret_cast<const f32x4*>(&sL[st][16 * j + 4 * g4]);
+      const f32x4 d4 = *reinterpret_cast<const f32x4*>(&sD[st][16 * j + 4 * g4]);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int ql = 16 * j + 4 * g4 + i;
-        const int q = q0 + ql;
-        const float p = (myk <= q && q < a.S && myk < a.S) ? exp2f(sc[j][i] * c - sL[st][ql]) : 0.f;
+        const int q = q0 + 16 * j + 4 * g4 + i;
+        const float p = (myk <= q && q < a.S && myk < a.S) ? exp2f(sc[j][i] * c - l4[i]) : 0.f;
         sc[j][i] = p;
-        dp[j][i] = p * (dp[j][i] - sD[st][ql]);
+        dp[j][i] = p * (dp[j][i] - d4[i]);
       }
+    }
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt) {
       const u32x4 pf = pack8(sc[2 * tt], sc[2 * tt + 1]);
