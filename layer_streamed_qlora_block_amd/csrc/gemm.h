@@ -49,9 +49,10 @@ struct GemmArgs {
 
 // Returns 0, or -1 when the (tile, loaders, epilogue) combination is not built.
 int gemm_launch(const GemmArgs& g, int aload, int bload, int epi, int tile, hipStream_t st);
-// Large dequant-GEMMs (256 x 256 tiles, 512 threads): B_NF4_NT with
-// EPI_BF16 (LORA_FWD allowed) and B_NF4_NN with EPI_F32 / EPI_BF16 (no
-// residual) / EPI_SWIGLU_BWD (LORA_DX allowed); split-K (ksplit > 1) writes
+// Large GEMMs (256 x 256 tiles, 512 threads): B_NF4_NT with EPI_BF16
+// (LORA_FWD allowed), B_NF4_NN with EPI_F32 / EPI_BF16 (no residual) /
+// EPI_SWIGLU_BWD (LORA_DX allowed), and B_BF16_NT with EPI_CE_STATS /
+// EPI_CE_GRAD (statistics per 128-column half, no split); split-K (ksplit > 1) writes
 // float partials to g.partial (ksplit * M * N floats) and then runs
 // gemm_reduce_epi.  gemm_big_ok checks the shape and alignment conditions;
 // gemm_big_launch returns -1 when they do not hold.

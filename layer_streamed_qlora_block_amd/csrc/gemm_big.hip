@@ -65,6 +65,9 @@ QLS_DEV int nn_pos(int n, int k) { return n * PITCH + 8 * ((k >> 3) ^ nn_swz(n))
 template <int BL> struct Stage;
 template <> struct Stage<B_NF4_NT> { u32x4 q; float s; static constexpr int kLoads = 2; };
 template <> struct Stage<B_NF4_NN> { uint32_t q[4]; float s[4]; static constexpr int kLoads = 8; };
+// bf16 W[n, k] (the LM head): the weight tile goes to LDS by DMA like the
+// activation tile, in the same swizzled layout; nothing passes through registers.
+template <> struct Stage<B_BF16_NT> { static constexpr int kLoads = 0; };
 
 // Wait until at most n vector-memory operations are outstanding and every LDS
 // operation is done (gfx9 s_waitcnt encoding: vmcnt bits 3:0 and 15:14,
@@ -83,7 +86,8 @@ struct Big {
   const float2* lut2;
   int t, lane, wm, wn, m0, n0;
   __amdgpu_buffer_rsrc_t ra, rq, rs;
-  uint32_t vdma[4], vq, vs;
+  uint32_t vdma[4], vdmb[4], vq, vs;
+  __amdgpu_buffer_rsrc_t rb;
   f32x16 acc[4][2];
 
   QLS_DEV Big(const GemmArgs& g_, uint16_t* a0, uint16_t* a1, uint16_t* b0, uint16_t* b1,
@@ -108,7 +112,15 @@ struct Big {
       const int r = 8 * (4 * (t >> 6) + j) + (lane >> 3);
       vdma[j] = (uint32_t)((r * g.lda + 8 * ((lane & 7) ^ a_swz(r))) * 2);
     }
-    if constexpr (BL == B_NF4_NT) {
+    if constexpr (BL == B_BF16_NT) {
+      // W rows n0.. (ldb elements apart), rows past N read 0.
+      rb = rsrc(g.Bh + (int64_t)n0 * g.ldb, (int64_t)(g.N - n0) * g.ldb * 2);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int r = 8 * (4 * (t >> 6) + j) + (lane >> 3);
+        vdmb[j] = (uint32_t)((r * g.ldb + 8 * ((lane & 7) ^ a_swz(r))) * 2);
+      }
+    } else if constexpr (BL == B_NF4_NT) {
       // W rows n0..: codes row n at n * ldq / 2, absmax at n * ldq / 64.
       rq = rsrc(g.Bq + (int64_t)n0 * g.ldq / 2, (int64_t)(g.N - n0) * g.ldq / 2);
       rs = rsrc(g.Bs + (int64_t)n0 * (g.ldq / 64), (int64_t)(g.N - n0) * (g.ldq / 64) * 4);
@@ -125,7 +137,7 @@ struct Big {
     }
   }
 
-  // Activation tile k0 .. k0+64 straight into LDS.
+  // Activation tile k0 .. k0+64 straight into LDS (and the bf16 weight tile).
   QLS_DEV void dma(uint16_t* s, int k0) {
 #pragma unroll
     for (int j = 0; j < 4; ++j)
@@ -133,9 +145,19 @@ struct Big {
           ra, (__attribute__((address_space(3))) void*)(s + (4 * (t >> 6) + j) * 512), 16, vdma[j],
           (uint32_t)k0 * 2, 0, 0);
   }
+  QLS_DEV void dma_b(uint16_t* s, int k0) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rb, (__attribute__((address_space(3))) void*)(s + (4 * (t >> 6) + j) * 512), 16, vdmb[j],
+          (uint32_t)k0 * 2, 0, 0);
+  }
 
   QLS_DEV void load(Stage<BL>& r, int k0) {
-    if constexpr (BL == B_NF4_NT) {
+    if constexpr (BL == B_BF16_NT) {
+      (void)r;
+      (void)k0;
+    } else if constexpr (BL == B_NF4_NT) {
       r.q = ld128(rq, vq, (uint32_t)k0 / 2);
       r.s = __uint_as_float(ld32(rs, vs, (uint32_t)k0 / 16));
     } else {
@@ -150,7 +172,12 @@ struct Big {
   // Dequantise one register stage into weight stage sB.
   QLS_DEV void store(const Stage<BL>& r, uint16_t* sB) const {
     const int row = t >> 1, half = t & 1;
-    if constexpr (BL == B_NF4_NT) {
+    if constexpr (BL == B_BF16_NT) {
+      (void)r;
+      (void)sB;
+      (void)row;
+      (void)half;
+    } else if constexpr (BL == B_NF4_NT) {
 #pragma unroll
       for (int w = 0; w < 4; ++w) {
         const uint32_t c = r.q[w];
@@ -192,6 +219,8 @@ struct Big {
         const int n = wn * 64 + 32 * j + (lane & 31);
         if constexpr (BL == B_NF4_NN)
           b[j] = *reinterpret_cast<const u32x4*>(sB + nn_pos(n, kofs));
+        else if constexpr (BL == B_BF16_NT)
+          b[j] = *reinterpret_cast<const u32x4*>(sB + a_pos(n, kofs));
         else
           b[j] = *reinterpret_cast<const u32x4*>(sB + n * PITCH + kofs);
       }
@@ -286,6 +315,7 @@ struct Big {
   // all but the newest kLoads vector operations before the barrier covers it.
   QLS_DEV void half_step(int kt, int kb, int nk, int cur, Stage<BL>& rld, const Stage<BL>& rst) {
     dma(sA[cur ^ 1], (kb + min(kt + 1, nk - 1)) * BK);
+    if constexpr (BL == B_BF16_NT) dma_b(sB[cur ^ 1], (kb + min(kt + 1, nk - 1)) * BK);
     asm volatile("" ::: "memory");
     load(rld, (kb + min(kt + 2, nk - 1)) * BK);
     mma(sA[cur], sB[cur]);
@@ -301,10 +331,12 @@ struct Big {
     const int nk = ke - kb;
     Stage<BL> r0, r1;
     dma(sA[0], kb * BK);
+    if constexpr (BL == B_BF16_NT) dma_b(sB[0], kb * BK);
     asm volatile("" ::: "memory");
     load(r0, kb * BK);
     load(r1, (kb + min(1, nk - 1)) * BK);
     store(r0, sB[0]);
+    wait_vm_lds<Stage<BL>::kLoads>();     // the first tiles' DMA (issued before r0, r1) is done
     __syncthreads();
     // Loads past the last step re-read step ke-1 (in bounds, never consumed).
     for (int kt = 0;; kt += 2) {
@@ -343,6 +375,61 @@ struct Big {
       for (int it = 0; it < EROWS * BN / 8 / NT; ++it) {
         const int rr = (t >> 5) + 16 * it, c8 = 8 * (t & 31);
         const int m = m0 + EROWS * h + rr, n = n0 + c8;
+        if constexpr (EPI == EPI_CE_STATS) {
+          // Per row and 128-column half of the tile (16 threads): max and
+          // sum of exp over the valid columns, and the target's logit.
+          const f32x4 x0 = *reinterpret_cast<const f32x4*>(sT + rr * TP + c8);
+          const f32x4 x1 = *reinterpret_cast<const f32x4*>(sT + rr * TP + c8 + 4);
+          const float v[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+          float mx = -INFINITY;
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            if (n + e < g.N) mx = fmaxf(mx, v[e]);
+#pragma unroll
+          for (int o = 1; o < 16; o <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
+          float sm = 0.f;
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            if (n + e < g.N) sm += __expf(v[e] - mx);
+#pragma unroll
+          for (int o = 1; o < 16; o <<= 1) sm += __shfl_xor(sm, o, 64);
+          const int nh = n0 + 128 * ((t & 31) >> 4);
+          if (m < g.M) {
+            if ((t & 15) == 0 && nh < g.N) {
+              const int gt = (g.col0 + nh) / 128;
+              g.stats[((int64_t)m * g.stats_ld + gt) * 2 + 0] = mx;
+              g.stats[((int64_t)m * g.stats_ld + gt) * 2 + 1] = sm;
+            }
+            const int tg = g.tgt[m] - g.col0 - n;
+            if (tg >= 0 && tg < 8 && n + tg < g.N) g.tgt_logit[m] = v[tg];
+          }
+          continue;
+        }
+        if constexpr (EPI == EPI_CE_GRAD) {
+          // dlogits = w_m (softmax - onehot(target)), bf16.
+          if (m < g.M && n < g.N) {
+            const f32x4 x0 = *reinterpret_cast<const f32x4*>(sT + rr * TP + c8);
+            const f32x4 x1 = *reinterpret_cast<const f32x4*>(sT + rr * TP + c8 + 4);
+            const float v[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+            const float w = g.roww[m], ls = g.lse[m];
+            const int tg = g.tgt[m] - g.col0 - n;
+            float d[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              d[e] = 0.f;
+              if (w != 0.f) {
+                d[e] = __expf(v[e] - ls);
+                if (tg == e) d[e] -= 1.f;
+                d[e] *= w;
+              }
+            }
+            u32x4 o;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) o[e] = pack2_bf16(d[2 * e], d[2 * e + 1]);
+            *reinterpret_cast<u32x4*>(reinterpret_cast<uint16_t*>(C) + (int64_t)m * ldc + n) = o;
+          }
+          continue;
+        }
         if (m < g.M && n < g.N) {
           const f32x4 x0 = *reinterpret_cast<const f32x4*>(sT + rr * TP + c8);
           const f32x4 x1 = *reinterpret_cast<const f32x4*>(sT + rr * TP + c8 + 4);
@@ -416,7 +503,13 @@ big_kernel(GemmArgs g, const float* __restrict__ cb) {
   // LoRA term goes into slice 0 only, and each slice writes alpha * acc as a
   // float partial that gemm_reduce_epi sums in slice order.
   const int nk = g.K / BK, ks = g.ksplit > 1 ? g.ksplit : 1, z = blockIdx.z;
-  if (z == 0 && ((BL == B_NF4_NT && g.lora == LORA_FWD) || (BL == B_NF4_NN && g.lora == LORA_DX))) k.lora();
+  if constexpr (BL != B_BF16_NT)
+    if (z == 0 && ((BL == B_NF4_NT && g.lora == LORA_FWD) || (BL == B_NF4_NN && g.lora == LORA_DX))) k.lora();
+  if constexpr (EPI == EPI_CE_STATS || EPI == EPI_CE_GRAD) {
+    k.mainloop(0, nk);
+    k.template epilogue<EPI>(g.C, g.ldc);
+    return;
+  }
   k.mainloop(nk * z / ks, nk * (z + 1) / ks);
   if (ks > 1)
     k.template epilogue<EPI_F32>(g.partial + (int64_t)z * g.M * g.N, g.N);
@@ -435,6 +528,14 @@ bool fits31(int64_t bytes) { return bytes < 0x7fffffffLL; }
 
 bool gemm_big_ok(const GemmArgs& g, int bload, int epi) {
   if (g.M <= 0 || g.N <= 0 || g.K <= 0 || g.K % BK) return false;
+  if (bload == B_BF16_NT) {
+    if (epi != EPI_CE_STATS && epi != EPI_CE_GRAD) return false;
+    if (g.ksplit > 1 || g.lora != LORA_NONE || g.lda % 8 || !a16(g.A) || !fits31((int64_t)g.M * g.lda * 2)) return false;
+    if (!g.Bh || !a16(g.Bh) || g.ldb % 8 || g.ldb < g.K || g.N % 8 || !fits31((int64_t)g.N * g.ldb * 2)) return false;
+    if (!g.tgt) return false;
+    if (epi == EPI_CE_STATS) return g.stats && g.tgt_logit;
+    return g.C && a16(g.C) && g.ldc % 8 == 0 && g.lse && g.roww;
+  }
   if (g.ksplit > 1 && (!g.partial || !a16(g.partial) || g.N % 8 || g.ksplit > g.K / BK)) return false;
   if (g.lda % 8 || !a16(g.A) || !fits31((int64_t)g.M * g.lda * 2)) return false;
   if (g.ldq % 64 || !g.Bq || !g.Bs || !a16(g.C)) return false;
@@ -474,7 +575,11 @@ int gemm_big_launch(const GemmArgs& g, int bload, int epi, hipStream_t st) {
   const unsigned ks = g.ksplit > 1 ? (unsigned)g.ksplit : 1u;
   const dim3 grid(tiles, 1, ks);
   if (g.ev0) (void)hipEventRecord(g.ev0, st);
-  if (bload == B_NF4_NT)
+  if (bload == B_BF16_NT && epi == EPI_CE_STATS)
+    hipLaunchKernelGGL((big_kernel<B_BF16_NT, EPI_CE_STATS>), grid, dim3(NT), 0, st, g, cb);
+  else if (bload == B_BF16_NT)
+    hipLaunchKernelGGL((big_kernel<B_BF16_NT, EPI_CE_GRAD>), grid, dim3(NT), 0, st, g, cb);
+  else if (bload == B_NF4_NT)
     hipLaunchKernelGGL((big_kernel<B_NF4_NT, EPI_BF16>), grid, dim3(NT), 0, st, g, cb);
   else if (epi == EPI_F32)
     hipLaunchKernelGGL((big_kernel<B_NF4_NN, EPI_F32>), grid, dim3(NT), 0, st, g, cb);
@@ -483,6 +588,6 @@ int gemm_big_launch(const GemmArgs& g, int bload, int epi, hipStream_t st) {
   else
     hipLaunchKernelGGL((big_kernel<B_NF4_NN, EPI_SWIGLU_BWD>), grid, dim3(NT), 0, st, g, cb);
   if (g.ev1) (void)hipEventRecord(g.ev1, st);
-  if (ks > 1) gemm_reduce_epi(g, epi, st);
+  if (ks > 1 && bload != B_BF16_NT) gemm_reduce_epi(g, epi, st);
   return 0;
 }

@@ -474,6 +474,10 @@ int bwd_layer(qls_session* S, int l, const uint8_t* rec, const uint16_t* x, floa
 // ---------------------------------------------------------------- head
 // Pass 1 over vocabulary chunks: per-row (max, sum exp) per 128-column tile and
 // the target logit, then the log-sum-exp and per-row log-prob.
+// LM-head chunks with at least 192 output tiles of 256 x 256 (one wave of
+// workgroups over the CUs) run on the large-tile kernels.
+bool head_big(int T, int width) { return cdiv(T, 256) * cdiv(width, 256) >= 192; }
+
 int head_fwd(qls_session* S, const uint16_t* xL, int T, float* logp_out) {
   const Shape& sh = S->sh;
   const int d = sh.c.hidden, V = sh.c.vocab;
@@ -489,7 +493,10 @@ int head_fwd(qls_session* S, const uint16_t* xL, int T, float* logp_out) {
     g.tgt = S->at<int32_t>(S->p.tgt);
     g.stats = S->at<float>(S->p.stats); g.stats_ld = S->z.ntiles;
     g.tgt_logit = S->at<float>(S->p.tgt_logit); g.col0 = col0;
-    QLS_RC(gemm_launch(g, A_ROW, B_BF16_NT, EPI_CE_STATS, kTile, st));
+    if (head_big(T, width) && gemm_big_ok(g, B_BF16_NT, EPI_CE_STATS))
+      QLS_RC(gemm_big_launch(g, B_BF16_NT, EPI_CE_STATS, st));
+    else
+      QLS_RC(gemm_launch(g, A_ROW, B_BF16_NT, EPI_CE_STATS, kTile, st));
   }
   ce_finalize(S->at<float>(S->p.stats), S->z.ntiles, S->at<float>(S->p.tgt_logit),
               S->at<int32_t>(S->p.tgt), T, S->at<float>(S->p.lse_t), logp_out, st);
@@ -513,7 +520,10 @@ int head_bwd(qls_session* S, const uint16_t* xL, int T) {
     g.C = dlog; g.ldc = S->z.Vc;
     g.tgt = S->at<int32_t>(S->p.tgt); g.lse = S->at<float>(S->p.lse_t); g.roww = S->at<float>(S->p.roww);
     g.col0 = col0;
-    QLS_RC(gemm_launch(g, A_ROW, B_BF16_NT, EPI_CE_GRAD, kTile, st));
+    if (head_big(T, width) && gemm_big_ok(g, B_BF16_NT, EPI_CE_GRAD))
+      QLS_RC(gemm_big_launch(g, B_BF16_NT, EPI_CE_GRAD, st));
+    else
+      QLS_RC(gemm_launch(g, A_ROW, B_BF16_NT, EPI_CE_GRAD, kTile, st));
     GemmArgs h{};
     h.M = T; h.N = d; h.K = width;
     h.A = dlog; h.lda = S->z.Vc;
