@@ -150,8 +150,9 @@ def main():
                     help="store format: double-quantised absmax (112.5 MB per 8B layer, the pages' store) "
                          "or float32 absmax (122.7 MB)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--optimizer", choices=["adamw", "none"], default="adamw",
-                    help="update the LoRA vector with AdamW (lr 2e-5, the pages' config) inside every timed step")
+    ap.add_argument("--optimizer", choices=["adamw", "adamw-separate", "none"], default="adamw",
+                    help="update the LoRA vector with AdamW (lr 2e-5, the pages' config) inside every timed step: "
+                         "folded into the backward sweep (adamw) or as a separate call after it")
     ap.add_argument("--dpo", action="store_true", help="same as --pref dpo")
     ap.add_argument("--pref", nargs="*", default=[], choices=["dpo", "simpo", "orpo", "kto"],
                     help="also time preference steps of these heads (2 x seq, shared 128-token prompt)")
@@ -205,9 +206,12 @@ def main():
     print(f"[bench] session ready ({sess.ws_bytes / 1e9:.2f} GB workspace), setup "
           f"{time.perf_counter() - t_setup:.1f} s", file=sys.stderr, flush=True)
 
-    opt = q.AdamW(lora, lr=2e-5) if args.optimizer == "adamw" else None
+    opt = q.AdamW(lora, lr=2e-5) if args.optimizer != "none" else None
 
     def train_step():
+        if args.optimizer == "adamw":
+            sess.sft_step_adamw(ids, opt, grads, loss)
+            return
         sess.sft_step(ids, lora, grads, loss)
         if opt is not None:
             opt.step(grads)
@@ -270,7 +274,8 @@ def main():
                                 f"per layer) in pinned host memory streamed through 2 device slots, bf16 embedding + "
                                 f"LM head 128256 x 4096 resident, LoRA r64 alpha16 on 7 linears"),
                    "global_batch": B, "seq_len": S, "parallelism": "single GPU", "mode": args.mode,
-                   "absmax": args.absmax, "disk_layers": args.disk_layers, "optimizer": (None if opt is None else "AdamW lr 2e-5 on the LoRA vector")},
+                   "absmax": args.absmax, "disk_layers": args.disk_layers, "optimizer": (None if opt is None else "AdamW lr 2e-5 on the LoRA vector"
+                                 + (", folded into the backward sweep" if args.optimizer == "adamw" else ""))},
         "roofline": {"bound": "mfma", "kernel": dom["name"],
                      "achieved": dom["tflops"],
                      "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",

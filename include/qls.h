@@ -351,6 +351,17 @@ void qls_session_destroy(qls_session* s);  /* NULL-safe; synchronises its stream
 int qls_sft_step(qls_session* s, const int32_t* d_ids, int B, int S, const float* d_lora,
                  float* d_grads, float* d_loss, float* h_loss);
 
+/* qls_sft_step followed by qls_adamw_step(d_lora, d_grads, d_m, d_v, n, step,
+ * ...) over the whole LoRA vector, with each layer's slice updated as soon as
+ * that layer's backward has made its gradients final, so the optimizer runs
+ * while the remaining layers stream.  d_lora is read (before any update of
+ * this step) and updated in place; d_grads holds the step's gradients as in
+ * qls_sft_step.  Results equal the two separate calls bit for bit.  Errors as
+ * qls_sft_step and qls_adamw_step. */
+int qls_sft_step_adamw(qls_session* s, const int32_t* d_ids, int B, int S, float* d_lora,
+                       float* d_grads, float* d_m, float* d_v, int step, double lr, double beta1,
+                       double beta2, double eps, double weight_decay, float* d_loss, float* h_loss);
+
 /* Forward-only sweep returning per-sequence sums of next-token log-probs over
  * positions [prompt_len, S): d_seq_logp float32 [B]; d_tok_logp (optional)
  * float32 [B x S] with entry t = log p(ids_{t+1} | ids_{<=t}) (0 at t = S-1).

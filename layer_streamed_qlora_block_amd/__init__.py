@@ -114,6 +114,8 @@ _SIG = {
     "qls_session_create": (_I, [_P, C.POINTER(RunCfg), _P, _I64, _P, _P, C.POINTER(Resident), C.POINTER(_P)]),
     "qls_session_destroy": (None, [_P]),
     "qls_sft_step": (_I, [_P, _P, _I, _I, _P, _P, _P, _P]),
+    "qls_sft_step_adamw": (_I, [_P, _P, _I, _I, _P, _P, _P, _P, _I, C.c_double, C.c_double, C.c_double,
+                                C.c_double, C.c_double, _P, _P]),
     "qls_logprobs": (_I, [_P, _P, _I, _I, _I, _P, _P, _P]),
     "qls_dpo_step": (_I, [_P, _P, _P, _I, _I, _F, _P, _P, _P, _P, _P]),
     "qls_pref_step": (_I, [_P, C.POINTER(PrefCfg), _P, _P, _I, _I, _P, _P, _P, _P, _P]),
@@ -312,6 +314,15 @@ def qls_sft_step(sess, ids, B, S, lora, grads, loss, want_host_loss=False):
     hl = C.c_float(0.0)
     _check(_lib.qls_sft_step(sess, _ptr(ids), B, S, _ptr(lora), _ptr(grads), _ptr(loss),
                              C.byref(hl) if want_host_loss else None))
+    return hl.value if want_host_loss else None
+
+
+def qls_sft_step_adamw(sess, ids, B, S, lora, grads, m, v, step, lr, beta1, beta2, eps, weight_decay, loss,
+                       want_host_loss=False):
+    hl = C.c_float(0.0)
+    _check(_lib.qls_sft_step_adamw(sess, _ptr(ids), B, S, _ptr(lora), _ptr(grads), _ptr(m), _ptr(v), step, lr,
+                                   beta1, beta2, eps, weight_decay, _ptr(loss),
+                                   C.byref(hl) if want_host_loss else None))
     return hl.value if want_host_loss else None
 
 

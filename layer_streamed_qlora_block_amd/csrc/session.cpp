@@ -137,8 +137,17 @@ struct TimedK { hipEvent_t a, b, c; double gflop; bool big; };
 
 }  // namespace
 
+// AdamW folded into the backward sweep (qls_sft_step_adamw): on while one runs.
+struct FusedOpt {
+  bool on = false;
+  float *p = nullptr, *m = nullptr, *v = nullptr;
+  int t = 0;
+  double lr = 0, b1 = 0, b2 = 0, eps = 0, wd = 0;
+};
+
 struct qls_session {
   const qls_store* st = nullptr;
+  FusedOpt opt;
   int ram_layers = 0;                   // layers [ram_layers, L) come from the disk tier
   std::unique_ptr<DiskReader> disk;
   Shape sh;
@@ -544,10 +553,11 @@ int check_tokens(qls_session* S, int B, int Sq) {
   return QLS_OK;
 }
 
-int cast_lora(qls_session* S, const float* d_lora) {
-  lora_cast(d_lora, S->ll.per_layer, S->at<uint16_t>(S->p.lbf), S->ll.per_layer, S->sh.c.n_layers,
-            S->seg, S->cs);
-  return QLS_OK;
+// bf16 working copy of one layer's LoRA matrices, made just before the layer's
+// first forward of a step (so all but layer 0's cast overlap the stream).
+void cast_lora_layer(qls_session* S, const float* d_lora, int l) {
+  const int64_t pl = S->ll.per_layer;
+  lora_cast(d_lora + (int64_t)l * pl, pl, S->at<uint16_t>(S->p.lbf) + (int64_t)l * pl, pl, 1, S->seg, S->cs);
 }
 
 int begin_step(qls_session* S) {
@@ -575,8 +585,9 @@ int end_step(qls_session* S, float* h_loss, const float* d_loss) {
 }
 
 // Forward sweep; policy into the checkpoints, and (if ref) the adapters-disabled
-// reference stream alongside on each resident layer.
-int forward_sweep(qls_session* S, int T, int B, int Sq, bool lora, bool ref) {
+// reference stream alongside on each resident layer.  d_lora (with lora):
+// the float32 LoRA vector, cast layer by layer as the sweep reaches it.
+int forward_sweep(qls_session* S, int T, int B, int Sq, bool lora, bool ref, const float* d_lora) {
   const int L = S->sh.c.n_layers;
   uint16_t* xr[2] = {S->at<uint16_t>(S->p.xref0), S->at<uint16_t>(S->p.xref1)};
   for (int l = 0; l < L; ++l) {
@@ -588,6 +599,7 @@ int forward_sweep(qls_session* S, int T, int B, int Sq, bool lora, bool ref) {
       rc = fwd_layer(S, l, rec, xr[l & 1], xr[(l + 1) & 1], false, T, B, Sq);
       if (rc) return rc;
     }
+    if (lora) cast_lora_layer(S, d_lora, l);
     rc = fwd_layer(S, l, rec, S->ck(l), S->ck(l + 1), lora, T, B, Sq);
     if (rc) return rc;
     rc = release(S, l, &te);
@@ -608,6 +620,12 @@ int backward_sweep(qls_session* S, int T, int B, int Sq, float* grads) {
     if (rc) return rc;
     rc = bwd_layer(S, l, rec, S->ck(l), grads, T, B, Sq);
     if (rc) return rc;
+    if (S->opt.on) {
+      // Fused AdamW: layer l's gradients are final, update its slice now.
+      const int64_t pl = S->ll.per_layer, o = (int64_t)l * pl;
+      const FusedOpt& f = S->opt;
+      adamw_update(f.p + o, grads + o, f.m + o, f.v + o, pl, f.t, f.lr, f.b1, f.b2, f.eps, f.wd, S->cs);
+    }
     rc = release(S, l, &te);
     if (rc) return rc;
     if (l - 2 >= 0 && (rc = prefetch(S, l - 2, -1))) return rc;
@@ -754,10 +772,9 @@ int qls_sft_step(qls_session* S, const int32_t* d_ids, int B, int Sq, const floa
   const int T = B * Sq;
   const Shape& sh = S->sh;
   if ((rc = begin_step(S))) return rc;
-  cast_lora(S, d_lora);
   embed_gather(d_ids, S->res.d_embed, S->ck(0), T, sh.c.hidden, sh.c.vocab, S->at<int>(S->p.scal), S->cs);
   ce_targets(d_ids, B, Sq, S->at<int32_t>(S->p.tgt), S->cs);
-  if ((rc = forward_sweep(S, T, B, Sq, true, false))) return rc;
+  if ((rc = forward_sweep(S, T, B, Sq, true, false, d_lora))) return rc;
   const uint16_t* xL = S->ck(sh.c.n_layers);
   if ((rc = head_fwd(S, xL, T, S->at<float>(S->p.logp)))) return rc;
   sft_weights_loss(S->at<float>(S->p.logp), S->at<int32_t>(S->p.tgt), T, B * (Sq - 1),
@@ -766,6 +783,21 @@ int qls_sft_step(qls_session* S, const int32_t* d_ids, int B, int Sq, const floa
   if ((rc = backward_sweep(S, T, B, Sq, d_grads))) return rc;
   QLS_HIP(hipGetLastError());
   return end_step(S, h_loss, d_loss);
+}
+
+int qls_sft_step_adamw(qls_session* S, const int32_t* d_ids, int B, int Sq, float* d_lora, float* d_grads,
+                       float* d_m, float* d_v, int step, double lr, double beta1, double beta2, double eps,
+                       double weight_decay, float* d_loss, float* h_loss) {
+  if (!S || !d_m || !d_v) return fail(QLS_EINVAL, "NULL argument");
+  if (step < 1) return fail(QLS_EINVAL, "step must be >= 1");
+  if (!(beta1 >= 0.0 && beta1 < 1.0) || !(beta2 >= 0.0 && beta2 < 1.0) || !(eps > 0.0))
+    return fail(QLS_EINVAL, "betas must be in [0, 1) and eps positive");
+  S->opt.on = true;
+  S->opt.p = d_lora; S->opt.m = d_m; S->opt.v = d_v; S->opt.t = step;
+  S->opt.lr = lr; S->opt.b1 = beta1; S->opt.b2 = beta2; S->opt.eps = eps; S->opt.wd = weight_decay;
+  const int rc = qls_sft_step(S, d_ids, B, Sq, d_lora, d_grads, d_loss, h_loss);
+  S->opt.on = false;
+  return rc;
 }
 
 int qls_logprobs(qls_session* S, const int32_t* d_ids, int B, int Sq, int prompt_len, const float* d_lora,
@@ -777,10 +809,10 @@ int qls_logprobs(qls_session* S, const int32_t* d_ids, int B, int Sq, int prompt
   const int T = B * Sq;
   const Shape& sh = S->sh;
   if ((rc = begin_step(S))) return rc;
-  if (d_lora) cast_lora(S, d_lora);
+
   embed_gather(d_ids, S->res.d_embed, S->ck(0), T, sh.c.hidden, sh.c.vocab, S->at<int>(S->p.scal), S->cs);
   ce_targets(d_ids, B, Sq, S->at<int32_t>(S->p.tgt), S->cs);
-  if ((rc = forward_sweep(S, T, B, Sq, d_lora != nullptr, false))) return rc;
+  if ((rc = forward_sweep(S, T, B, Sq, d_lora != nullptr, false, d_lora))) return rc;
   if ((rc = head_fwd(S, S->ck(sh.c.n_layers), T, S->at<float>(S->p.logp)))) return rc;
   seq_logp(S->at<float>(S->p.logp), B, Sq, prompt_len, d_seq_logp, d_tok_logp, S->cs);
   QLS_HIP(hipGetLastError());
@@ -810,13 +842,12 @@ int qls_pref_step(qls_session* S, const qls_pref_cfg* cfg, const int32_t* d_chos
   int32_t* ids = S->at<int32_t>(S->p.ids);
   QLS_HIP(hipMemcpyAsync(ids, d_chosen, Sq * 4, hipMemcpyDeviceToDevice, S->cs));
   QLS_HIP(hipMemcpyAsync(ids + Sq, d_rejected, Sq * 4, hipMemcpyDeviceToDevice, S->cs));
-  cast_lora(S, d_lora);
   embed_gather(ids, S->res.d_embed, S->ck(0), T, d, sh.c.vocab, S->at<int>(S->p.scal), S->cs);
   if (ref)
     QLS_HIP(hipMemcpyAsync(S->at<uint16_t>(S->p.xref0), S->ck(0), (size_t)T * d * 2, hipMemcpyDeviceToDevice,
                            S->cs));
   ce_targets(ids, B, Sq, S->at<int32_t>(S->p.tgt), S->cs);
-  if ((rc = forward_sweep(S, T, B, Sq, true, ref))) return rc;
+  if ((rc = forward_sweep(S, T, B, Sq, true, ref, d_lora))) return rc;
   const int L = sh.c.n_layers;
   if (ref) {
     const uint16_t* xref = S->at<uint16_t>(L & 1 ? S->p.xref1 : S->p.xref0);
@@ -853,7 +884,7 @@ int qls_layer_fwd_bwd(qls_session* S, int layer, const uint16_t* d_x, const uint
     QLS_HIP(hipEventRecord(S->step_ev.back().a, S->cs));
   }
   if ((rc = prefetch(S, layer, 1))) return rc;
-  cast_lora(S, d_lora);
+  cast_lora_layer(S, d_lora, layer);
   const uint8_t* rec;
   TimedEv te{};
   if ((rc = acquire(S, layer, &rec, &te))) return rc;

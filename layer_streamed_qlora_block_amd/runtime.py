@@ -14,7 +14,7 @@ import torch
 from . import (QLS_ABSMAX_DQ8, QLS_ABSMAX_F32, QLS_RESIDENT, QLS_STREAMED, RunCfg, model_cfg, qls_debug_set,
                pref_cfg, qls_adamw_step, qls_dpo_step, qls_pref_step, qls_layer_fwd_bwd, qls_layer_record_bytes_fmt, qls_logprobs, qls_lora_numel,
                qls_session_checkpoints, qls_session_create, qls_session_destroy, qls_session_reset_stats,
-               qls_session_stats, qls_sft_step, qls_store_create_fmt, qls_store_create_tiered, qls_store_destroy, qls_store_layer_view,
+               qls_session_stats, qls_sft_step, qls_sft_step_adamw, qls_store_create_fmt, qls_store_create_tiered, qls_store_destroy, qls_store_layer_view,
                qls_store_set_layer_fp32, qls_store_set_layer_nf4, qls_workspace_bytes)
 
 
@@ -116,6 +116,18 @@ class Session:
         self._enter()
         try:
             return qls_sft_step(self.h, ids, B, S, lora, grads, loss, want_host_loss=host_loss)
+        finally:
+            self._exit()
+
+    def sft_step_adamw(self, ids, opt: "AdamW", grads, loss, host_loss=False):
+        """SFT step with the AdamW update of opt.p (the LoRA vector) folded into
+        the backward sweep (qls_sft_step_adamw); advances opt's step count."""
+        B, S = ids.shape
+        opt.t += 1
+        self._enter()
+        try:
+            return qls_sft_step_adamw(self.h, ids, B, S, opt.p, grads, opt.m, opt.v, opt.t, opt.lr, opt.betas[0],
+                                      opt.betas[1], opt.eps, opt.wd, loss, want_host_loss=host_loss)
         finally:
             self._exit()
 

@@ -5,7 +5,8 @@
   a 4GB Laptop GPU: Hands-On Guide", section "The gotchas nobody's mentioning
   yet": matching loss curves as the practical check): the loss curves, the
   final LoRA vector and the optimizer moments are identical bit for bit, also
-  with slots poisoned on release.
+  with slots poisoned on release and with AdamW folded into the backward
+  sweep (qls_sft_step_adamw).
 * The same 20-step loop against the oracle's: every step's loss within 1e-3
   relative; the LoRA change over the 20 steps within 3e-2 relative L2 and
   cosine 0.999.
@@ -45,7 +46,7 @@ def test_adamw_bitwise_equals_oracle(q):
         assert np.array_equal(bits(got), want.view(np.uint32))
 
 
-def _loop(q, store, res, cfg, ids, steps, lr, mode, flags=0):
+def _loop(q, store, res, cfg, ids, steps, lr, mode, flags=0, fused=False):
     sess = q.Session(store, *res, max_tokens=ids.shape[0] * ids.shape[1], max_seq=ids.shape[1], mode=mode)
     sess.debug(flags)
     lora = torch.from_numpy(synth.pack_lora(cfg, synth.lora_init(cfg, b_std=0.0))).cuda()
@@ -55,6 +56,9 @@ def _loop(q, store, res, cfg, ids, steps, lr, mode, flags=0):
     d_ids = torch.from_numpy(ids).cuda()
     curve = []
     for _ in range(steps):
+        if fused:
+            curve.append(sess.sft_step_adamw(d_ids, opt, grads, loss, host_loss=True))
+            continue
         curve.append(sess.sft_step(d_ids, lora, grads, loss, host_loss=True))
         opt.step(grads)
     torch.cuda.synchronize()
@@ -79,13 +83,16 @@ def test_20_streamed_steps_equal_20_resident_steps(q):
     cfg = synth.scaled(synth.TINY, L=6)
     store, _, res = _store(q, cfg)
     ids = synth.token_ids(cfg, 1, 64, seed=11)
-    runs = {name: _loop(q, store, res, cfg, ids, 20, 1e-3, mode, flags)
-            for name, mode, flags in [("resident", q.QLS_RESIDENT, 0), ("streamed", q.QLS_STREAMED, 0),
-                                      ("poison", q.QLS_STREAMED, q.DBG_POISON_ON_RELEASE)]}
+    runs = {name: _loop(q, store, res, cfg, ids, 20, 1e-3, mode, flags, fused)
+            for name, mode, flags, fused in [("resident", q.QLS_RESIDENT, 0, False),
+                                             ("streamed", q.QLS_STREAMED, 0, False),
+                                             ("poison", q.QLS_STREAMED, q.DBG_POISON_ON_RELEASE, False),
+                                             ("fused", q.QLS_STREAMED, 0, True),
+                                             ("fused-poison", q.QLS_STREAMED, q.DBG_POISON_ON_RELEASE, True)]}
     curve = runs["resident"][0]
     print("loss curve", np.round(curve, 5).tolist(), flush=True)
     assert curve[-1] < curve[0]                               # it trains
-    for name in ("streamed", "poison"):
+    for name in ("streamed", "poison", "fused", "fused-poison"):
         c, p, o = runs[name]
         assert np.array_equal(c.view(np.uint32), curve.view(np.uint32)), name
         assert np.array_equal(bits(p), bits(runs["resident"][1])), name
