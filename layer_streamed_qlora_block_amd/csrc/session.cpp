@@ -203,10 +203,12 @@ struct qls_session {
   uint16_t* ck(int l) const { return at<uint16_t>(p.ckpt) + (int64_t)l * z.Tm * sh.c.hidden; }
   uint16_t* lw(int l) const { return at<uint16_t>(p.lbf) + (int64_t)l * ll.per_layer; }
 
+  // Timing events: read only after both streams are synchronized, so they skip
+  // the system-scope fence (cache write-back and invalidation) on record.
   hipEvent_t next_ev() {
     if (ev_next >= ev_pool.size()) {
       hipEvent_t e;
-      if (hipEventCreate(&e) != hipSuccess) return nullptr;
+      if (hipEventCreateWithFlags(&e, hipEventDisableSystemFence) != hipSuccess) return nullptr;
       ev_pool.push_back(e);
     }
     return ev_pool[ev_next++];
