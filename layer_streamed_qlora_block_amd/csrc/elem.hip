@@ -81,6 +81,72 @@ __global__ void __launch_bounds__(TB) rmsnorm_bwd_k(const uint16_t* __restrict__
   }
 }
 
+// Same as rmsnorm_bwd_k for d <= 8 * TB * NC: the thread's (up to NC) 8-wide
+// chunks of x, dy, w (and gres) stay in registers across the three passes.
+template <int NC>
+__global__ void __launch_bounds__(TB) rmsnorm_bwd_vec_k(const uint16_t* __restrict__ x,
+                                                        const uint16_t* __restrict__ w, float eps,
+                                                        const float* __restrict__ dy,
+                                                        const float* gres, float* out,
+                                                        uint16_t* __restrict__ out_bf16, int d) {
+  __shared__ float red[4];
+  const int64_t row = blockIdx.x;
+  const int nc = d / 8;
+  float xv[NC][8], dv[NC][8];
+  float ss = 0.f;
+#pragma unroll
+  for (int k = 0; k < NC; ++k) {
+    const int c = threadIdx.x + k * TB;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) { xv[k][e] = 0.f; dv[k][e] = 0.f; }
+    if (c < nc) {
+      const u32x4 xx = reinterpret_cast<const u32x4*>(x + row * d)[c];
+      const u32x4 ww = reinterpret_cast<const u32x4*>(w)[c];
+      const f32x4 d0 = reinterpret_cast<const f32x4*>(dy + row * d)[2 * c];
+      const f32x4 d1 = reinterpret_cast<const f32x4*>(dy + row * d)[2 * c + 1];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        xv[k][2 * q] = bflo(xx[q]);
+        xv[k][2 * q + 1] = bfhi(xx[q]);
+      }
+      const float dd[8] = {d0.x, d0.y, d0.z, d0.w, d1.x, d1.y, d1.z, d1.w};
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        dv[k][2 * q] = dd[2 * q] * bflo(ww[q]);          // dy * w
+        dv[k][2 * q + 1] = dd[2 * q + 1] * bfhi(ww[q]);
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) ss += xv[k][e] * xv[k][e];
+    }
+  }
+  const float rho = 1.f / sqrtf(block_sum(ss, red) / (float)d + eps);
+  float dot = 0.f;
+#pragma unroll
+  for (int k = 0; k < NC; ++k)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) dot += dv[k][e] * (xv[k][e] * rho);
+  const float mean = block_sum(dot, red) / (float)d;
+#pragma unroll
+  for (int k = 0; k < NC; ++k) {
+    const int c = threadIdx.x + k * TB;
+    if (c >= nc) continue;
+    float o[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[e] = rho * (dv[k][e] - xv[k][e] * rho * mean);
+    if (gres) {
+      const f32x4 g0 = reinterpret_cast<const f32x4*>(gres + row * d)[2 * c];
+      const f32x4 g1 = reinterpret_cast<const f32x4*>(gres + row * d)[2 * c + 1];
+      o[0] += g0.x; o[1] += g0.y; o[2] += g0.z; o[3] += g0.w;
+      o[4] += g1.x; o[5] += g1.y; o[6] += g1.z; o[7] += g1.w;
+    }
+    reinterpret_cast<f32x4*>(out + row * d)[2 * c] = f32x4{o[0], o[1], o[2], o[3]};
+    reinterpret_cast<f32x4*>(out + row * d)[2 * c + 1] = f32x4{o[4], o[5], o[6], o[7]};
+    if (out_bf16)
+      reinterpret_cast<u32x4*>(out_bf16 + row * d)[c] =
+          u32x4{pack2_bf16(o[0], o[1]), pack2_bf16(o[2], o[3]), pack2_bf16(o[4], o[5]), pack2_bf16(o[6], o[7])};
+  }
+}
+
 // cs: [S][hd/2][2] (cos, sin).  One thread per rotated pair.
 __global__ void rope_fwd_k(uint16_t* __restrict__ qkv, int64_t ld, int T, int S, int nh_q,
                            int nh_k, int hd, const float* __restrict__ cs) {
@@ -97,6 +163,87 @@ __global__ void rope_fwd_k(uint16_t* __restrict__ qkv, int64_t ld, int T, int S,
   const float x1 = bf2f(p[j]), x2 = bf2f(p[j + h2]);
   p[j] = f2bf(x1 * c - x2 * s);
   p[j + h2] = f2bf(x2 * c + x1 * s);
+}
+
+// As rope_fwd_k, four consecutive pairs per thread (h2 % 4 == 0): 8-byte
+// loads and stores of the bf16 halves and 16-byte loads of (cos, sin).
+__global__ void rope_fwd4_k(uint16_t* __restrict__ qkv, int64_t ld, int T, int S, int nh_q, int nh_k, int hd,
+                            const float* __restrict__ cs) {
+  const int h2 = hd / 2, h8 = h2 / 4;
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t per_t = (int64_t)(nh_q + nh_k) * h8;
+  if (idx >= (int64_t)T * per_t) return;
+  const int t = (int)(idx / per_t);
+  const int rem = (int)(idx % per_t);
+  const int head = rem / h8, j = 4 * (rem % h8);
+  const int pos = t % S;
+  const f32x4 c01 = *reinterpret_cast<const f32x4*>(cs + ((int64_t)pos * h2 + j) * 2);
+  const f32x4 c23 = *reinterpret_cast<const f32x4*>(cs + ((int64_t)pos * h2 + j + 2) * 2);
+  const float c[4] = {c01.x, c01.z, c23.x, c23.z}, sn[4] = {c01.y, c01.w, c23.y, c23.w};
+  uint16_t* p = qkv + (int64_t)t * ld + (int64_t)head * hd;
+  const u32x2 a = *reinterpret_cast<const u32x2*>(p + j), b = *reinterpret_cast<const u32x2*>(p + j + h2);
+  const float x1[4] = {bflo(a.x), bfhi(a.x), bflo(a.y), bfhi(a.y)};
+  const float x2[4] = {bflo(b.x), bfhi(b.x), bflo(b.y), bfhi(b.y)};
+  float y1[4], y2[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    y1[e] = x1[e] * c[e] - x2[e] * sn[e];
+    y2[e] = x2[e] * c[e] + x1[e] * sn[e];
+  }
+  *reinterpret_cast<u32x2*>(p + j) = u32x2{pack2_bf16(y1[0], y1[1]), pack2_bf16(y1[2], y1[3])};
+  *reinterpret_cast<u32x2*>(p + j + h2) = u32x2{pack2_bf16(y2[0], y2[1]), pack2_bf16(y2[2], y2[3])};
+}
+
+// As rope_bwd_k, four consecutive pairs (or v elements) per thread.
+__global__ void rope_bwd4_k(const float* __restrict__ dq, const float* __restrict__ dk,
+                            const float* __restrict__ dv, uint16_t* __restrict__ out, int64_t ld,
+                            int T, int S, int nh_q, int nh_k, int hd, const float* __restrict__ cs) {
+  const int h2 = hd / 2, h8 = h2 / 4;
+  const int qd = nh_q * hd, kvd = nh_k * hd;
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t per_t = (int64_t)(nh_q + nh_k) * h8 + kvd / 4;
+  if (idx >= (int64_t)T * per_t) return;
+  const int t = (int)(idx / per_t);
+  const int rem = (int)(idx % per_t);
+  uint16_t* o = out + (int64_t)t * ld;
+  const int grp = nh_q / nh_k;
+  if (rem < (nh_q + nh_k) * h8) {
+    const int head = rem / h8, j = 4 * (rem % h8);
+    const int pos = t % S;
+    const f32x4 c01 = *reinterpret_cast<const f32x4*>(cs + ((int64_t)pos * h2 + j) * 2);
+    const f32x4 c23 = *reinterpret_cast<const f32x4*>(cs + ((int64_t)pos * h2 + j + 2) * 2);
+    const float c[4] = {c01.x, c01.z, c23.x, c23.z}, sn[4] = {c01.y, c01.w, c23.y, c23.w};
+    f32x4 x1, x2;
+    if (head < nh_q) {
+      const float* src = dq + (int64_t)t * qd + (int64_t)head * hd;
+      x1 = *reinterpret_cast<const f32x4*>(src + j);
+      x2 = *reinterpret_cast<const f32x4*>(src + j + h2);
+    } else {                      // kv head: sum the query-head partials in order
+      const float* src = dk + (int64_t)t * qd + (int64_t)(head - nh_q) * grp * hd;
+      x1 = f32x4{0.f, 0.f, 0.f, 0.f};
+      x2 = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int i = 0; i < grp; ++i) {
+        x1 += *reinterpret_cast<const f32x4*>(src + i * hd + j);
+        x2 += *reinterpret_cast<const f32x4*>(src + i * hd + j + h2);
+      }
+    }
+    float y1[4], y2[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      y1[e] = x1[e] * c[e] + x2[e] * sn[e];
+      y2[e] = x2[e] * c[e] - x1[e] * sn[e];
+    }
+    *reinterpret_cast<u32x2*>(o + (int64_t)head * hd + j) = u32x2{pack2_bf16(y1[0], y1[1]), pack2_bf16(y1[2], y1[3])};
+    *reinterpret_cast<u32x2*>(o + (int64_t)head * hd + j + h2) =
+        u32x2{pack2_bf16(y2[0], y2[1]), pack2_bf16(y2[2], y2[3])};
+  } else {
+    const int e = 4 * (rem - (nh_q + nh_k) * h8);      // element of the kv-width v row
+    const int g = e / hd, j = e % hd;
+    const float* src = dv + (int64_t)t * qd + (int64_t)g * grp * hd + j;
+    f32x4 v = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int i = 0; i < grp; ++i) v += *reinterpret_cast<const f32x4*>(src + i * hd);
+    *reinterpret_cast<u32x2*>(o + qd + kvd + e) = u32x2{pack2_bf16(v.x, v.y), pack2_bf16(v.z, v.w)};
+  }
 }
 
 __global__ void rope_bwd_k(const float* __restrict__ dq, const float* __restrict__ dk,
@@ -348,12 +495,25 @@ void rmsnorm_fwd(const uint16_t* x, const uint16_t* w, float eps, uint16_t* y, i
 void rmsnorm_bwd(const uint16_t* x, const uint16_t* w, float eps, const float* dy, const float* gres,
                  float* out, uint16_t* out_bf16, int T, int d, hipStream_t st) {
   if (T <= 0) return;
-  hipLaunchKernelGGL(rmsnorm_bwd_k, dim3(T), dim3(TB), 0, st, x, w, eps, dy, gres, out, out_bf16, d);
+  const auto a16 = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; };
+  const bool vec = d % 8 == 0 && a16(x) && a16(w) && a16(dy) && a16(out) && (!gres || a16(gres)) &&
+                   (!out_bf16 || a16(out_bf16));
+  if (vec && d <= 8 * TB * 2)
+    hipLaunchKernelGGL(rmsnorm_bwd_vec_k<2>, dim3(T), dim3(TB), 0, st, x, w, eps, dy, gres, out, out_bf16, d);
+  else if (vec && d <= 8 * TB * 4)
+    hipLaunchKernelGGL(rmsnorm_bwd_vec_k<4>, dim3(T), dim3(TB), 0, st, x, w, eps, dy, gres, out, out_bf16, d);
+  else
+    hipLaunchKernelGGL(rmsnorm_bwd_k, dim3(T), dim3(TB), 0, st, x, w, eps, dy, gres, out, out_bf16, d);
 }
 void rope_fwd(uint16_t* qkv, int64_t ld, int T, int S, int H, int KV, int hd, const float* cs,
               hipStream_t st) {
   const int64_t n = (int64_t)T * (H + KV) * (hd / 2);
   if (n <= 0) return;
+  if (hd % 8 == 0 && ld % 4 == 0 && (reinterpret_cast<uintptr_t>(qkv) & 7) == 0) {
+    hipLaunchKernelGGL(rope_fwd4_k, dim3((unsigned)ceil_div64(n / 4, 256)), dim3(256), 0, st, qkv, ld, T, S,
+                       H, KV, hd, cs);
+    return;
+  }
   hipLaunchKernelGGL(rope_fwd_k, dim3((unsigned)ceil_div64(n, 256)), dim3(256), 0, st, qkv, ld, T, S,
                      H, KV, hd, cs);
 }
@@ -361,6 +521,13 @@ void rope_bwd(const float* dq, const float* dk, const float* dv, uint16_t* dqkv,
               int S, int H, int KV, int hd, const float* cs, hipStream_t st) {
   const int64_t n = (int64_t)T * ((H + KV) * (hd / 2) + KV * hd / 2);
   if (n <= 0) return;
+  if (hd % 8 == 0 && ld % 4 == 0 && (reinterpret_cast<uintptr_t>(dqkv) & 7) == 0 &&
+      ((reinterpret_cast<uintptr_t>(dq) | reinterpret_cast<uintptr_t>(dk) | reinterpret_cast<uintptr_t>(dv)) & 15) == 0) {
+    const int64_t n4 = (int64_t)T * ((H + KV) * (hd / 8) + KV * hd / 4);   // threads: 4 pairs or 4 v elements each
+    hipLaunchKernelGGL(rope_bwd4_k, dim3((unsigned)ceil_div64(n4, 256)), dim3(256), 0, st, dq, dk, dv,
+                       dqkv, ld, T, S, H, KV, hd, cs);
+    return;
+  }
   hipLaunchKernelGGL(rope_bwd_k, dim3((unsigned)ceil_div64(n, 256)), dim3(256), 0, st, dq, dk, dv,
                      dqkv, ld, T, S, H, KV, hd, cs);
 }
