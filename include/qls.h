@@ -233,7 +233,8 @@ int qls_linear_bwd(const uint8_t* d_codes, const float* d_absmax, int N, int K,
  * [B*S x H hd], dk and dv float32 [B*S x KV hd], each the sum over the query
  * heads of its kv head, in head order.  d_ws: qls_attention_ws_bytes(B, S, H,
  * hd) bytes of scratch.  hd in {64, 128}, H a multiple of KV and at most 8 KV;
- * QLS_EUNSUPPORTED otherwise, QLS_EINVAL for NULL buffers or sizes <= 0.
+ * QLS_EUNSUPPORTED otherwise, QLS_EINVAL for NULL buffers, buffers not
+ * 16-byte aligned or sizes <= 0.
  * Asynchronous on `stream`. */
 int64_t qls_attention_ws_bytes(int B, int S, int H, int hd);
 int qls_attention_fwd(const uint16_t* d_qkv, int B, int S, int H, int KV, int hd, uint16_t* d_out,

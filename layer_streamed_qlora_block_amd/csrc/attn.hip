@@ -238,19 +238,27 @@ __global__ void __launch_bounds__(512) attn_fwd_k(AttnArgs a) {
   }
 }
 
-// D[b,h,q] = sum_j dO[q, h, j] * O[q, h, j]; one wave per (row, head).
+// D[b,h,q] = sum_j dO[q, h, j] * O[q, h, j]; HD/8 lanes per (row, head), 8
+// elements (16 bytes) of each operand per lane.
 template <int HD>
 __global__ void attn_pre_k(const uint16_t* __restrict__ dO, const uint16_t* __restrict__ O,
                            int64_t ld, int S, int H, int T, float* __restrict__ D) {
-  const int64_t wid = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) >> 6;
-  const int lane = threadIdx.x & 63;
-  if (wid >= (int64_t)T * H) return;
-  const int tok = (int)(wid / H), h = (int)(wid % H);
+  constexpr int L = HD / 8;                       // lanes per (row, head): 16 or 8
+  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t pair = gid / L;
+  const int c = (int)(gid % L);
+  const bool ok = pair < (int64_t)T * H;
+  const int tok = ok ? (int)(pair / H) : 0, h = ok ? (int)(pair % H) : 0;
   float acc = 0.f;
-  for (int j = lane; j < HD; j += 64)
-    acc += bf2f(dO[(int64_t)tok * ld + h * HD + j]) * bf2f(O[(int64_t)tok * ld + h * HD + j]);
-  acc = warp_sum(acc);
-  if (lane == 0) {
+  if (ok) {
+    const u32x4 a = *reinterpret_cast<const u32x4*>(dO + (int64_t)tok * ld + h * HD + 8 * c);
+    const u32x4 o = *reinterpret_cast<const u32x4*>(O + (int64_t)tok * ld + h * HD + 8 * c);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) acc += bflo(a[q]) * bflo(o[q]) + bfhi(a[q]) * bfhi(o[q]);
+  }
+#pragma unroll
+  for (int off = 1; off < L; off <<= 1) acc += __shfl_xor(acc, off, 64);
+  if (ok && c == 0) {
     const int b = tok / S, s = tok % S;
     D[((int64_t)b * H + h) * S + s] = acc;
   }
@@ -528,12 +536,12 @@ int attn_bwd(const AttnBwdArgs& a, int B, hipStream_t st) {
   if (!group_ok(a.H, a.KV) || a.ld % 8 || a.lddo % 8 || a.q_off % 8 || a.k_off % 8 || a.v_off % 8) return -1;
   const dim3 gq((a.S + 31) / 32, a.KV, B), gk((a.S + BQ - 1) / BQ, a.H, B), bq(64 * (a.H / a.KV));
   if (a.hd == 128) {
-    hipLaunchKernelGGL(attn_pre_k<128>, dim3((unsigned)ceil_div64(waves * 64, 256)), dim3(256), 0, st,
+    hipLaunchKernelGGL(attn_pre_k<128>, dim3((unsigned)ceil_div64(waves * 16, 256)), dim3(256), 0, st,
                        a.dO, a.O, a.lddo, a.S, a.H, T, a.D);
     hipLaunchKernelGGL(attn_dq_k<128>, gq, bq, 0, st, a);
     hipLaunchKernelGGL(attn_dkv_k<128>, gk, dim3(NT), 0, st, a);
   } else if (a.hd == 64) {
-    hipLaunchKernelGGL(attn_pre_k<64>, dim3((unsigned)ceil_div64(waves * 64, 256)), dim3(256), 0, st,
+    hipLaunchKernelGGL(attn_pre_k<64>, dim3((unsigned)ceil_div64(waves * 8, 256)), dim3(256), 0, st,
                        a.dO, a.O, a.lddo, a.S, a.H, T, a.D);
     hipLaunchKernelGGL(attn_dq_k<64>, gq, bq, 0, st, a);
     hipLaunchKernelGGL(attn_dkv_k<64>, gk, dim3(NT), 0, st, a);

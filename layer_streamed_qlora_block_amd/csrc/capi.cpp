@@ -2,6 +2,7 @@
 // attention entry points.
 #include <algorithm>
 #include <cmath>
+#include <initializer_list>
 #include <string>
 
 #include "attn.h"
@@ -96,9 +97,17 @@ static int attn_check(int B, int S, int H, int KV, int hd) {
   return QLS_OK;
 }
 
+// True when every pointer is 16-byte aligned (the kernels load 8 bf16 at a time).
+static bool aligned16(std::initializer_list<const void*> ps) {
+  for (const void* p : ps)
+    if (reinterpret_cast<uintptr_t>(p) % 16) return false;
+  return true;
+}
+
 int qls_attention_fwd(const uint16_t* qkv, int B, int S, int H, int KV, int hd, uint16_t* out, float* lse,
                       void* stream) {
   if (!qkv || !out || !lse) return fail(QLS_EINVAL, "NULL buffer");
+  if (!aligned16({qkv, out, lse})) return fail(QLS_EINVAL, "attention buffers must be 16-byte aligned");
   int rc = attn_check(B, S, H, KV, hd);
   if (rc) return rc;
   AttnArgs a{};
@@ -113,6 +122,8 @@ int qls_attention_fwd(const uint16_t* qkv, int B, int S, int H, int KV, int hd, 
 int qls_attention_bwd(const uint16_t* qkv, const uint16_t* out, const uint16_t* dout, const float* lse, int B,
                       int S, int H, int KV, int hd, float* dq, float* dk, float* dv, void* ws, void* stream) {
   if (!qkv || !out || !dout || !lse || !dq || !dk || !dv || !ws) return fail(QLS_EINVAL, "NULL buffer");
+  if (!aligned16({qkv, out, dout, lse, dq, dk, dv, ws}))
+    return fail(QLS_EINVAL, "attention buffers must be 16-byte aligned");
   int rc = attn_check(B, S, H, KV, hd);
   if (rc) return rc;
   hipStream_t st = (hipStream_t)stream;

@@ -30,8 +30,21 @@ __global__ void __launch_bounds__(TB) rmsnorm_fwd_k(const uint16_t* __restrict__
   const int64_t row = blockIdx.x;
   const u32x4* xr = reinterpret_cast<const u32x4*>(x + row * d);
   const int nc = d / 8;
+  // The first kKeep chunks of each thread stay in registers for the second pass.
+  constexpr int kKeep = 4;
+  u32x4 keep[kKeep];
   float ss = 0.f;
-  for (int c = threadIdx.x; c < nc; c += TB) {
+#pragma unroll
+  for (int i = 0; i < kKeep; ++i) {
+    const int c = threadIdx.x + i * TB;
+    keep[i] = c < nc ? xr[c] : u32x4{0, 0, 0, 0};
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const float a = bflo(keep[i][q]), b = bfhi(keep[i][q]);
+      ss += a * a + b * b;
+    }
+  }
+  for (int c = threadIdx.x + kKeep * TB; c < nc; c += TB) {
     const u32x4 v = xr[c];
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
@@ -43,14 +56,18 @@ __global__ void __launch_bounds__(TB) rmsnorm_fwd_k(const uint16_t* __restrict__
   const float rho = 1.f / sqrtf(tot / (float)d + eps);
   const u32x4* wr = reinterpret_cast<const u32x4*>(w);
   u32x4* yr = reinterpret_cast<u32x4*>(y + row * d);
-  for (int c = threadIdx.x; c < nc; c += TB) {
-    const u32x4 v = xr[c], ww = wr[c];
+  const auto put = [&](int c, const u32x4& v) {
+    const u32x4 ww = wr[c];
     u32x4 o;
 #pragma unroll
     for (int q = 0; q < 4; ++q)
       o[q] = pack2_bf16(bflo(v[q]) * rho * bflo(ww[q]), bfhi(v[q]) * rho * bfhi(ww[q]));
     yr[c] = o;
-  }
+  };
+#pragma unroll
+  for (int i = 0; i < kKeep; ++i)
+    if (threadIdx.x + i * TB < nc) put(threadIdx.x + i * TB, keep[i]);
+  for (int c = threadIdx.x + kKeep * TB; c < nc; c += TB) put(c, xr[c]);
 }
 
 // out = gres + rho (dy*w - xhat * mean(dy*w*xhat)), xhat = rho x.
