@@ -150,6 +150,8 @@ def main():
                     help="store format: double-quantised absmax (112.5 MB per 8B layer, the pages' store) "
                          "or float32 absmax (122.7 MB)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--stream-fence", action="store_true",
+                    help="copy stream waits on slot releases on the device (default: the host waits)")
     ap.add_argument("--optimizer", choices=["adamw", "adamw-separate", "none"], default="adamw",
                     help="update the LoRA vector with AdamW (lr 2e-5, the pages' config) inside every timed step: "
                          "folded into the backward sweep (adamw) or as a separate call after it")
@@ -203,6 +205,8 @@ def main():
     mode = q.QLS_STREAMED if args.mode == "streamed" else q.QLS_RESIDENT
     max_tokens = max(T, 2 * S) if (args.dpo or args.pref) else T
     sess = q.Session(store, emb, lm, fn, max_tokens=max_tokens, max_seq=S, mode=mode, timing=True)
+    if args.stream_fence:
+        sess.debug(q.DBG_STREAM_FENCE)
     print(f"[bench] session ready ({sess.ws_bytes / 1e9:.2f} GB workspace), setup "
           f"{time.perf_counter() - t_setup:.1f} s", file=sys.stderr, flush=True)
 
@@ -274,6 +278,7 @@ def main():
                                 f"per layer) in pinned host memory streamed through 2 device slots, bf16 embedding + "
                                 f"LM head 128256 x 4096 resident, LoRA r64 alpha16 on 7 linears"),
                    "global_batch": B, "seq_len": S, "parallelism": "single GPU", "mode": args.mode,
+                   "slot_fence": "device" if args.stream_fence else "host",
                    "absmax": args.absmax, "disk_layers": args.disk_layers, "optimizer": (None if opt is None else "AdamW lr 2e-5 on the LoRA vector"
                                  + (", folded into the backward sweep" if args.optimizer == "adamw" else ""))},
         "roofline": {"bound": "mfma", "kernel": dom["name"],

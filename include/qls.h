@@ -441,12 +441,16 @@ int qls_session_reset_stats(qls_session* s);
  *                              stream before each layer copy
  *   QLS_DBG_COMPUTE_DELAY      a bounded spin kernel of about delay_us on the
  *                              compute stream before each slot release
- *   QLS_DBG_NO_REUSE           reload every layer even when a slot still holds it */
+ *   QLS_DBG_NO_REUSE           reload every layer even when a slot still holds it
+ *   QLS_DBG_STREAM_FENCE       the copy stream waits on a slot's release on the
+ *                              device; by default the host waits for the
+ *                              release before it enqueues the copy */
 enum {
   QLS_DBG_POISON_ON_RELEASE = 1u,
   QLS_DBG_COPY_DELAY = 2u,
   QLS_DBG_COMPUTE_DELAY = 4u,
-  QLS_DBG_NO_REUSE = 8u
+  QLS_DBG_NO_REUSE = 8u,
+  QLS_DBG_STREAM_FENCE = 16u
 };
 int qls_debug_set(qls_session* s, uint32_t flags, int delay_us);
 

@@ -26,7 +26,7 @@ QLS_PREF_DPO, QLS_PREF_SIMPO, QLS_PREF_ORPO, QLS_PREF_KTO = 0, 1, 2, 3
 PREF_KINDS = {"dpo": QLS_PREF_DPO, "simpo": QLS_PREF_SIMPO, "orpo": QLS_PREF_ORPO, "kto": QLS_PREF_KTO}
 NMOD = 7
 MODULES = ("q", "k", "v", "o", "gate", "up", "down")
-DBG_POISON_ON_RELEASE, DBG_COPY_DELAY, DBG_COMPUTE_DELAY, DBG_NO_REUSE = 1, 2, 4, 8
+DBG_POISON_ON_RELEASE, DBG_COPY_DELAY, DBG_COMPUTE_DELAY, DBG_NO_REUSE, DBG_STREAM_FENCE = 1, 2, 4, 8, 16
 
 
 class QlsError(RuntimeError):

@@ -10,12 +10,21 @@
 // 2L - 2 records; a slot that still holds the layer a prefetch asks for is not
 // copied again (across steps too).
 //
-// Ordering is two-sided with events: the copy stream waits on `released[s]`
-// (recorded on the compute stream after the last kernel that reads slot s)
-// before overwriting the slot, and the compute stream waits on `copied[s]`
+// Ordering is two-sided with events: a slot is overwritten only after
+// `released[s]` (recorded on the compute stream after the last kernel that
+// reads slot s) has completed, and the compute stream waits on `copied[s]`
 // before the first kernel that reads it.  That is the guard against the
 // size-dependent silent wrong-gradient class of bug described on the same page
 // ("Did a correctness bug invalidate the Llama 3.1 8B result?").
+//
+// The release is awaited on the host, which then enqueues the copy: a
+// device-side wait of the copy stream on the compute stream's event delays
+// each copy by 50-80 us on this runtime even when the event completed long
+// before, and the copies are the step's critical path when it is link-bound.
+// To keep the compute stream fed meanwhile, the sweeps request layer l+1
+// after enqueueing layer l (its slot was released by layer l-1), so the host
+// blocks while a whole layer of kernels is queued.  QLS_DBG_STREAM_FENCE
+// restores the device-side wait.
 #include <algorithm>
 #include <chrono>
 #include <cmath>
@@ -222,8 +231,8 @@ void sleep_cb(void* us) {
 }
 
 // ---------------------------------------------------------------- pool
-// Enqueue the copy of `layer` into slot layer & 1 on the copy stream, after
-// the slot's release.  A disk-tier layer is first read into a pinned staging
+// Enqueue the copy of `layer` into slot layer & 1 on the copy stream once the
+// slot's release has completed (blocking this thread until then).  A disk-tier layer is first read into a pinned staging
 // buffer (blocking this thread until the read is done); dir = the sweep's
 // direction, for the reader's read-ahead.
 int prefetch(qls_session* S, int layer, int dir) {
@@ -231,7 +240,8 @@ int prefetch(qls_session* S, int layer, int dir) {
   const int s = layer & 1;
   const bool reuse = !(S->dbg & (QLS_DBG_NO_REUSE | QLS_DBG_POISON_ON_RELEASE));
   if (reuse && S->slot_layer[s] == layer) return QLS_OK;
-  QLS_HIP(hipStreamWaitEvent(S->ps, S->released[s], 0));
+  if (S->dbg & QLS_DBG_STREAM_FENCE) QLS_HIP(hipStreamWaitEvent(S->ps, S->released[s], 0));
+  else QLS_HIP(hipEventSynchronize(S->released[s]));
   if (S->dbg & QLS_DBG_COPY_DELAY)
     QLS_HIP(hipLaunchHostFunc(S->ps, sleep_cb, (void*)(intptr_t)S->delay_us));
   const uint8_t* src = store_record(S->st, layer);
@@ -606,7 +616,7 @@ int forward_sweep(qls_session* S, int T, int B, int Sq, bool lora, bool ref, con
     if (rc) return rc;
     rc = release(S, l, &te);
     if (rc) return rc;
-    if (l + 2 < L && (rc = prefetch(S, l + 2, 1))) return rc;
+    if (l + 1 < L && S->slot_layer[(l + 1) & 1] != l + 1 && (rc = prefetch(S, l + 1, 1))) return rc;
   }
   return QLS_OK;
 }
@@ -630,7 +640,7 @@ int backward_sweep(qls_session* S, int T, int B, int Sq, float* grads) {
     }
     rc = release(S, l, &te);
     if (rc) return rc;
-    if (l - 2 >= 0 && (rc = prefetch(S, l - 2, -1))) return rc;
+    if (l - 1 >= 0 && S->slot_layer[(l - 1) & 1] != l - 1 && (rc = prefetch(S, l - 1, -1))) return rc;
   }
   return QLS_OK;
 }
