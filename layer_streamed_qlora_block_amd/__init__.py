@@ -10,6 +10,11 @@ from __future__ import annotations
 import ctypes as C
 import os
 
+# torch first: its HIP runtime must be the process's one.  Loading libqls.so
+# before torch would bind the system HIP runtime, and torch's own copy would
+# then find no GPU.
+import torch  # noqa: F401
+
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libqls.so")
 
