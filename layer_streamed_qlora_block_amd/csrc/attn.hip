@@ -35,6 +35,12 @@ constexpr int BQ = 64;                 // query rows / keys per block
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
+// 2^x with v_exp_f32 alone.  Every argument here is a logit minus a running
+// maximum or the row's log-sum-exp (<= 0 up to rounding), so a result below
+// 2^-126 is negligible next to the row's other terms and flushes to zero;
+// exp2f would wrap each call in a range-scaling sequence for that case.
+QLS_DEV float fexp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
 QLS_DEV u32x4 pack8(const f32x4& a, const f32x4& b) {
   return u32x4{pack2_bf16(a[0], a[1]), pack2_bf16(a[2], a[3]), pack2_bf16(b[0], b[1]),
                pack2_bf16(b[2], b[3])};
@@ -178,13 +184,13 @@ __global__ void __launch_bounds__(512) attn_fwd_k(AttnArgs a) {
       mloc = fmaxf(mloc, __shfl_xor(mloc, 32, 64));
       const float m_new = fmaxf(m_run[qg], mloc);
       const float m_use = m_new == -INFINITY ? 0.f : m_new;
-      const float alpha = exp2f(m_run[qg] - m_use);
+      const float alpha = fexp2(m_run[qg] - m_use);
       float ls = 0.f;
 #pragma unroll
       for (int j = 0; j < 4; ++j)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const float p = exp2f(sc[qg][j][i] - m_use);
+          const float p = fexp2(sc[qg][j][i] - m_use);
           sc[qg][j][i] = p;
           ls += p;
         }
@@ -339,7 +345,7 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int key = k0 + 16 * j + 4 * g4 + i;
-          const float p = (key <= myq[qg] && key < a.S && myq[qg] < a.S) ? exp2f(sc[qg][j][i] * c - lse2[qg]) : 0.f;
+          const float p = (key <= myq[qg] && key < a.S && myq[qg] < a.S) ? fexp2(sc[qg][j][i] * c - lse2[qg]) : 0.f;
           sc[qg][j][i] = p * (dp[qg][j][i] - Dq[qg]);     // dS (rounded to bf16 below)
         }
       dsf[qg][0] = pack8(sc[qg][0], sc[qg][1]);
@@ -447,6 +453,9 @@ __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2)))
         dp[j] = mfma16(frag<HD>(so, 16 * j + c16, 32 * s + 8 * g4), vf[s], dp[j]);
       }
     }
+    // Scheduling barriers between the phases keep the compiler from hoisting
+    // the next phase's LDS reads across them, which raises register pressure.
+    __builtin_amdgcn_sched_barrier(0);
     // sc[j][i] = S[q = q0 + 16j + 4g4 + i][key = myk]
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -455,11 +464,12 @@ __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2)))
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int q = q0 + 16 * j + 4 * g4 + i;
-        const float p = (myk <= q && q < a.S && myk < a.S) ? exp2f(sc[j][i] * c - l4[i]) : 0.f;
+        const float p = (myk <= q && q < a.S && myk < a.S) ? fexp2(sc[j][i] * c - l4[i]) : 0.f;
         sc[j][i] = p;
         dp[j][i] = p * (dp[j][i] - d4[i]);
       }
     }
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt) {
       const u32x4 pf = pack8(sc[2 * tt], sc[2 * tt + 1]);
@@ -469,6 +479,7 @@ __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2)))
         dv[hb] = mfma16(pf, frag_t<HD>(so, 32 * tt, 16 * hb, g4, c16), dv[hb]);
         dk[hb] = mfma16(dsf, frag_t<HD>(sq, 32 * tt, 16 * hb, g4, c16), dk[hb]);
       }
+      __builtin_amdgcn_sched_barrier(0);
     }
   };
 
