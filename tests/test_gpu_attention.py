@@ -3,7 +3,8 @@ the oracle, through the C ABI (qls_attention_fwd / qls_attention_bwd).
 
 Shapes cover head dims 64 and 128, 1 to 8 query heads per kv head (5 too),
 one and two sequences, lengths that are not multiples of the 32-row and
-64-key blocks, and one length that spans many blocks.  Floating outputs are
+64-key blocks, one length that spans many blocks, and the 8B shape at 4096
+tokens (32 query heads, 8 kv heads).  Floating outputs are
 held to the bar of the step: relative L2 <= 1e-2 and cosine >= 0.999 (the two
 sides round the probabilities to bf16 against different running maxima and
 sum in different orders); the log-sum-exp to 1e-5 relative."""
@@ -18,8 +19,10 @@ from tests.gpu_util import f32, report
 pytestmark = pytest.mark.gpu
 PM = om.Prec("mirror")
 
+# The last shape is the 8B model's attention at 4096 tokens, the launch the
+# seq-4096 step times.
 SHAPES = [(1, 64, 4, 2, 64), (2, 200, 8, 2, 128), (1, 300, 5, 1, 128), (1, 257, 8, 8, 64),
-          (1, 97, 16, 2, 64), (1, 1024, 8, 2, 128)]
+          (1, 97, 16, 2, 64), (1, 1024, 8, 2, 128), (1, 4096, 32, 8, 128)]
 
 
 @pytest.fixture(scope="module")

@@ -72,11 +72,13 @@ def _linear_case(N, K, T, r, seed):
     return codes, absmax, Wd, x, A, B, dy
 
 
-# (N, K, T, r): the 8B MLP shape, ragged shapes (T not a tile multiple,
-# K % 64 != 0 so NF4 blocks straddle rows), and a forward and a dX with at
-# least 256 output tiles of 256 x 256 (the large-tile kernels; ragged in T).
-CASES = [(14336, 4096, 512, 64, 22), (256, 688, 101, 8, 30), (688, 256, 77, 8, 40),
-         (7680, 1024, 2100, 16, 50), (1024, 7680, 2100, 16, 60)]
+# (N, K, T, r): the 8B MLP shape at 512 and at 4096 tokens (the latter in the
+# large-tile launch the seq-4096 step uses: 16 x 56 tiles forward, 16 x 16 dX),
+# ragged shapes (T not a tile multiple, K % 64 != 0 so NF4 blocks straddle
+# rows), and a forward and a dX with at least 256 output tiles of 256 x 256
+# (the large-tile kernels; ragged in T).
+CASES = [(14336, 4096, 512, 64, 22), (14336, 4096, 4096, 64, 80), (256, 688, 101, 8, 30),
+         (688, 256, 77, 8, 40), (7680, 1024, 2100, 16, 50), (1024, 7680, 2100, 16, 60)]
 
 
 @pytest.mark.parametrize("N,K,T,r,seed", CASES)
