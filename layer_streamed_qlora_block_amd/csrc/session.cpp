@@ -5,9 +5,10 @@
 // it held is finished (page "Can You Fine-Tune Llama 3.1 8B on a 4GB GPU?
 // ...", section "How Soup's layer streaming actually works", item 3).  The
 // backward sweep reads the layers again because each layer's forward is
-// recomputed from its checkpointed input (same section, item 4).  The last two
-// layers of the forward sweep are still resident at the turn, so a step loads
-// 2L - 2 records; a slot that still holds the layer a prefetch asks for is not
+// recomputed from its checkpointed input (same section, item 4), except the
+// last layer, whose forward intermediates are still in the workspace at the
+// turn.  The last two layers of the forward sweep are still resident at the
+// turn, so a step loads 2L - 2 records; a slot that still holds the layer a prefetch asks for is not
 // copied again (across steps too).
 //
 // Ordering is two-sided with events: a slot is overwritten only after
@@ -172,6 +173,9 @@ struct qls_session {
   qls_resident res;
   hipEvent_t copied[2] = {}, released[2] = {};
   int slot_layer[2] = {-1, -1};
+  // Layer whose forward intermediates (with adapters) the workspace still
+  // holds: the last layer of a forward sweep, until the backward reaches it.
+  int acts_layer = -1;
   // Double-quantised stores: expansion buffer e = layer & 1 holds the float32
   // absmax of exp_layer[e], decoded from copy number exp_gen[e] of its slot.
   int64_t slot_gen[2] = {0, 0};
@@ -602,6 +606,7 @@ int end_step(qls_session* S, float* h_loss, const float* d_loss) {
 int forward_sweep(qls_session* S, int T, int B, int Sq, bool lora, bool ref, const float* d_lora) {
   const int L = S->sh.c.n_layers;
   uint16_t* xr[2] = {S->at<uint16_t>(S->p.xref0), S->at<uint16_t>(S->p.xref1)};
+  S->acts_layer = -1;
   for (int l = 0; l < L; ++l) {
     const uint8_t* rec;
     TimedEv te{};
@@ -614,6 +619,7 @@ int forward_sweep(qls_session* S, int T, int B, int Sq, bool lora, bool ref, con
     if (lora) cast_lora_layer(S, d_lora, l);
     rc = fwd_layer(S, l, rec, S->ck(l), S->ck(l + 1), lora, T, B, Sq);
     if (rc) return rc;
+    S->acts_layer = lora ? l : -1;
     rc = release(S, l, &te);
     if (rc) return rc;
     if (l + 1 < L && S->slot_layer[(l + 1) & 1] != l + 1 && (rc = prefetch(S, l + 1, 1))) return rc;
@@ -628,8 +634,14 @@ int backward_sweep(qls_session* S, int T, int B, int Sq, float* grads) {
     TimedEv te{};
     int rc = acquire(S, l, &rec, &te);
     if (rc) return rc;
-    rc = fwd_layer(S, l, rec, S->ck(l), S->at<uint16_t>(S->p.xo), true, T, B, Sq);
-    if (rc) return rc;
+    // Recompute the layer's forward from its checkpoint, except for the last
+    // layer at the turn: the forward sweep's intermediates of that layer are
+    // still in the workspace (the same kernels would reproduce them bit for bit).
+    if (l != S->acts_layer) {
+      rc = fwd_layer(S, l, rec, S->ck(l), S->at<uint16_t>(S->p.xo), true, T, B, Sq);
+      if (rc) return rc;
+    }
+    S->acts_layer = -1;
     rc = bwd_layer(S, l, rec, S->ck(l), grads, T, B, Sq);
     if (rc) return rc;
     if (S->opt.on) {
