@@ -174,12 +174,22 @@ __global__ void __launch_bounds__(512) attn_fwd_k(AttnArgs a) {
 #pragma unroll
       for (int j = 0; j < 4; ++j)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int key = k0 + 16 * j + 4 * g4 + i;
-          const float x = (key <= myq[qg] && key < a.S) ? sc[qg][j][i] * c : -INFINITY;
-          sc[qg][j][i] = x;
-          mloc = fmaxf(mloc, x);
-        }
+        for (int i = 0; i < 4; ++i) sc[qg][j][i] *= c;
+      // Only the block that holds the diagonal (the last one) has keys to mask;
+      // every earlier block lies wholly at or below the workgroup's first row.
+      if (k0 + 63 > q0) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int key = k0 + 16 * j + 4 * g4 + i;
+            if (!(key <= myq[qg] && key < a.S)) sc[qg][j][i] = -INFINITY;
+          }
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) mloc = fmaxf(mloc, sc[qg][j][i]);
       mloc = fmaxf(mloc, __shfl_xor(mloc, 16, 64));
       mloc = fmaxf(mloc, __shfl_xor(mloc, 32, 64));
       const float m_new = fmaxf(m_run[qg], mloc);
