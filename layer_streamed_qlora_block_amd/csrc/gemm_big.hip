@@ -2,7 +2,9 @@
 // workgroup, v_mfma_f32_32x32x16_bf16 with fp32 accumulation.
 //
 //   * NT:  Y = X W^T (+ s U_g B_g^T) (+ residual), W NF4 [N, K] (the forward);
-//   * NN:  dX = dY W (+ du_cat A_cat), contraction over W's rows (the backward).
+//   * NN:  dX = dY W (+ du_cat A_cat), contraction over W's rows (the backward);
+//   * bf16 W: the LM head, [N, K] for the logits (cross-entropy epilogues) and
+//     [K, N] for dh = dlogits W (float output, plain or accumulated).
 //
 // Eight waves, two per SIMD, in a 2 x 4 grid; each wave owns 128 x 64 of the
 // tile (4 x 2 MFMA blocks, 128 accumulators per lane), so the other wave on
@@ -68,6 +70,15 @@ template <> struct Stage<B_NF4_NN> { uint32_t q[4]; float s[4]; static constexpr
 // bf16 W[n, k] (the LM head): the weight tile goes to LDS by DMA like the
 // activation tile, in the same swizzled layout; nothing passes through registers.
 template <> struct Stage<B_BF16_NT> { static constexpr int kLoads = 0; };
+// bf16 W[k, n] (dh = dlogits W): the weight tile goes to LDS by DMA as 64
+// row-major rows of 256 columns, and the MFMA reads it column-wise with the
+// transposing ds_read_b64_tr_b16.
+template <> struct Stage<B_BF16_NN> { static constexpr int kLoads = 0; };
+
+// Row-major bf16 weight tile [64 k][256 n]: 16-byte chunk c of row r sits at
+// chunk c ^ 2 (r mod 4), so the four rows a 16-lane transposing read covers
+// (two adjacent chunks each) land in eight distinct 16-byte bank groups.
+QLS_DEV int t_pos(int r, int n) { return r * BN + 8 * ((n >> 3) ^ (2 * (r & 3))) + (n & 7); }
 
 // Wait until at most n vector-memory operations are outstanding and every LDS
 // operation is done (gfx9 s_waitcnt encoding: vmcnt bits 3:0 and 15:14,
@@ -120,6 +131,17 @@ struct Big {
         const int r = 8 * (4 * (t >> 6) + j) + (lane >> 3);
         vdmb[j] = (uint32_t)((r * g.ldb + 8 * ((lane & 7) ^ a_swz(r))) * 2);
       }
+    } else if constexpr (BL == B_BF16_NN) {
+      // W rows k (ldb elements apart), columns n0 .. n0 + 255 (N % 256 == 0).
+      // DMA: wave w, instruction j fills tile rows 2 (4w + j) and +1 (1 KB);
+      // lane l lands in row +l/32, chunk slot l%32, which holds chunk
+      // (l%32) ^ 2 (row mod 4).
+      rb = rsrc(g.Bh + n0, ((int64_t)g.K * g.ldb - n0) * 2);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int r = 2 * (4 * (t >> 6) + j) + (lane >> 5);
+        vdmb[j] = (uint32_t)((r * g.ldb + 8 * ((lane & 31) ^ (2 * (r & 3)))) * 2);
+      }
     } else if constexpr (BL == B_NF4_NT) {
       // W rows n0..: codes row n at n * ldq / 2, absmax at n * ldq / 64.
       rq = rsrc(g.Bq + (int64_t)n0 * g.ldq / 2, (int64_t)(g.N - n0) * g.ldq / 2);
@@ -146,15 +168,16 @@ struct Big {
           (uint32_t)k0 * 2, 0, 0);
   }
   QLS_DEV void dma_b(uint16_t* s, int k0) {
+    // NT: k0 columns along each W row; NN: k0 rows down.
+    const uint32_t soff = BL == B_BF16_NN ? (uint32_t)k0 * (uint32_t)g.ldb * 2u : (uint32_t)k0 * 2u;
 #pragma unroll
     for (int j = 0; j < 4; ++j)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          rb, (__attribute__((address_space(3))) void*)(s + (4 * (t >> 6) + j) * 512), 16, vdmb[j],
-          (uint32_t)k0 * 2, 0, 0);
+          rb, (__attribute__((address_space(3))) void*)(s + (4 * (t >> 6) + j) * 512), 16, vdmb[j], soff, 0, 0);
   }
 
   QLS_DEV void load(Stage<BL>& r, int k0) {
-    if constexpr (BL == B_BF16_NT) {
+    if constexpr (BL == B_BF16_NT || BL == B_BF16_NN) {
       (void)r;
       (void)k0;
     } else if constexpr (BL == B_NF4_NT) {
@@ -172,7 +195,7 @@ struct Big {
   // Dequantise one register stage into weight stage sB.
   QLS_DEV void store(const Stage<BL>& r, uint16_t* sB) const {
     const int row = t >> 1, half = t & 1;
-    if constexpr (BL == B_BF16_NT) {
+    if constexpr (BL == B_BF16_NT || BL == B_BF16_NN) {
       (void)r;
       (void)sB;
       (void)row;
@@ -217,7 +240,20 @@ struct Big {
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
         const int n = wn * 64 + 32 * j + (lane & 31);
-        if constexpr (BL == B_NF4_NN)
+        if constexpr (BL == B_BF16_NN) {
+          // 8 contraction rows kofs .. kofs + 7 of column n: a 16-lane group
+          // reads rows +0..3 and +4..7, columns nb .. nb + 15 (lane i of the
+          // group supplies row i / 4, columns 4 (i % 4) .. + 3).
+          typedef short v4s __attribute__((ext_vector_type(4)));
+          const int nb = wn * 64 + 32 * j + 16 * ((lane >> 4) & 1);
+          const int r = kofs + ((lane & 15) >> 2), c = nb + 4 * (lane & 3);
+          const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (__attribute__((address_space(3))) v4s*)(sB + t_pos(r, c)));
+          const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (__attribute__((address_space(3))) v4s*)(sB + t_pos(r + 4, c)));
+          const u32x2 x = __builtin_bit_cast(u32x2, lo), y = __builtin_bit_cast(u32x2, hi);
+          b[j] = u32x4{x.x, x.y, y.x, y.y};
+        } else if constexpr (BL == B_NF4_NN)
           b[j] = *reinterpret_cast<const u32x4*>(sB + nn_pos(n, kofs));
         else if constexpr (BL == B_BF16_NT)
           b[j] = *reinterpret_cast<const u32x4*>(sB + a_pos(n, kofs));
@@ -315,7 +351,7 @@ struct Big {
   // all but the newest kLoads vector operations before the barrier covers it.
   QLS_DEV void half_step(int kt, int kb, int nk, int cur, Stage<BL>& rld, const Stage<BL>& rst) {
     dma(sA[cur ^ 1], (kb + min(kt + 1, nk - 1)) * BK);
-    if constexpr (BL == B_BF16_NT) dma_b(sB[cur ^ 1], (kb + min(kt + 1, nk - 1)) * BK);
+    if constexpr (BL == B_BF16_NT || BL == B_BF16_NN) dma_b(sB[cur ^ 1], (kb + min(kt + 1, nk - 1)) * BK);
     asm volatile("" ::: "memory");
     load(rld, (kb + min(kt + 2, nk - 1)) * BK);
     mma(sA[cur], sB[cur]);
@@ -331,7 +367,7 @@ struct Big {
     const int nk = ke - kb;
     Stage<BL> r0, r1;
     dma(sA[0], kb * BK);
-    if constexpr (BL == B_BF16_NT) dma_b(sB[0], kb * BK);
+    if constexpr (BL == B_BF16_NT || BL == B_BF16_NN) dma_b(sB[0], kb * BK);
     asm volatile("" ::: "memory");
     load(r0, kb * BK);
     load(r1, (kb + min(1, nk - 1)) * BK);
@@ -453,6 +489,11 @@ struct Big {
             float* c = reinterpret_cast<float*>(C) + (int64_t)m * ldc + n;
             *reinterpret_cast<f32x4*>(c) = f32x4{y[0], y[1], y[2], y[3]};
             *reinterpret_cast<f32x4*>(c + 4) = f32x4{y[4], y[5], y[6], y[7]};
+          } else if constexpr (EPI == EPI_F32_ACC) {
+            float* c = reinterpret_cast<float*>(C) + (int64_t)m * ldc + n;
+            const f32x4 c0 = *reinterpret_cast<const f32x4*>(c), c1 = *reinterpret_cast<const f32x4*>(c + 4);
+            *reinterpret_cast<f32x4*>(c) = f32x4{c0.x + y[0], c0.y + y[1], c0.z + y[2], c0.w + y[3]};
+            *reinterpret_cast<f32x4*>(c + 4) = f32x4{c1.x + y[4], c1.y + y[5], c1.z + y[6], c1.w + y[7]};
           } else if constexpr (EPI == EPI_SWIGLU_BWD) {
             // y = dL/da for a = silu(g) * u: dg = y u silu'(g), du = y silu(g).
             const u32x4 gv = *reinterpret_cast<const u32x4*>(g.gu + (int64_t)m * g.ldgu + n);
@@ -503,7 +544,7 @@ big_kernel(GemmArgs g, const float* __restrict__ cb) {
   // LoRA term goes into slice 0 only, and each slice writes alpha * acc as a
   // float partial that gemm_reduce_epi sums in slice order.
   const int nk = g.K / BK, ks = g.ksplit > 1 ? g.ksplit : 1, z = blockIdx.z;
-  if constexpr (BL != B_BF16_NT)
+  if constexpr (BL == B_NF4_NT || BL == B_NF4_NN)
     if (z == 0 && ((BL == B_NF4_NT && g.lora == LORA_FWD) || (BL == B_NF4_NN && g.lora == LORA_DX))) k.lora();
   if constexpr (EPI == EPI_CE_STATS || EPI == EPI_CE_GRAD) {
     k.mainloop(0, nk);
@@ -538,6 +579,12 @@ bool gemm_big_ok(const GemmArgs& g, int bload, int epi) {
   }
   if (g.ksplit > 1 && (!g.partial || !a16(g.partial) || g.N % 8 || g.ksplit > g.K / BK)) return false;
   if (g.lda % 8 || !a16(g.A) || !fits31((int64_t)g.M * g.lda * 2)) return false;
+  if (bload == B_BF16_NN) {
+    if (epi != EPI_F32 && epi != EPI_F32_ACC) return false;
+    if (g.lora != LORA_NONE || !g.Bh || !a16(g.Bh) || g.ldb % 8 || g.ldb < g.N || g.N % BN) return false;
+    if (!fits31((int64_t)g.K * g.ldb * 2)) return false;
+    return g.C && a16(g.C) && g.ldc % 4 == 0;
+  }
   if (g.ldq % 64 || !g.Bq || !g.Bs || !a16(g.C)) return false;
   if (bload == B_NF4_NT) {
     if (epi != EPI_BF16 || g.N % 8 || g.ldc % 8 || g.ldq < g.K) return false;
@@ -579,6 +626,10 @@ int gemm_big_launch(const GemmArgs& g, int bload, int epi, hipStream_t st) {
     hipLaunchKernelGGL((big_kernel<B_BF16_NT, EPI_CE_STATS>), grid, dim3(NT), 0, st, g, cb);
   else if (bload == B_BF16_NT)
     hipLaunchKernelGGL((big_kernel<B_BF16_NT, EPI_CE_GRAD>), grid, dim3(NT), 0, st, g, cb);
+  else if (bload == B_BF16_NN && epi == EPI_F32)
+    hipLaunchKernelGGL((big_kernel<B_BF16_NN, EPI_F32>), grid, dim3(NT), 0, st, g, cb);
+  else if (bload == B_BF16_NN)
+    hipLaunchKernelGGL((big_kernel<B_BF16_NN, EPI_F32_ACC>), grid, dim3(NT), 0, st, g, cb);
   else if (bload == B_NF4_NT)
     hipLaunchKernelGGL((big_kernel<B_NF4_NT, EPI_BF16>), grid, dim3(NT), 0, st, g, cb);
   else if (epi == EPI_F32)

@@ -554,9 +554,18 @@ int head_bwd(qls_session* S, const uint16_t* xL, int T) {
     h.A = dlog; h.lda = S->z.Vc;
     h.Bh = S->res.d_lm_head + (int64_t)col0 * d; h.ldb = d;
     h.alpha = 1.f; h.C = dhf; h.ldc = d;
-    h.ksplit = big_split(T, d, width);
     h.partial = S->at<float>(S->p.part);
-    QLS_RC(gemm_launch(h, A_ROW, B_BF16_NN, c == 0 ? EPI_F32 : EPI_F32_ACC, kTile, st));
+    const int epi = c == 0 ? EPI_F32 : EPI_F32_ACC;
+    // dh on 256 x 256 tiles when the product fills the GPU (with split-K at
+    // small T), under the same rule as the dequant-GEMMs.
+    const GemmPlan pl = plan_nf4(T, d, width, true);
+    h.ksplit = pl.ksplit;
+    if (pl.big && gemm_big_ok(h, B_BF16_NN, epi)) {
+      QLS_RC(gemm_big_launch(h, B_BF16_NN, epi, st));
+    } else {
+      h.ksplit = big_split(T, d, width);
+      QLS_RC(gemm_launch(h, A_ROW, B_BF16_NN, epi, kTile, st));
+    }
   }
   rmsnorm_bwd(xL, S->res.d_final_norm, sh.c.rms_eps, dhf, nullptr, S->at<float>(S->p.g), nullptr, T, d, st);
   return QLS_OK;

@@ -105,6 +105,30 @@ def test_sft_two_sequences_matches_oracle(q, tiny):
     sess.close()
 
 
+# One 4096-wide layer with a small vocabulary at 4096 tokens: the LM head's
+# dh = dlogits W product (4096 x 4096 outputs, two vocabulary chunks of 1024)
+# runs on the 256 x 256 kernel with the bf16 weight read row-major and
+# transposed in LDS, written by the first chunk and accumulated by the second.
+HEAD_WIDE = synth.ModelCfg(L=1, d=4096, H=8, KV=2, hd=128, I=512, V=2048, eps=1e-5,
+                           theta=500000.0, r=8, alpha=16.0)
+
+
+def test_lm_head_on_large_tiles_matches_oracle(q):
+    cfg = HEAD_WIDE
+    store, model, res = _setup(q, cfg)
+    ids = synth.token_ids(cfg, 1, 4096, seed=23)
+    lora = synth.lora_init(cfg, b_std=0.01)
+    sess = q.Session(store, *res, max_tokens=4096, max_seq=4096, ce_chunk=1024)
+    hl, _, grads = _run_sft(q, sess, cfg, ids, lora)
+    sess.close()
+    print("oracle step at 4096 tokens", flush=True)
+    ol, og, _ = om.sft_step(cfg, PM, model, lora, ids)
+    print(f"loss gpu={hl:.7f} oracle={ol:.7f}", flush=True)
+    assert abs(hl - ol) <= 1e-3 * abs(ol)
+    r, c = report("grads wide head", grads.cpu().numpy(), _flat_oracle_grads(cfg, og))
+    assert r <= 1e-2 and c >= 0.999
+
+
 def test_b_zero_gives_zero_dA(q, tiny):
     cfg, store, model, res = tiny
     sess = q.Session(store, *res, max_tokens=64, max_seq=64)
