@@ -51,8 +51,9 @@ struct GemmArgs {
 int gemm_launch(const GemmArgs& g, int aload, int bload, int epi, int tile, hipStream_t st);
 // Large GEMMs (256 x 256 tiles, 512 threads): B_NF4_NT with EPI_BF16
 // (LORA_FWD allowed), B_NF4_NN with EPI_F32 / EPI_BF16 (no residual) /
-// EPI_SWIGLU_BWD (LORA_DX allowed), and B_BF16_NT with EPI_CE_STATS /
-// EPI_CE_GRAD (statistics per 128-column half, no split); split-K (ksplit > 1) writes
+// EPI_SWIGLU_BWD (LORA_DX allowed), B_BF16_NT with EPI_CE_STATS /
+// EPI_CE_GRAD (statistics per 128-column half, no split), and B_BF16_NN with
+// EPI_F32 / EPI_F32_ACC (N % 256 == 0, no LoRA); split-K (ksplit > 1) writes
 // float partials to g.partial (ksplit * M * N floats) and then runs
 // gemm_reduce_epi.  gemm_big_ok checks the shape and alignment conditions;
 // gemm_big_launch returns -1 when they do not hold.
