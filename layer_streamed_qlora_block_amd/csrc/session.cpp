@@ -397,7 +397,9 @@ int fwd_layer(qls_session* S, int l, const uint8_t* rec, const uint16_t* x, uint
   return QLS_OK;
 }
 
-// g (float [T, d]) holds dL/d(layer output) on entry and dL/d(layer input) on exit.
+// g (float [T, d]) holds dL/d(layer output) on entry and dL/d(layer input) on
+// exit; dyb holds bf16(g) on entry and on exit (the kernel that produces g
+// writes both).
 int bwd_layer(qls_session* S, int l, const uint8_t* rec, const uint16_t* x, float* grads, int T, int B,
               int Sq) {
   const Shape& sh = S->sh;
@@ -424,8 +426,7 @@ int bwd_layer(qls_session* S, int l, const uint8_t* rec, const uint16_t* x, floa
   const uint16_t* uqkv = S->at<uint16_t>(S->p.uqkv);
   const uint16_t* ugu = S->at<uint16_t>(S->p.ugu);
 
-  // ---- down projection + SwiGLU
-  f32_to_bf16(g, dyb, (int64_t)T * d, st);
+  // ---- down projection + SwiGLU (dY = dyb)
   QLS_RC(skinny_du(dyb, d, T, d, lw + S->wb[QLS_DOWN], r, s, du, r, part, st));
   QLS_RC(skinny_dB(dyb, d, T, d, S->at<uint16_t>(S->p.udown), r, s, dB(QLS_DOWN), part, st, r));
   QLS_RC(skinny_dA(du, r, T, r, a, I, I, dA(QLS_DOWN), part, st));
@@ -492,7 +493,7 @@ int bwd_layer(qls_session* S, int l, const uint8_t* rec, const uint16_t* x, floa
   x4.du = du; x4.lddu = 3 * r; x4.Acat = lw + S->wa[QLS_Q]; x4.rc = 3 * r;
   x4.out = dn; x4.ldo = d; x4.epi = EPI_F32; x4.ws = part;
   QLS_RC(S->run_dx(x4, st));
-  rmsnorm_bwd(x, w.na, sh.c.rms_eps, dn, dh, g, nullptr, T, d, st);
+  rmsnorm_bwd(x, w.na, sh.c.rms_eps, dn, dh, g, dyb, T, d, st);
   return QLS_OK;
 }
 
@@ -567,7 +568,8 @@ int head_bwd(qls_session* S, const uint16_t* xL, int T) {
       QLS_RC(gemm_launch(h, A_ROW, B_BF16_NN, epi, kTile, st));
     }
   }
-  rmsnorm_bwd(xL, S->res.d_final_norm, sh.c.rms_eps, dhf, nullptr, S->at<float>(S->p.g), nullptr, T, d, st);
+  rmsnorm_bwd(xL, S->res.d_final_norm, sh.c.rms_eps, dhf, nullptr, S->at<float>(S->p.g), S->at<uint16_t>(S->p.dyb),
+              T, d, st);
   return QLS_OK;
 }
 
@@ -924,6 +926,7 @@ int qls_layer_fwd_bwd(qls_session* S, int layer, const uint16_t* d_x, const uint
   if ((rc = fwd_layer(S, layer, rec, d_x, d_out, true, T, B, Sq))) return rc;
   if ((rc = fwd_layer(S, layer, rec, d_x, S->at<uint16_t>(S->p.xo), true, T, B, Sq))) return rc;
   bf16_to_f32(d_gout, S->at<float>(S->p.g), (int64_t)T * d, S->cs);
+  QLS_HIP(hipMemcpyAsync(S->at<uint16_t>(S->p.dyb), d_gout, (size_t)T * d * 2, hipMemcpyDeviceToDevice, S->cs));
   if ((rc = bwd_layer(S, layer, rec, d_x, d_grads, T, B, Sq))) return rc;
   QLS_HIP(hipMemcpyAsync(d_gin, S->at<float>(S->p.g), (size_t)T * d * 4, hipMemcpyDeviceToDevice, S->cs));
   if ((rc = release(S, layer, &te))) return rc;
