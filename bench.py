@@ -35,7 +35,7 @@ BF16_PEAK_TFLOPS = 2500.0       # MI355X dense bf16 MFMA
 # HBM bytes per launch of a dequant-GEMM kernel, from rocprofv3 FETCH_SIZE /
 # WRITE_SIZE passes scaled by a known-size copy (profiles/hbm_traffic_dequant_gemm_8b.md);
 # valid only for the kernel code they were taken on, keyed by (kernel, sequence length).
-TRAFFIC_BYTES_PER_LAUNCH = {("dq_fwd_256", 512): 160.4e6, ("dq_fwd_256", 4096): 755.6e6}
+TRAFFIC_BYTES_PER_LAUNCH = {("dq_fwd_256", 512): 165.5e6, ("dq_fwd_256", 4096): 755.6e6}
 PCIE_GEN5_X16_GBPS = 64.0       # theoretical per direction
 
 

@@ -56,7 +56,7 @@ int big_split(int M, int N, int K) {
 // One 256 x 256 workgroup (512 threads, ~138 KB of LDS) fills a CU, so a
 // launch of at least 192 of them (one wave over the 256 CUs, >= 75% of them
 // busy) runs the big kernels.  With fewer output tiles the contraction is
-// split into up to 256 / tiles slices of at least 16 steps of 64, partials
+// split into up to 256 / tiles slices of at least 12 steps of 64, partials
 // within kBigPartial; when that still leaves fewer than 192 workgroups the
 // 128 x 128 kernels (several workgroups per CU) take the GEMM.
 GemmPlan plan_nf4(int M, int N, int K, bool can_split) {
@@ -64,7 +64,7 @@ GemmPlan plan_nf4(int M, int N, int K, bool can_split) {
   if (tiles >= 192) return {true, 1};
   if (can_split) {
     const int nk = K / 64;
-    for (int ks = (int)std::min<int64_t>(256 / std::max<int64_t>(tiles, 1), nk / 16); ks >= 2; --ks)
+    for (int ks = (int)std::min<int64_t>(256 / std::max<int64_t>(tiles, 1), nk / 12); ks >= 2; --ks)
       if (tiles * ks >= 192 && (int64_t)M * N * ks <= kBigPartial) return {true, ks};
   }
   return {false, can_split ? big_split(M, N, K) : 1};
