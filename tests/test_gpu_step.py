@@ -268,6 +268,21 @@ def test_bad_token_id_is_reported(q, tiny):
     sess.close()
 
 
+def test_degenerate_sizes_are_refused(q, tiny):
+    """No next-token target (S = 1), more tokens than the workspace holds, and
+    an empty batch are refused before any launch; the session stays usable."""
+    cfg, store, _, res = tiny
+    sess = q.Session(store, *res, max_tokens=64, max_seq=64)
+    lora = synth.lora_init(cfg)
+    for B, S in [(1, 1), (2, 48), (0, 16)]:
+        with pytest.raises(q.QlsError) as e:
+            _run_sft(q, sess, cfg, synth.token_ids(cfg, B, S), lora)
+        assert e.value.code == q.QLS_EINVAL, (B, S)
+    hl, _, grads = _run_sft(q, sess, cfg, synth.token_ids(cfg, 1, 64), lora)
+    assert np.isfinite(hl) and np.all(np.isfinite(grads.cpu().numpy()))
+    sess.close()
+
+
 def test_workspace_too_small_is_rejected(q, tiny):
     cfg, store, _, res = tiny
     run = q.RunCfg(q.QLS_STREAMED, 64, 64, 0, 0)
