@@ -5,9 +5,10 @@
 // it held is finished (page "Can You Fine-Tune Llama 3.1 8B on a 4GB GPU?
 // ...", section "How Soup's layer streaming actually works", item 3).  The
 // backward sweep reads the layers again because each layer's forward is
-// recomputed from its checkpointed input (same section, item 4), except the
-// last layer, whose forward intermediates are still in the workspace at the
-// turn.  The last two layers of the forward sweep are still resident at the
+// recomputed from its checkpointed input (same section, item 4), except at
+// the two ends of the sweep, where the copy engine idles: the last layer's
+// forward intermediates are still in the workspace at the turn, and layer 0's
+// are saved by the forward sweep for the backward that closes the step.  The last two layers of the forward sweep are still resident at the
 // turn, so a step loads 2L - 2 records; a slot that still holds the layer a prefetch asks for is not
 // copied again (across steps too).
 //
@@ -50,6 +51,7 @@ struct Plan {
   int64_t lbf, hf, stats, lse_t, tgt_logit, logp, logp_ref, roww, tgt, ids, dlog, dhf, part;
   int64_t xref0, xref1, scal, rope;
   int64_t amax;   // two float32 absmax expansions (double-quantised stores only)
+  int64_t acts0;  // layer 0's forward intermediates, kept for its backward (the [n1, g) range)
   int64_t total;
 };
 
@@ -122,6 +124,7 @@ Plan make_plan(const Shape& sh, const RecordLayout& lay, const qls_run_cfg& run,
   p.scal = take(64);
   p.rope = take((int64_t)z.Smax * (sh.c.head_dim / 2) * 2 * 4);
   p.amax = take(lay.fmt == QLS_ABSMAX_DQ8 ? 2 * lay.nblocks * 4 : 0);
+  p.acts0 = take(p.g - p.n1);
   p.total = off;
   return p;
 }
@@ -176,6 +179,8 @@ struct qls_session {
   // Layer whose forward intermediates (with adapters) the workspace still
   // holds: the last layer of a forward sweep, until the backward reaches it.
   int acts_layer = -1;
+  // Layer 0's forward intermediates (with adapters) were saved to p.acts0.
+  bool acts0_saved = false;
   // Double-quantised stores: expansion buffer e = layer & 1 holds the float32
   // absmax of exp_layer[e], decoded from copy number exp_gen[e] of its slot.
   int64_t slot_gen[2] = {0, 0};
@@ -618,6 +623,7 @@ int forward_sweep(qls_session* S, int T, int B, int Sq, bool lora, bool ref, con
   const int L = S->sh.c.n_layers;
   uint16_t* xr[2] = {S->at<uint16_t>(S->p.xref0), S->at<uint16_t>(S->p.xref1)};
   S->acts_layer = -1;
+  S->acts0_saved = false;
   for (int l = 0; l < L; ++l) {
     const uint8_t* rec;
     TimedEv te{};
@@ -633,6 +639,14 @@ int forward_sweep(qls_session* S, int T, int B, int Sq, bool lora, bool ref, con
     S->acts_layer = lora ? l : -1;
     rc = release(S, l, &te);
     if (rc) return rc;
+    if (l == 0 && lora && L > 1) {
+      // Keep layer 0's intermediates for its backward, which closes the step
+      // while the copy engine has nothing left to load; ordered after the
+      // slot's release so the next copy is not held back.
+      QLS_HIP(hipMemcpyAsync(S->at<uint8_t>(S->p.acts0), S->at<uint8_t>(S->p.n1), (size_t)(S->p.g - S->p.n1),
+                             hipMemcpyDeviceToDevice, S->cs));
+      S->acts0_saved = true;
+    }
     if (l + 1 < L && S->slot_layer[(l + 1) & 1] != l + 1 && (rc = prefetch(S, l + 1, 1))) return rc;
   }
   return QLS_OK;
@@ -645,14 +659,20 @@ int backward_sweep(qls_session* S, int T, int B, int Sq, float* grads) {
     TimedEv te{};
     int rc = acquire(S, l, &rec, &te);
     if (rc) return rc;
-    // Recompute the layer's forward from its checkpoint, except for the last
-    // layer at the turn: the forward sweep's intermediates of that layer are
-    // still in the workspace (the same kernels would reproduce them bit for bit).
-    if (l != S->acts_layer) {
+    // Recompute the layer's forward from its checkpoint, except at the two
+    // ends of the sweep, where the copy engine idles: the last layer's
+    // intermediates are still in the workspace at the turn, and layer 0's were
+    // saved by the forward sweep (the same kernels would reproduce them bit
+    // for bit).
+    if (l == 0 && S->acts0_saved && l != S->acts_layer) {
+      QLS_HIP(hipMemcpyAsync(S->at<uint8_t>(S->p.n1), S->at<uint8_t>(S->p.acts0), (size_t)(S->p.g - S->p.n1),
+                             hipMemcpyDeviceToDevice, S->cs));
+    } else if (l != S->acts_layer) {
       rc = fwd_layer(S, l, rec, S->ck(l), S->at<uint16_t>(S->p.xo), true, T, B, Sq);
       if (rc) return rc;
     }
     S->acts_layer = -1;
+    if (l == 0) S->acts0_saved = false;
     rc = bwd_layer(S, l, rec, S->ck(l), grads, T, B, Sq);
     if (rc) return rc;
     if (S->opt.on) {
