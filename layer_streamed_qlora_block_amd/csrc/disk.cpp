@@ -13,7 +13,10 @@
 
 namespace {
 
-constexpr int kReadParts = 4;   // concurrent preads per record
+// preads per record, run concurrently.  One sequential read of the record is
+// the fastest on the virtual disks measured (6.4 GB/s; 2 parts 5.6, 4 parts
+// 4.8, 8 parts 3.5, 16 parts 2.4).
+constexpr int kReadParts = 1;
 
 int64_t round_up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
 

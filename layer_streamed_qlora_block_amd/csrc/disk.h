@@ -20,9 +20,9 @@ constexpr int64_t kDiskAlign = 4096;
 
 // Reads are buffered preads straight into the pinned staging buffers (direct
 // I/O cannot target driver-mapped pinned pages: the kernel refuses to pin them
-// again), split over a few threads, and each record's pages are dropped from
-// the page cache after the read, so every read of a disk layer comes from the
-// device rather than from host memory.
+// again), and each record's pages are dropped from the page cache after the
+// read, so every read of a disk layer comes from the device rather than from
+// host memory.
 
 class DiskFile {
  public:
