@@ -440,7 +440,9 @@ int qls_session_reset_stats(qls_session* s);
  *   QLS_DBG_COPY_DELAY         a host callback sleeping delay_us on the copy
  *                              stream before each layer copy
  *   QLS_DBG_COMPUTE_DELAY      a bounded spin kernel of about delay_us on the
- *                              compute stream before each slot release
+ *                              compute stream before each slot release and
+ *                              after each release of a code part (q|k|v, o,
+ *                              gate|up, down) of a slot
  *   QLS_DBG_NO_REUSE           reload every layer even when a slot still holds it
  *   QLS_DBG_STREAM_FENCE       the copy stream waits on a slot's release on the
  *                              device; by default the host waits for the

@@ -27,6 +27,19 @@
 // after enqueueing layer l (its slot was released by layer l-1), so the host
 // blocks while a whole layer of kernels is queued.  QLS_DBG_STREAM_FENCE
 // restores the device-side wait.
+//
+// The first copy of each sweep (layer 2 going forward, layer L-3 going
+// backward) would wait for a layer that holds a pinned slot while the copy
+// engine idles: layer 0's forward at the start of a step, the last layer's
+// backward at the turn.  That copy goes in five parts: the q|k|v, o, gate|up
+// and down codes and the rest (absmax data and norms).  The layer's kernels
+// stop reading the code parts one after another (in module order going
+// forward, in reverse order in the backward), each part has its own release
+// event, recorded after the last product that reads it, and the copy takes
+// the parts in that order, each after its own event, the rest after
+// `released[s]`; it so starts with the layer's first product instead of after
+// its last kernel.  Every other copy is one transfer after `released[s]`
+// (each extra transfer costs the link some throughput).
 #include <algorithm>
 #include <chrono>
 #include <cmath>
@@ -44,6 +57,11 @@
 namespace {
 
 constexpr int kTile = 128;
+
+// Parts of a layer record, in the order of its bytes: the q|k|v, o, gate|up
+// and down code blobs, then the rest (absmax data, norms).
+enum { PART_QKV = 0, PART_O, PART_GU, PART_DOWN, PART_REST };
+constexpr unsigned kAllParts = (1u << PART_REST) - 1;
 
 struct Plan {
   int64_t slots, ckpt, n1, qkv, attn, lse, Dv, h, n2, gu, a, uqkv, uo, ugu, udown;
@@ -175,6 +193,11 @@ struct qls_session {
   hipStream_t cs = nullptr, ps = nullptr;
   qls_resident res;
   hipEvent_t copied[2] = {}, released[2] = {};
+  // Release of each code part of a slot (PART_*); `marked[s]` has bit p set
+  // once the current use of slot s has recorded part p's event.
+  hipEvent_t part_rel[2][PART_REST] = {};
+  unsigned marked[2] = {0, 0};
+  bool parts_next = false;   // the next copy goes in parts (set at the start of a sweep)
   int slot_layer[2] = {-1, -1};
   // Layer whose forward intermediates (with adapters) the workspace still
   // holds: the last layer of a forward sweep, until the backward reaches it.
@@ -216,6 +239,25 @@ struct qls_session {
     return rc;
   }
 
+  // The product just enqueued on the compute stream was the last reader of
+  // code part `part` of layer l's slot in this use of it.
+  int mark(int l, int part) {
+    if (run.mode == QLS_RESIDENT) return QLS_OK;
+    QLS_HIP(hipEventRecord(part_rel[l & 1][part], cs));
+    marked[l & 1] |= 1u << part;
+    // Test hook: hold back the kernels after the release so that a copy into
+    // a part that is still read later would land first.
+    if (dbg & QLS_DBG_COMPUTE_DELAY) spin_delay((int64_t)delay_us * wall_khz / 1000, cs);
+    return QLS_OK;
+  }
+  // Byte range [*a, *b) of part `part` of a record.
+  void part_range(int part, int64_t* a, int64_t* b) const {
+    static const int first[PART_REST + 1] = {QLS_Q, QLS_O, QLS_GATE, QLS_DOWN, -1};
+    const int64_t codes_end = lay.code_off[QLS_DOWN] + sh.numel[QLS_DOWN] / 2;
+    *a = part == PART_REST ? codes_end : lay.code_off[first[part]];
+    *b = part == PART_DOWN ? codes_end : part == PART_REST ? lay.bytes : lay.code_off[first[part + 1]];
+  }
+
   template <class T> T* at(int64_t off) const { return reinterpret_cast<T*>(ws + off); }
   float* amax_buf(int l) const { return at<float>(p.amax) + (int64_t)(l & 1) * lay.nblocks; }
   uint16_t* ck(int l) const { return at<uint16_t>(p.ckpt) + (int64_t)l * z.Tm * sh.c.hidden; }
@@ -241,29 +283,45 @@ void sleep_cb(void* us) {
 
 // ---------------------------------------------------------------- pool
 // Enqueue the copy of `layer` into slot layer & 1 on the copy stream once the
-// slot's release has completed (blocking this thread until then).  A disk-tier layer is first read into a pinned staging
+// slot's release has completed, or part by part, each once its own release
+// has completed, for the first copy of a sweep (blocking this thread until
+// then).  A disk-tier layer is first read into a pinned staging
 // buffer (blocking this thread until the read is done); dir = the sweep's
-// direction, for the reader's read-ahead.
+// direction: the order in which its layers free the code parts, and the
+// reader's read-ahead.
 int prefetch(qls_session* S, int layer, int dir) {
   if (S->run.mode == QLS_RESIDENT) return QLS_OK;
   const int s = layer & 1;
   const bool reuse = !(S->dbg & (QLS_DBG_NO_REUSE | QLS_DBG_POISON_ON_RELEASE));
   if (reuse && S->slot_layer[s] == layer) return QLS_OK;
-  if (S->dbg & QLS_DBG_STREAM_FENCE) QLS_HIP(hipStreamWaitEvent(S->ps, S->released[s], 0));
-  else QLS_HIP(hipEventSynchronize(S->released[s]));
-  if (S->dbg & QLS_DBG_COPY_DELAY)
-    QLS_HIP(hipLaunchHostFunc(S->ps, sleep_cb, (void*)(intptr_t)S->delay_us));
+  const bool parts = S->parts_next;
+  S->parts_next = false;
   const uint8_t* src = store_record(S->st, layer);
   int buf = -1;
   if (layer >= S->ram_layers) {
     src = S->disk->take(layer, dir, &buf);
     if (!src) return fail(QLS_EIO, S->disk->error());
   }
-  TimedEv te{};
-  if (S->timing) { te.a = S->next_ev(); te.b = S->next_ev(); QLS_HIP(hipEventRecord(te.a, S->ps)); }
-  QLS_HIP(hipMemcpyAsync(S->at<uint8_t>(S->p.slots) + s * S->lay.bytes, src, S->lay.bytes,
-                         hipMemcpyHostToDevice, S->ps));
-  if (S->timing) { QLS_HIP(hipEventRecord(te.b, S->ps)); S->copy_ev.push_back(te); }
+  uint8_t* dst = S->at<uint8_t>(S->p.slots) + s * S->lay.bytes;
+  static const int fwd_order[PART_REST + 1] = {PART_QKV, PART_O, PART_GU, PART_DOWN, PART_REST};
+  static const int bwd_order[PART_REST + 1] = {PART_DOWN, PART_GU, PART_O, PART_QKV, PART_REST};
+  // The device-side fence waits once, for the whole slot (`released[s]` is
+  // recorded after every part's event).
+  if (S->dbg & QLS_DBG_STREAM_FENCE) QLS_HIP(hipStreamWaitEvent(S->ps, S->released[s], 0));
+  for (int i = parts ? 0 : PART_REST; i <= PART_REST; ++i) {
+    const int part = dir >= 0 ? fwd_order[i] : bwd_order[i];
+    if (!(S->dbg & QLS_DBG_STREAM_FENCE))
+      QLS_HIP(hipEventSynchronize(part == PART_REST ? S->released[s] : S->part_rel[s][part]));
+    if ((i == 0 || !parts) && (S->dbg & QLS_DBG_COPY_DELAY))
+      QLS_HIP(hipLaunchHostFunc(S->ps, sleep_cb, (void*)(intptr_t)S->delay_us));
+    int64_t a = 0, b = S->lay.bytes;
+    if (parts) S->part_range(part, &a, &b);
+    if (b <= a) continue;
+    TimedEv te{};
+    if (S->timing) { te.a = S->next_ev(); te.b = S->next_ev(); QLS_HIP(hipEventRecord(te.a, S->ps)); }
+    QLS_HIP(hipMemcpyAsync(dst + a, src + a, (size_t)(b - a), hipMemcpyHostToDevice, S->ps));
+    if (S->timing) { QLS_HIP(hipEventRecord(te.b, S->ps)); S->copy_ev.push_back(te); }
+  }
   if (buf >= 0 && S->disk->after_copy(buf, S->ps)) return fail(QLS_EHIP, "hipEventRecord failed");
   QLS_HIP(hipEventRecord(S->copied[s], S->ps));
   S->slot_layer[s] = layer;
@@ -284,6 +342,7 @@ int acquire(qls_session* S, int layer, const uint8_t** rec, TimedEv* te) {
     }
     QLS_HIP(hipStreamWaitEvent(S->cs, S->copied[s], 0));
     *rec = S->at<uint8_t>(S->p.slots) + s * S->lay.bytes;
+    S->marked[s] = 0;
   }
   if (S->lay.fmt == QLS_ABSMAX_DQ8) {
     // Decode the 8-bit absmax of this record once per arrival, on the compute
@@ -306,6 +365,10 @@ int release(qls_session* S, int layer, TimedEv* te) {
   if (S->timing) { QLS_HIP(hipEventRecord(te->b, S->cs)); S->comp_ev.push_back(*te); }
   if (S->run.mode == QLS_RESIDENT) return QLS_OK;
   const int s = layer & 1;
+  // Parts this use did not mark are released with the rest.
+  for (int part = 0; part < PART_REST; ++part)
+    if (!(S->marked[s] >> part & 1)) QLS_HIP(hipEventRecord(S->part_rel[s][part], S->cs));
+  S->marked[s] = kAllParts;
   QLS_HIP(hipEventRecord(S->released[s], S->cs));
   if (S->dbg & QLS_DBG_POISON_ON_RELEASE) {
     QLS_HIP(hipStreamWaitEvent(S->ps, S->released[s], 0));
@@ -365,6 +428,7 @@ int fwd_layer(qls_session* S, int l, const uint8_t* rec, const uint16_t* x, uint
   f.Bm[0] = lw + S->wb[QLS_Q]; f.Bm[1] = lw + S->wb[QLS_K]; f.Bm[2] = lw + S->wb[QLS_V];
   f.s = sh.s; f.y = qkv; f.ldy = sh.nqkv; f.u = S->at<uint16_t>(S->p.uqkv); f.ws = part;
   QLS_RC(S->run_fwd(f, lora, st));
+  QLS_RC(S->mark(l, PART_QKV));
   rope_fwd(qkv, sh.nqkv, T, Sq, sh.c.n_heads, sh.c.n_kv_heads, sh.c.head_dim, S->at<float>(S->p.rope), st);
   AttnArgs aa{};
   aa.qkv = qkv; aa.ld = sh.nqkv; aa.q_off = 0; aa.k_off = sh.qd; aa.v_off = sh.qd + sh.kvd;
@@ -380,6 +444,7 @@ int fwd_layer(qls_session* S, int l, const uint8_t* rec, const uint16_t* x, uint
   f.nmod = 1; f.mod_end[0] = d; f.Bm[0] = lw + S->wb[QLS_O];
   f.s = sh.s; f.res = x; f.ldres = d; f.y = h; f.ldy = d; f.u = S->at<uint16_t>(S->p.uo); f.ws = part;
   QLS_RC(S->run_fwd(f, lora, st));
+  QLS_RC(S->mark(l, PART_O));
 
   rmsnorm_fwd(h, w.nm, sh.c.rms_eps, n2, T, d, st);
   f = LinearFwd{};
@@ -390,6 +455,7 @@ int fwd_layer(qls_session* S, int l, const uint8_t* rec, const uint16_t* x, uint
   f.Bm[0] = lw + S->wb[QLS_GATE]; f.Bm[1] = lw + S->wb[QLS_UP];
   f.s = sh.s; f.y = gu; f.ldy = 2 * I; f.u = S->at<uint16_t>(S->p.ugu); f.ws = part;
   QLS_RC(S->run_fwd(f, lora, st));
+  QLS_RC(S->mark(l, PART_GU));
   swiglu_fwd(gu, a, T, I, st);
 
   f = LinearFwd{};
@@ -399,7 +465,7 @@ int fwd_layer(qls_session* S, int l, const uint8_t* rec, const uint16_t* x, uint
   f.nmod = 1; f.mod_end[0] = d; f.Bm[0] = lw + S->wb[QLS_DOWN];
   f.s = sh.s; f.res = h; f.ldres = d; f.y = xout; f.ldy = d; f.u = S->at<uint16_t>(S->p.udown); f.ws = part;
   QLS_RC(S->run_fwd(f, lora, st));
-  return QLS_OK;
+  return S->mark(l, PART_DOWN);
 }
 
 // g (float [T, d]) holds dL/d(layer output) on entry and dL/d(layer input) on
@@ -442,6 +508,7 @@ int bwd_layer(qls_session* S, int l, const uint8_t* rec, const uint16_t* x, floa
   x1.out = dgu; x1.ldo = 2 * I; x1.epi = EPI_SWIGLU_BWD; x1.ws = part;
   x1.gu = S->at<uint16_t>(S->p.gu); x1.ldgu = 2 * I; x1.I = I;
   QLS_RC(S->run_dx(x1, st));
+  QLS_RC(S->mark(l, PART_DOWN));
 
   // ---- gate / up
   for (int k = 0; k < 2; ++k) {
@@ -456,6 +523,7 @@ int bwd_layer(qls_session* S, int l, const uint8_t* rec, const uint16_t* x, floa
   x2.du = du; x2.lddu = 2 * r; x2.Acat = lw + S->wa[QLS_GATE]; x2.rc = 2 * r;
   x2.out = dn; x2.ldo = d; x2.epi = EPI_F32; x2.ws = part;
   QLS_RC(S->run_dx(x2, st));
+  QLS_RC(S->mark(l, PART_GU));
   rmsnorm_bwd(h, w.nm, sh.c.rms_eps, dn, g, dh, dyb, T, d, st);
 
   // ---- o projection
@@ -468,6 +536,7 @@ int bwd_layer(qls_session* S, int l, const uint8_t* rec, const uint16_t* x, floa
   x3.du = du; x3.lddu = r; x3.Acat = lw + S->wa[QLS_O]; x3.rc = r;
   x3.out = S->at<uint16_t>(S->p.dattn); x3.ldo = sh.qd; x3.epi = EPI_BF16; x3.ws = part;
   QLS_RC(S->run_dx(x3, st));
+  QLS_RC(S->mark(l, PART_O));
 
   // ---- attention + RoPE
   AttnBwdArgs ab{};
@@ -498,6 +567,7 @@ int bwd_layer(qls_session* S, int l, const uint8_t* rec, const uint16_t* x, floa
   x4.du = du; x4.lddu = 3 * r; x4.Acat = lw + S->wa[QLS_Q]; x4.rc = 3 * r;
   x4.out = dn; x4.ldo = d; x4.epi = EPI_F32; x4.ws = part;
   QLS_RC(S->run_dx(x4, st));
+  QLS_RC(S->mark(l, PART_QKV));
   rmsnorm_bwd(x, w.na, sh.c.rms_eps, dn, dh, g, dyb, T, d, st);
   return QLS_OK;
 }
@@ -624,6 +694,7 @@ int forward_sweep(qls_session* S, int T, int B, int Sq, bool lora, bool ref, con
   uint16_t* xr[2] = {S->at<uint16_t>(S->p.xref0), S->at<uint16_t>(S->p.xref1)};
   S->acts_layer = -1;
   S->acts0_saved = false;
+  S->parts_next = true;
   for (int l = 0; l < L; ++l) {
     const uint8_t* rec;
     TimedEv te{};
@@ -649,11 +720,13 @@ int forward_sweep(qls_session* S, int T, int B, int Sq, bool lora, bool ref, con
     }
     if (l + 1 < L && S->slot_layer[(l + 1) & 1] != l + 1 && (rc = prefetch(S, l + 1, 1))) return rc;
   }
+  S->parts_next = false;
   return QLS_OK;
 }
 
 int backward_sweep(qls_session* S, int T, int B, int Sq, float* grads) {
   const int L = S->sh.c.n_layers;
+  S->parts_next = true;
   for (int l = L - 1; l >= 0; --l) {
     const uint8_t* rec;
     TimedEv te{};
@@ -685,6 +758,7 @@ int backward_sweep(qls_session* S, int T, int B, int Sq, float* grads) {
     if (rc) return rc;
     if (l - 1 >= 0 && S->slot_layer[(l - 1) & 1] != l - 1 && (rc = prefetch(S, l - 1, -1))) return rc;
   }
+  S->parts_next = false;
   return QLS_OK;
 }
 
@@ -769,6 +843,10 @@ int qls_session_create(const qls_store* st, const qls_run_cfg* run, void* d_ws, 
       return cleanup(fail(QLS_EHIP, "hipEventCreate failed"));
     if (hipEventRecord(S->released[i], S->cs) != hipSuccess)
       return cleanup(fail(QLS_EHIP, "hipEventRecord failed"));
+    for (int part = 0; part < PART_REST; ++part)
+      if (hipEventCreateWithFlags(&S->part_rel[i][part], hipEventDisableTiming) != hipSuccess ||
+          hipEventRecord(S->part_rel[i][part], S->cs) != hipSuccess)
+        return cleanup(fail(QLS_EHIP, "hipEventCreate failed"));
   }
   std::vector<float> tab;
   fill_rope_table(sh, run->max_seq, &tab);
@@ -814,6 +892,8 @@ void qls_session_destroy(qls_session* S) {
   for (int i = 0; i < 2; ++i) {
     if (S->copied[i]) (void)hipEventDestroy(S->copied[i]);
     if (S->released[i]) (void)hipEventDestroy(S->released[i]);
+    for (auto e : S->part_rel[i])
+      if (e) (void)hipEventDestroy(e);
   }
   for (auto e : S->ev_pool) (void)hipEventDestroy(e);
   delete S;

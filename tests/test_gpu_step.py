@@ -160,16 +160,18 @@ def test_streamed_equals_resident_bitwise(q, deep):
     for name, mode, flags in [("resident", q.QLS_RESIDENT, 0), ("streamed", q.QLS_STREAMED, 0),
                               ("poison", q.QLS_STREAMED, q.DBG_POISON_ON_RELEASE),
                               ("delays", q.QLS_STREAMED, q.DBG_COPY_DELAY | q.DBG_COMPUTE_DELAY),
+                              ("compute-delay", q.QLS_STREAMED, q.DBG_COMPUTE_DELAY),
                               ("stream-fence", q.QLS_STREAMED, q.DBG_STREAM_FENCE),
                               ("stream-fence-delays", q.QLS_STREAMED,
                                q.DBG_STREAM_FENCE | q.DBG_COPY_DELAY | q.DBG_COMPUTE_DELAY)]:
         print(f"run {name}", flush=True)
         sess = q.Session(store, *res, max_tokens=64, max_seq=64, mode=mode)
-        sess.debug(flags, 2000 if flags & q.DBG_COPY_DELAY else 0)
-        hl, loss, grads = _run_sft(q, sess, cfg, ids, lora)
+        sess.debug(flags, 2000 if flags & (q.DBG_COPY_DELAY | q.DBG_COMPUTE_DELAY) else 0)
+        for _ in range(2):                        # the second step starts with layers 0 and 1 resident
+            hl, loss, grads = _run_sft(q, sess, cfg, ids, lora)
         out[name] = (bits(loss), bits(grads), bits(sess.checkpoints(64)))
         sess.close()
-    for name in ("streamed", "poison", "delays", "stream-fence", "stream-fence-delays"):
+    for name in ("streamed", "poison", "delays", "compute-delay", "stream-fence", "stream-fence-delays"):
         assert np.array_equal(out[name][0], out["resident"][0]), name           # loss
         assert np.array_equal(out[name][2], out["resident"][2]), name           # forward question
         assert np.array_equal(out[name][1], out["resident"][1]), name           # gradient question
