@@ -84,8 +84,11 @@ typedef struct qls_model_cfg {
 
 /* Per-session run configuration.
  *   mode        QLS_STREAMED: two device slots, layers copied host->device
- *               on a copy stream one layer ahead; QLS_RESIDENT: the whole
- *               store is copied to the device once at session creation.
+ *               on a copy stream one layer ahead, each copy after the slot's
+ *               previous layer has released it (the first copy of a sweep
+ *               part by part, each code blob after its last reader);
+ *               QLS_RESIDENT: the whole store is copied to the device once
+ *               at session creation.
  *   max_tokens  upper bound on B*S of any call (DPO uses 2*S).
  *   max_seq     upper bound on S.
  *   ce_chunk    vocabulary columns per cross-entropy chunk (0 = 32768;
