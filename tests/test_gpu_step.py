@@ -178,6 +178,34 @@ def test_streamed_equals_resident_bitwise(q, deep):
     assert np.all(np.isfinite(out["resident"][1].view(np.float32)))
 
 
+def test_dpo_streamed_equals_resident_bitwise(q, deep):
+    """The fused reference pass reads every resident layer twice before the
+    slot's code parts are released; the first copy of each sweep then goes in
+    parts (on 6 layers: layer 2 forward, layer 3 backward)."""
+    cfg, store, _, res = deep
+    c, r = synth.dpo_pair(cfg, 64, 16)
+    c, r = torch.from_numpy(c).cuda(), torch.from_numpy(r).cuda()
+    d_lora = torch.from_numpy(synth.pack_lora(cfg, synth.lora_init(cfg, b_std=0.01))).cuda()
+    out = {}
+    for name, mode, flags in [("resident", q.QLS_RESIDENT, 0), ("streamed", q.QLS_STREAMED, 0),
+                              ("compute-delay", q.QLS_STREAMED, q.DBG_COMPUTE_DELAY),
+                              ("poison", q.QLS_STREAMED, q.DBG_POISON_ON_RELEASE)]:
+        print(f"dpo run {name}", flush=True)
+        sess = q.Session(store, *res, max_tokens=128, max_seq=64, mode=mode)
+        sess.debug(flags, 2000 if flags & q.DBG_COMPUTE_DELAY else 0)
+        grads = torch.full_like(d_lora, float("nan"))
+        loss = torch.empty(1, dtype=torch.float32, device="cuda")
+        for _ in range(2):
+            sess.dpo_step(c, r, 16, 0.1, d_lora, grads, loss)
+        torch.cuda.synchronize()
+        out[name] = (bits(loss), bits(grads))
+        sess.close()
+    for name in ("streamed", "compute-delay", "poison"):
+        assert np.array_equal(out[name][0], out["resident"][0]), name
+        assert np.array_equal(out[name][1], out["resident"][1]), name
+    assert np.all(np.isfinite(out["resident"][1].view(np.float32)))
+
+
 def test_layer_load_counts(q, deep):
     cfg, store, _, res = deep
     L = cfg.L
