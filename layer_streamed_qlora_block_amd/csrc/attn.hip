@@ -102,6 +102,16 @@ QLS_DEV u32x4 frag_t(const uint16_t* tile, int k0, int col0, int g4, int c16) {
   return u32x4{x.x, x.y, y.x, y.y};
 }
 
+// Work order over the grid's x (rank: 0 = the most key / query blocks to
+// walk) and y (heads): workgroups are dispatched in linear (x, y) order, so
+// rank r of every head goes before rank r + 1 of any, and the longest
+// workgroups start first instead of those of the last heads starting last.
+QLS_DEV void rank_major(int* rank, int* y) {
+  const int id = (int)(blockIdx.x + gridDim.x * blockIdx.y);
+  *rank = id / (int)gridDim.y;
+  *y = id % (int)gridDim.y;
+}
+
 QLS_DEV void wait_dma() {
   __builtin_amdgcn_s_waitcnt(0 | (7 << 4) | (0 << 8) | (0 << 14));   // vmcnt(0) lgkmcnt(0)
   asm volatile("" ::: "memory");
@@ -122,8 +132,10 @@ __global__ void __launch_bounds__(512) attn_fwd_k(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t sV1[64 * HD];
   const int G = a.H / a.KV;
   const int nqb = (a.S + 31) / 32;
-  const int qb = nqb - 1 - (int)blockIdx.x;       // long rows first
-  const int g = blockIdx.y, b = blockIdx.z;
+  int rank, g;
+  rank_major(&rank, &g);
+  const int qb = nqb - 1 - rank;                  // long rows first
+  const int b = blockIdx.z;
   const int t = threadIdx.x, lane = t & 63, w = t >> 6, g4 = lane >> 4, c16 = lane & 15;
   const int h = g * G + w;
   const int q0 = qb * 32;
@@ -292,8 +304,10 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))
   __shared__ __attribute__((aligned(16))) uint16_t sV1[64 * HD];
   const int G = a.H / a.KV;
   const int nqb = (a.S + 31) / 32;
-  const int qb = nqb - 1 - (int)blockIdx.x;
-  const int g = blockIdx.y, b = blockIdx.z;
+  int rank, g;
+  rank_major(&rank, &g);
+  const int qb = nqb - 1 - rank;                  // long rows first
+  const int b = blockIdx.z;
   const int t = threadIdx.x, lane = t & 63, w = t >> 6, g4 = lane >> 4, c16 = lane & 15;
   const int h = g * G + w;
   const int q0 = qb * 32;
@@ -415,8 +429,9 @@ __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2)))
   __shared__ __attribute__((aligned(16))) float sL[2][64];
   __shared__ __attribute__((aligned(16))) float sD[2][64];
   const int nqb = (a.S + BQ - 1) / BQ;
-  const int kb = (int)blockIdx.x;
-  const int h = blockIdx.y, b = blockIdx.z;
+  int kb, h;
+  rank_major(&kb, &h);                            // key block 0 walks the most query blocks
+  const int b = blockIdx.z;
   const int g = h / (a.H / a.KV);
   const int t = threadIdx.x, lane = t & 63, w = t >> 6, g4 = lane >> 4, c16 = lane & 15;
   const int k0 = kb * BQ;
