@@ -62,6 +62,10 @@ int gemm_big_launch(const GemmArgs& g, int bload, int epi, hipStream_t st);
 // out = epilogue(sum_z partial[z]) for split-K: mode 0 -> bf16 alpha*sum, 1 -> f32 alpha*sum.
 void gemm_reduce(const float* partial, int ksplit, int M, int N, float alpha, int mode,
                  void* C, int64_t ldc, hipStream_t st);
+// gemm_reduce with mode 1 (float), row block i (rows i*rows .. +rows-1 of the
+// M x N sum) written to C[i] (ldc); M / rows <= 4 blocks, else -1.
+int gemm_reduce_rows(const float* partial, int ksplit, int M, int N, float alpha, float* const* C, int rows,
+                     int64_t ldc, hipStream_t st);
 int64_t gemm_partial_elems(int M, int N, int ksplit);
 // Sums the ksplit partials of g (in split order) and applies epilogue epi to g.C
 // (N % 4 == 0).

@@ -706,6 +706,20 @@ __global__ void reduce_kernel(const float* __restrict__ P, int ks, int M, int N,
   else reinterpret_cast<float*>(C)[(int64_t)m * ldc + n] = alpha * s;
 }
 
+// reduce_kernel's sum (fp32 output), with row block m / rows of the product
+// going to its own matrix: C[m / rows], row m % rows.
+struct RowBlocks { float* c[4]; int rows; };
+__global__ void reduce_rows_kernel(const float* __restrict__ P, int ks, int M, int N, float alpha,
+                                   RowBlocks o, int64_t ldc) {
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t MN = (int64_t)M * N;
+  if (idx >= MN) return;
+  const int m = (int)(idx / N), n = (int)(idx % N);
+  float s = 0.f;
+  for (int z = 0; z < ks; ++z) s += P[z * MN + idx];
+  o.c[m / o.rows][(int64_t)(m % o.rows) * ldc + n] = alpha * s;
+}
+
 // Sum of the split-K partials in split order, then the GEMM's own epilogue;
 // four consecutive columns per thread (N % 4 == 0).
 __global__ void reduce_epi_kernel(GemmArgs g, int epi) {
@@ -811,6 +825,18 @@ void gemm_reduce(const float* partial, int ksplit, int M, int N, float alpha, in
   const int64_t MN = (int64_t)M * N;
   hipLaunchKernelGGL(reduce_kernel, dim3((unsigned)ceil_div64(MN, 256)), dim3(256), 0, st, partial,
                      ksplit, M, N, alpha, mode, C, ldc);
+}
+
+int gemm_reduce_rows(const float* partial, int ksplit, int M, int N, float alpha, float* const* C, int rows,
+                     int64_t ldc, hipStream_t st) {
+  RowBlocks o{};
+  if (rows <= 0 || M % rows || M / rows > 4) return -1;
+  for (int i = 0; i < M / rows; ++i) o.c[i] = C[i];
+  o.rows = rows;
+  const int64_t MN = (int64_t)M * N;
+  hipLaunchKernelGGL(reduce_rows_kernel, dim3((unsigned)ceil_div64(MN, 256)), dim3(256), 0, st, partial,
+                     ksplit, M, N, alpha, o, ldc);
+  return 0;
 }
 
 int64_t gemm_partial_elems(int M, int N, int ksplit) { return (int64_t)M * N * ksplit; }

@@ -101,6 +101,19 @@ int skinny_dA(const uint16_t* du, int64_t lddu, int T, int r, const uint16_t* x,
   return skinny(A_COL, du, lddu, B_BF16_NN, x, ldx, r, K, T, 1.f, 1, dA, K, part, st);
 }
 
+int skinny_dA_multi(const uint16_t* du, int64_t lddu, int T, int r, int nmod, const uint16_t* x, int64_t ldx,
+                    int K, float* const* dA, float* part, hipStream_t st) {
+  if (nmod < 1 || nmod > 4) return -1;
+  GemmArgs g{};
+  g.M = nmod * r; g.N = K; g.K = T;
+  g.A = du; g.lda = lddu;
+  g.Bh = x; g.ldb = ldx;
+  g.ksplit = pick_split(g.M, g.N, g.K);
+  g.partial = part;
+  if (gemm_launch(g, A_COL, B_BF16_NN, EPI_PARTIAL, 64, st)) return -1;
+  return gemm_reduce_rows(part, g.ksplit, g.M, g.N, 1.f, dA, r, K, st);
+}
+
 int linear_fwd(LinearFwd& f, hipStream_t st) {
   const int64_t ldx = f.ldx ? f.ldx : f.K;
   const bool lora = f.A != nullptr && f.r > 0;

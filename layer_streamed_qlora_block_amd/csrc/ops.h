@@ -62,6 +62,10 @@ int skinny_dB(const uint16_t* dy, int64_t lddy, int T, int N, const uint16_t* u,
 // dA = du^T x    (float32)          du [T, r] (lddu), x [T, K] (ldx)  -> dA [r, K]
 int skinny_dA(const uint16_t* du, int64_t lddu, int T, int r, const uint16_t* x, int64_t ldx,
               int K, float* dA, float* part, hipStream_t st);
+// dA_i = du_i^T x for nmod (<= 4) modules sharing x, as one product:
+// du = [du_0 | du_1 | ...] [T, nmod r] (lddu), x [T, K] (ldx) -> dA[i] [r, K]
+int skinny_dA_multi(const uint16_t* du, int64_t lddu, int T, int r, int nmod, const uint16_t* x, int64_t ldx,
+                    int K, float* const* dA, float* part, hipStream_t st);
 // Largest split-K partial buffer (floats) any skinny product of these sizes needs.
 int64_t skinny_partial_floats(int64_t max_mn);
 

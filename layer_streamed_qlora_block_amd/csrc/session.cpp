@@ -515,8 +515,9 @@ int bwd_layer(qls_session* S, int l, const uint8_t* rec, const uint16_t* x, floa
     const int m = k == 0 ? QLS_GATE : QLS_UP;
     QLS_RC(skinny_du(dgu + k * I, 2 * I, T, I, lw + S->wb[m], r, s, du + k * r, 2 * r, part, st));
     QLS_RC(skinny_dB(dgu + k * I, 2 * I, T, I, ugu + k * r, 2 * r, s, dB(m), part, st, r));
-    QLS_RC(skinny_dA(du + k * r, 2 * r, T, r, n2, d, d, dA(m), part, st));
   }
+  float* const dA_gu[2] = {dA(QLS_GATE), dA(QLS_UP)};   // both contract n2: one product
+  QLS_RC(skinny_dA_multi(du, 2 * r, T, r, 2, n2, d, d, dA_gu, part, st));
   LinearDx x2{};
   x2.T = T; x2.Kc = 2 * I; x2.Nout = d; x2.dy = dgu; x2.lddy = 2 * I;
   x2.codes = w.code[QLS_GATE]; x2.absmax = w.amax[QLS_GATE]; x2.ldq = d;
@@ -559,8 +560,9 @@ int bwd_layer(qls_session* S, int l, const uint8_t* rec, const uint16_t* x, floa
     const int m = QLS_Q + k;
     QLS_RC(skinny_du(dqkv + col[k], sh.nqkv, T, nout[k], lw + S->wb[m], r, s, du + k * r, 3 * r, part, st));
     QLS_RC(skinny_dB(dqkv + col[k], sh.nqkv, T, nout[k], uqkv + k * r, 3 * r, s, dB(m), part, st, r));
-    QLS_RC(skinny_dA(du + k * r, 3 * r, T, r, n1, d, d, dA(m), part, st));
   }
+  float* const dA_qkv[3] = {dA(QLS_Q), dA(QLS_K), dA(QLS_V)};   // all contract n1: one product
+  QLS_RC(skinny_dA_multi(du, 3 * r, T, r, 3, n1, d, d, dA_qkv, part, st));
   LinearDx x4{};
   x4.T = T; x4.Kc = sh.nqkv; x4.Nout = d; x4.dy = dqkv; x4.lddy = sh.nqkv;
   x4.codes = w.code[QLS_Q]; x4.absmax = w.amax[QLS_Q]; x4.ldq = d;
