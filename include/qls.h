@@ -47,7 +47,7 @@
 extern "C" {
 #endif
 
-#define QLS_ABI_VERSION 2
+#define QLS_ABI_VERSION 3
 
 enum {
   QLS_OK = 0,
@@ -161,6 +161,15 @@ typedef struct qls_stats {
    * reader thread and the time the step's host thread waited for a record. */
   int64_t disk_reads, disk_bytes;
   double disk_read_ms, disk_wait_ms;
+  /* Copy time not covered by any layer's compute span (copy_ms - overlap_ms;
+   * timing on): the part of the layer stream that sits on the step's
+   * critical path ([P1] "How Soup's layer streaming actually works").  */
+  double exposed_copy_ms;
+  /* Largest workspace any call since the last reset needed: the
+   * qls_workspace_bytes of this session's run configuration with max_tokens
+   * and max_seq set to that call's token count and sequence length (ws_bytes
+   * is the size for the configured maxima). */
+  int64_t peak_ws_bytes;
 } qls_stats;
 
 typedef struct qls_store qls_store;
@@ -315,11 +324,13 @@ void qls_store_destroy(qls_store* st);   /* NULL-safe; removes a disk tier's fil
  * records as in qls_store_create_fmt; layers [ram_layers, n_layers) live in
  * the file `path` (created or truncated, owned by the store, deleted by
  * qls_store_destroy), one record per 4096-byte-aligned slot, written when the
- * layer is set.  A streamed session reads a disk layer with O_DIRECT (when the
- * file system allows it) into one of three pinned staging buffers, from a
- * thread that reads the next disk layer of the sweep ahead of its request, and
- * copies it to the device slot from there; a resident session reads every
- * disk layer once at creation.  Errors: QLS_EINVAL (format, ram_layers
+ * layer is set.  A streamed session reads a disk layer with one buffered
+ * sequential pread of the whole record into one of three pinned staging
+ * buffers, then drops the record's pages from the page cache
+ * (POSIX_FADV_DONTNEED) so that the next read comes from the device again; a
+ * reader thread reads the next disk layer of the sweep ahead of its request,
+ * and the copy to the device slot starts from the staging buffer.  A resident
+ * session reads every disk layer once at creation.  Errors: QLS_EINVAL (format, ram_layers
  * outside [0, n_layers], no path with disk layers), QLS_ENOPIN, QLS_EIO. */
 enum { QLS_TIER_PINNED = 0, QLS_TIER_DISK = 1 };
 int qls_store_create_tiered(const qls_model_cfg* cfg, int absmax_format, int ram_layers,
@@ -328,6 +339,12 @@ int qls_store_create_tiered(const qls_model_cfg* cfg, int absmax_format, int ram
 int qls_store_layer_tier(const qls_store* st, int layer);
 
 /* ---------------------------------------------------------------- session
+ * Token ids: the embedding gather turns an id outside [0, vocab) into a zero
+ * row and raises a per-session device flag, which stays raised until it is
+ * reported: by the next step-like call given a host loss pointer (h_loss), or
+ * by qls_session_stats, which return QLS_EINVAL and clear it (the step
+ * itself has run, AdamW included, on the zero rows).
+ *
  * Device bytes a session needs: the two slots (or the whole store when
  * RESIDENT), layer-input checkpoints, one layer's activations and gradients,
  * the bf16 LoRA working copy, the cross-entropy chunk and split-K scratch. */
@@ -434,7 +451,9 @@ int qls_layer_fwd_bwd(qls_session* s, int layer, const uint16_t* d_x, const uint
  * [(n_layers + 1) x tokens x hidden] (entry n_layers = final hidden state). */
 int qls_session_checkpoints(qls_session* s, const uint16_t** d_ptr, int64_t* tokens);
 
-int qls_session_stats(qls_session* s, qls_stats* out);   /* synchronises the session */
+/* Synchronises the session and fills *out; then reports a raised token-id
+ * flag (QLS_EINVAL, *out still filled). */
+int qls_session_stats(qls_session* s, qls_stats* out);
 int qls_session_reset_stats(qls_session* s);
 
 /* Test hooks; they add operations and never switch kernels.
@@ -449,15 +468,35 @@ int qls_session_reset_stats(qls_session* s);
  *   QLS_DBG_NO_REUSE           reload every layer even when a slot still holds it
  *   QLS_DBG_STREAM_FENCE       the copy stream waits on a slot's release on the
  *                              device; by default the host waits for the
- *                              release before it enqueues the copy */
+ *                              release before it enqueues the copy
+ *   QLS_DBG_RECOMPUTE_ALL      the backward sweep recomputes every layer's
+ *                              forward from its checkpoint, also at the two
+ *                              ends of the sweep, where it otherwise reuses
+ *                              the last layer's forward intermediates and
+ *                              restores layer 0's saved ones */
 enum {
   QLS_DBG_POISON_ON_RELEASE = 1u,
   QLS_DBG_COPY_DELAY = 2u,
   QLS_DBG_COMPUTE_DELAY = 4u,
   QLS_DBG_NO_REUSE = 8u,
-  QLS_DBG_STREAM_FENCE = 16u
+  QLS_DBG_STREAM_FENCE = 16u,
+  QLS_DBG_RECOMPUTE_ALL = 32u
 };
 int qls_debug_set(qls_session* s, uint32_t flags, int delay_us);
+
+/* Test hook for checking gradients layer by layer on a real step ([P1] "The
+ * gradient bug also reveals something important about AI benchmarks": a loss
+ * can look right while the gradients are wrong).  While d_buf is non-NULL,
+ * every backward sweep (qls_sft_step, qls_sft_step_adamw, qls_pref_step,
+ * qls_dpo_step) copies the float32 residual gradient at each layer boundary
+ * into d_buf, float32 [(n_layers + 1) x B*S x hidden]: entry l = dL/dx_l, the
+ * gradient with respect to layer l's input checkpoint (entry n_layers: the
+ * gradient the final norm and LM head hand to the last layer).  The copies
+ * run on the compute stream; they add operations and never switch kernels.
+ * A step fails with QLS_EINVAL before any launch when n_floats is smaller
+ * than (n_layers + 1) * B*S * hidden.  d_buf NULL turns the hook off; the
+ * buffer is borrowed. */
+int qls_debug_capture_grads(qls_session* s, float* d_buf, int64_t n_floats);
 
 #ifdef __cplusplus
 }

@@ -32,6 +32,7 @@ PREF_KINDS = {"dpo": QLS_PREF_DPO, "simpo": QLS_PREF_SIMPO, "orpo": QLS_PREF_ORP
 NMOD = 7
 MODULES = ("q", "k", "v", "o", "gate", "up", "down")
 DBG_POISON_ON_RELEASE, DBG_COPY_DELAY, DBG_COMPUTE_DELAY, DBG_NO_REUSE, DBG_STREAM_FENCE = 1, 2, 4, 8, 16
+DBG_RECOMPUTE_ALL = 32
 
 
 class QlsError(RuntimeError):
@@ -78,7 +79,7 @@ class Stats(C.Structure):
                 ("dq_dx_big_ms", C.c_double), ("dq_dx_big_gflop", C.c_double), ("dq_dx_big_launches", C.c_int64),
                 ("dq_fwd_reduce_ms", C.c_double), ("dq_dx_reduce_ms", C.c_double),
                 ("disk_reads", C.c_int64), ("disk_bytes", C.c_int64), ("disk_read_ms", C.c_double),
-                ("disk_wait_ms", C.c_double)]
+                ("disk_wait_ms", C.c_double), ("exposed_copy_ms", C.c_double), ("peak_ws_bytes", C.c_int64)]
 
     def as_dict(self):
         return {k: getattr(self, k) for k, _ in self._fields_}
@@ -129,6 +130,7 @@ _SIG = {
     "qls_session_stats": (_I, [_P, C.POINTER(Stats)]),
     "qls_session_reset_stats": (_I, [_P]),
     "qls_debug_set": (_I, [_P, C.c_uint32, _I]),
+    "qls_debug_capture_grads": (_I, [_P, _P, _I64]),
 }
 for _name, (_res, _args) in _SIG.items():
     _fn = getattr(_lib, _name)
@@ -382,6 +384,12 @@ def qls_session_reset_stats(sess):
 
 def qls_debug_set(sess, flags, delay_us=0):
     _check(_lib.qls_debug_set(sess, flags, delay_us))
+
+
+def qls_debug_capture_grads(sess, buf, n_floats=None):
+    if buf is not None and n_floats is None:
+        n_floats = buf.numel()
+    _check(_lib.qls_debug_capture_grads(sess, _ptr(buf), 0 if buf is None else n_floats))
 
 
 from .runtime import AdamW, Session, Store  # noqa: E402  (torch-facing convenience objects)

@@ -63,9 +63,11 @@ int skinny_dB(const uint16_t* dy, int64_t lddy, int T, int N, const uint16_t* u,
 int skinny_dA(const uint16_t* du, int64_t lddu, int T, int r, const uint16_t* x, int64_t ldx,
               int K, float* dA, float* part, hipStream_t st);
 // dA_i = du_i^T x for nmod (<= 4) modules sharing x, as one product:
-// du = [du_0 | du_1 | ...] [T, nmod r] (lddu), x [T, K] (ldx) -> dA[i] [r, K]
+// du = [du_0 | du_1 | ...] [T, nmod r] (lddu), x [T, K] (ldx) -> dA[i] [r, K].
+// Always goes through float partials (nmod r x K per slice) in part, which
+// holds part_floats floats; -1 when they would not fit.
 int skinny_dA_multi(const uint16_t* du, int64_t lddu, int T, int r, int nmod, const uint16_t* x, int64_t ldx,
-                    int K, float* const* dA, float* part, hipStream_t st);
+                    int K, float* const* dA, float* part, int64_t part_floats, hipStream_t st);
 // Largest split-K partial buffer (floats) any skinny product of these sizes needs.
 int64_t skinny_partial_floats(int64_t max_mn);
 

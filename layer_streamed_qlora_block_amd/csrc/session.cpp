@@ -89,6 +89,16 @@ Sizes sizes_of(const Shape& sh, const qls_run_cfg& run) {
   return z;
 }
 
+// Floats of the split-K partial buffer: the largest output any skinny LoRA
+// product of a step writes unsplit (the q|k|v dA product writes 3 r x hidden
+// partials even without a split), with the floors of skinny_partial_floats.
+int64_t part_floats(const Shape& sh, int64_t T) {
+  const int64_t d = sh.c.hidden, I = sh.c.intermediate, r = sh.c.lora_r;
+  const int64_t mx = std::max({T * 3 * r, I * r, (int64_t)sh.qd * r, r * std::max<int64_t>(d, I), 3 * r * d,
+                               2 * r * d});
+  return skinny_partial_floats(mx);
+}
+
 Plan make_plan(const Shape& sh, const RecordLayout& lay, const qls_run_cfg& run, int64_t lora_numel) {
   const Sizes z = sizes_of(sh, run);
   const int64_t T = z.Tm, d = sh.c.hidden, I = sh.c.intermediate, r = sh.c.lora_r;
@@ -135,8 +145,7 @@ Plan make_plan(const Shape& sh, const RecordLayout& lay, const qls_run_cfg& run,
   p.ids = take(T * 4);
   p.dlog = take(T * z.Vc * 2);
   p.dhf = take(T * d * 4);
-  const int64_t mx = std::max({T * 3 * r, I * r, (int64_t)sh.qd * r, r * std::max<int64_t>(d, I)});
-  p.part = take(skinny_partial_floats(mx) * 4);
+  p.part = take(part_floats(sh, T) * 4);
   p.xref0 = take(T * d * 2);
   p.xref1 = take(T * d * 2);
   p.scal = take(64);
@@ -211,6 +220,11 @@ struct qls_session {
   int64_t exp_gen[2] = {-1, -1};
   uint32_t dbg = 0;
   int delay_us = 0;
+  // Test hook (qls_debug_capture_grads): residual gradients at every layer
+  // boundary of a backward sweep, (n_layers + 1) x T x hidden floats.
+  float* cap = nullptr;
+  int64_t cap_n = 0;
+  int64_t peak_ws = 0;      // largest workspace a call since the last reset needed
   int64_t wall_khz = 100000;
   // stats
   int64_t steps = 0, loads = 0, h2d = 0;
@@ -517,7 +531,7 @@ int bwd_layer(qls_session* S, int l, const uint8_t* rec, const uint16_t* x, floa
     QLS_RC(skinny_dB(dgu + k * I, 2 * I, T, I, ugu + k * r, 2 * r, s, dB(m), part, st, r));
   }
   float* const dA_gu[2] = {dA(QLS_GATE), dA(QLS_UP)};   // both contract n2: one product
-  QLS_RC(skinny_dA_multi(du, 2 * r, T, r, 2, n2, d, d, dA_gu, part, st));
+  QLS_RC(skinny_dA_multi(du, 2 * r, T, r, 2, n2, d, d, dA_gu, part, part_floats(sh, S->z.Tm), st));
   LinearDx x2{};
   x2.T = T; x2.Kc = 2 * I; x2.Nout = d; x2.dy = dgu; x2.lddy = 2 * I;
   x2.codes = w.code[QLS_GATE]; x2.absmax = w.amax[QLS_GATE]; x2.ldq = d;
@@ -562,7 +576,7 @@ int bwd_layer(qls_session* S, int l, const uint8_t* rec, const uint16_t* x, floa
     QLS_RC(skinny_dB(dqkv + col[k], sh.nqkv, T, nout[k], uqkv + k * r, 3 * r, s, dB(m), part, st, r));
   }
   float* const dA_qkv[3] = {dA(QLS_Q), dA(QLS_K), dA(QLS_V)};   // all contract n1: one product
-  QLS_RC(skinny_dA_multi(du, 3 * r, T, r, 3, n1, d, d, dA_qkv, part, st));
+  QLS_RC(skinny_dA_multi(du, 3 * r, T, r, 3, n1, d, d, dA_qkv, part, part_floats(sh, S->z.Tm), st));
   LinearDx x4{};
   x4.T = T; x4.Kc = sh.nqkv; x4.Nout = d; x4.dy = dqkv; x4.lddy = sh.nqkv;
   x4.codes = w.code[QLS_Q]; x4.absmax = w.amax[QLS_Q]; x4.ldq = d;
@@ -669,10 +683,20 @@ int begin_step(qls_session* S) {
     S->step_ev.push_back({S->next_ev(), S->next_ev()});
     QLS_HIP(hipEventRecord(S->step_ev.back().a, S->cs));
   }
-  QLS_HIP(hipMemsetAsync(S->at<int>(S->p.scal), 0, 64, S->cs));
   int rc = prefetch(S, 0, 1);
   if (!rc && S->sh.c.n_layers > 1) rc = prefetch(S, 1, 1);
   return rc;
+}
+
+// The embedding gather raises a device flag for a token id outside [0, vocab);
+// it stays set until a call reports it.  Reads it after the compute stream
+// has drained: QLS_EINVAL (and the flag cleared) when it was set.
+int report_bad_ids(qls_session* S) {
+  int bad = 0;
+  QLS_HIP(hipMemcpy(&bad, S->at<int>(S->p.scal), sizeof(int), hipMemcpyDeviceToHost));
+  if (!bad) return QLS_OK;
+  QLS_HIP(hipMemset(S->at<int>(S->p.scal), 0, sizeof(int)));
+  return fail(QLS_EINVAL, "token id outside [0, vocab) in a step since the last check");
 }
 
 int end_step(qls_session* S, float* h_loss, const float* d_loss) {
@@ -680,11 +704,22 @@ int end_step(qls_session* S, float* h_loss, const float* d_loss) {
   if (S->timing) QLS_HIP(hipEventRecord(S->step_ev.back().b, S->cs));
   if (h_loss) {
     QLS_HIP(hipStreamSynchronize(S->cs));
-    int bad = 0;
-    QLS_HIP(hipMemcpy(&bad, S->at<int>(S->p.scal), sizeof(int), hipMemcpyDeviceToHost));
-    if (bad) return fail(QLS_EINVAL, "token id outside [0, vocab)");
+    int rc = report_bad_ids(S);
+    if (rc) return rc;
     if (d_loss) QLS_HIP(hipMemcpy(h_loss, d_loss, sizeof(float), hipMemcpyDeviceToHost));
   }
+  return QLS_OK;
+}
+
+// Per-call bookkeeping before any launch: the workspace high-water mark and
+// the capture buffer's size.
+int begin_call(qls_session* S, int T, int Sq) {
+  qls_run_cfg r = S->run;
+  r.max_tokens = T;
+  r.max_seq = Sq;
+  S->peak_ws = std::max(S->peak_ws, make_plan(S->sh, S->lay, r, S->ll.per_layer * S->sh.c.n_layers).total);
+  if (S->cap && S->cap_n < (int64_t)(S->sh.c.n_layers + 1) * T * S->sh.c.hidden)
+    return fail(QLS_EINVAL, "gradient capture buffer smaller than (n_layers + 1) * tokens * hidden floats");
   return QLS_OK;
 }
 
@@ -726,8 +761,19 @@ int forward_sweep(qls_session* S, int T, int B, int Sq, bool lora, bool ref, con
   return QLS_OK;
 }
 
+// Test hook: copy the float32 residual gradient g = dL/dx_l into entry l of
+// the capture buffer.
+int capture(qls_session* S, int l, int T) {
+  if (!S->cap) return QLS_OK;
+  const int64_t n = (int64_t)T * S->sh.c.hidden;
+  QLS_HIP(hipMemcpyAsync(S->cap + (int64_t)l * n, S->at<float>(S->p.g), (size_t)n * 4, hipMemcpyDeviceToDevice,
+                         S->cs));
+  return QLS_OK;
+}
+
 int backward_sweep(qls_session* S, int T, int B, int Sq, float* grads) {
   const int L = S->sh.c.n_layers;
+  const bool shortcuts = !(S->dbg & QLS_DBG_RECOMPUTE_ALL);
   S->parts_next = true;
   for (int l = L - 1; l >= 0; --l) {
     const uint8_t* rec;
@@ -739,17 +785,19 @@ int backward_sweep(qls_session* S, int T, int B, int Sq, float* grads) {
     // intermediates are still in the workspace at the turn, and layer 0's were
     // saved by the forward sweep (the same kernels would reproduce them bit
     // for bit).
-    if (l == 0 && S->acts0_saved && l != S->acts_layer) {
+    if (shortcuts && l == 0 && S->acts0_saved && l != S->acts_layer) {
       QLS_HIP(hipMemcpyAsync(S->at<uint8_t>(S->p.n1), S->at<uint8_t>(S->p.acts0), (size_t)(S->p.g - S->p.n1),
                              hipMemcpyDeviceToDevice, S->cs));
-    } else if (l != S->acts_layer) {
+    } else if (!shortcuts || l != S->acts_layer) {
       rc = fwd_layer(S, l, rec, S->ck(l), S->at<uint16_t>(S->p.xo), true, T, B, Sq);
       if (rc) return rc;
     }
     S->acts_layer = -1;
     if (l == 0) S->acts0_saved = false;
+    if ((rc = capture(S, l + 1, T))) return rc;
     rc = bwd_layer(S, l, rec, S->ck(l), grads, T, B, Sq);
     if (rc) return rc;
+    if (l == 0 && (rc = capture(S, 0, T))) return rc;
     if (S->opt.on) {
       // Fused AdamW: layer l's gradients are final, update its slice now.
       const int64_t pl = S->ll.per_layer, o = (int64_t)l * pl;
@@ -850,6 +898,7 @@ int qls_session_create(const qls_store* st, const qls_run_cfg* run, void* d_ws, 
           hipEventRecord(S->part_rel[i][part], S->cs) != hipSuccess)
         return cleanup(fail(QLS_EHIP, "hipEventCreate failed"));
   }
+  if (hipMemset(S->at<int>(S->p.scal), 0, 64) != hipSuccess) return cleanup(fail(QLS_EHIP, "hipMemset failed"));
   std::vector<float> tab;
   fill_rope_table(sh, run->max_seq, &tab);
   hipError_t e = hipMemcpy(S->at<float>(S->p.rope), tab.data(), tab.size() * 4, hipMemcpyHostToDevice);
@@ -908,7 +957,7 @@ int qls_sft_step(qls_session* S, const int32_t* d_ids, int B, int Sq, const floa
   if (rc) return rc;
   const int T = B * Sq;
   const Shape& sh = S->sh;
-  if ((rc = begin_step(S))) return rc;
+  if ((rc = begin_call(S, T, Sq)) || (rc = begin_step(S))) return rc;
   embed_gather(d_ids, S->res.d_embed, S->ck(0), T, sh.c.hidden, sh.c.vocab, S->at<int>(S->p.scal), S->cs);
   ce_targets(d_ids, B, Sq, S->at<int32_t>(S->p.tgt), S->cs);
   if ((rc = forward_sweep(S, T, B, Sq, true, false, d_lora))) return rc;
@@ -945,7 +994,7 @@ int qls_logprobs(qls_session* S, const int32_t* d_ids, int B, int Sq, int prompt
   if (prompt_len < 1 || prompt_len >= Sq) return fail(QLS_EINVAL, "prompt_len must be in [1, S)");
   const int T = B * Sq;
   const Shape& sh = S->sh;
-  if ((rc = begin_step(S))) return rc;
+  if ((rc = begin_call(S, T, Sq)) || (rc = begin_step(S))) return rc;
 
   embed_gather(d_ids, S->res.d_embed, S->ck(0), T, sh.c.hidden, sh.c.vocab, S->at<int>(S->p.scal), S->cs);
   ce_targets(d_ids, B, Sq, S->at<int32_t>(S->p.tgt), S->cs);
@@ -975,7 +1024,7 @@ int qls_pref_step(qls_session* S, const qls_pref_cfg* cfg, const int32_t* d_chos
   const int B = 2, T = 2 * Sq;
   const Shape& sh = S->sh;
   const int d = sh.c.hidden;
-  if ((rc = begin_step(S))) return rc;
+  if ((rc = begin_call(S, T, Sq)) || (rc = begin_step(S))) return rc;
   int32_t* ids = S->at<int32_t>(S->p.ids);
   QLS_HIP(hipMemcpyAsync(ids, d_chosen, Sq * 4, hipMemcpyDeviceToDevice, S->cs));
   QLS_HIP(hipMemcpyAsync(ids + Sq, d_rejected, Sq * 4, hipMemcpyDeviceToDevice, S->cs));
@@ -1016,6 +1065,7 @@ int qls_layer_fwd_bwd(qls_session* S, int layer, const uint16_t* d_x, const uint
   int rc = check_tokens(S, B, Sq);
   if (rc) return rc;
   const int T = B * Sq, d = S->sh.c.hidden;
+  if ((rc = begin_call(S, T, Sq))) return rc;
   if (S->timing) {
     S->step_ev.push_back({S->next_ev(), S->next_ev()});
     QLS_HIP(hipEventRecord(S->step_ev.back().a, S->cs));
@@ -1052,6 +1102,7 @@ int qls_session_stats(qls_session* S, qls_stats* o) {
   o->layer_loads = S->loads;
   o->h2d_bytes = S->h2d;
   o->ws_bytes = S->p.total;
+  o->peak_ws_bytes = S->peak_ws;
   if (S->disk) {
     const DiskReader::Stats d = S->disk->stats();
     o->disk_reads = d.reads;
@@ -1088,10 +1139,10 @@ int qls_session_stats(qls_session* S, qls_stats* o) {
       if (k.big) { o->dq_dx_big_ms += ms; o->dq_dx_big_gflop += k.gflop; ++o->dq_dx_big_launches; }
     }
     o->dq_fwd_launches = (int64_t)S->kf_ev.size();
-
     o->dq_dx_launches = (int64_t)S->kd_ev.size();
+    o->exposed_copy_ms = std::max(0.0, o->copy_ms - o->overlap_ms);
   }
-  return QLS_OK;
+  return report_bad_ids(S);
 }
 
 int qls_session_reset_stats(qls_session* S) {
@@ -1099,8 +1150,17 @@ int qls_session_reset_stats(qls_session* S) {
   QLS_HIP(hipStreamSynchronize(S->cs));
   QLS_HIP(hipStreamSynchronize(S->ps));
   S->steps = S->loads = S->h2d = 0;
+  S->peak_ws = 0;
   S->clear_timing();
   if (S->disk) S->disk->reset_stats();
+  return QLS_OK;
+}
+
+int qls_debug_capture_grads(qls_session* S, float* d_buf, int64_t n_floats) {
+  if (!S) return fail(QLS_EINVAL, "NULL argument");
+  if (d_buf && n_floats <= 0) return fail(QLS_EINVAL, "n_floats must be positive");
+  S->cap = d_buf;
+  S->cap_n = d_buf ? n_floats : 0;
   return QLS_OK;
 }
 

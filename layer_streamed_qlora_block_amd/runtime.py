@@ -12,6 +12,7 @@ import numpy as np
 import torch
 
 from . import (QLS_ABSMAX_DQ8, QLS_ABSMAX_F32, QLS_RESIDENT, QLS_STREAMED, RunCfg, model_cfg, qls_debug_set,
+               qls_debug_capture_grads,
                pref_cfg, qls_adamw_step, qls_dpo_step, qls_pref_step, qls_layer_fwd_bwd, qls_layer_record_bytes_fmt, qls_logprobs, qls_lora_numel,
                qls_session_checkpoints, qls_session_create, qls_session_destroy, qls_session_reset_stats,
                qls_session_stats, qls_sft_step, qls_sft_step_adamw, qls_store_create_fmt, qls_store_create_tiered, qls_store_destroy, qls_store_layer_view,
@@ -184,6 +185,15 @@ class Session:
 
     def debug(self, flags, delay_us=0):
         qls_debug_set(self.h, flags, delay_us)
+
+    def capture_grads(self, buf):
+        """Test hook: every backward sweep copies dL/dx_l for l = 0..L into buf,
+        a float32 CUDA tensor of at least (L + 1) x tokens x hidden elements
+        (None turns it off); the session keeps a reference while it is set."""
+        if buf is not None and (buf.dtype != torch.float32 or not buf.is_cuda or not buf.is_contiguous()):
+            raise ValueError("buf must be a contiguous float32 CUDA tensor")
+        self._cap = buf
+        qls_debug_capture_grads(self.h, buf)
 
     def close(self):
         if getattr(self, "h", None):

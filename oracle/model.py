@@ -353,12 +353,9 @@ def backward_sweep(cfg, P, model, lora, xs, g, B, S, tabs):
     return g, grads
 
 
-def sft_step(cfg, P, model, lora, ids, x0=None):
-    """One SFT step: next-token cross-entropy, mean over the B*(S-1) targets.
-
-    Returns (loss, grads[l][name] = (dA, dB), aux) with aux holding the layer
-    input checkpoints and g_0 = dL/dx_0."""
-    ids = np.asarray(ids)
+def _sft_forward(cfg, P, model, lora, ids, x0=None):
+    """Forward sweep, head and the mean next-token cross-entropy over the
+    B*(S-1) targets.  Returns (loss, xs, tabs, hc, tgt, w)."""
     B, S = ids.shape
     xs, tabs = forward_sweep(cfg, P, model, lora, ids, x0)
     hc = head_forward(cfg, P, model, xs[-1])
@@ -367,6 +364,22 @@ def sft_step(cfg, P, model, lora, ids, x0=None):
     w = np.where(tgt >= 0, 1.0 / N, 0.0)
     terms = -row_logp(hc, tgt)
     loss = float(np.sum(terms.astype(np.float64) * w))
+    return loss, xs, tabs, hc, tgt, w
+
+
+def sft_loss(cfg, P, model, lora, ids):
+    """The SFT step's loss alone (forward sweep and head, no backward)."""
+    return _sft_forward(cfg, P, model, lora, np.asarray(ids))[0]
+
+
+def sft_step(cfg, P, model, lora, ids, x0=None):
+    """One SFT step: next-token cross-entropy, mean over the B*(S-1) targets.
+
+    Returns (loss, grads[l][name] = (dA, dB), aux) with aux holding the layer
+    input checkpoints and g_0 = dL/dx_0."""
+    ids = np.asarray(ids)
+    B, S = ids.shape
+    loss, xs, tabs, hc, tgt, w = _sft_forward(cfg, P, model, lora, ids, x0)
     g = head_backward(cfg, P, model, xs[-1], hc, tgt, w)
     g0, grads = backward_sweep(cfg, P, model, lora, xs, g, B, S, tabs)
     return loss, grads, {"xs": xs, "g0": g0, "lse": hc["lse"], "logits": hc["logits"]}

@@ -28,7 +28,7 @@ def test_exports_every_declared_symbol(q):
     for name in sorted(declared):
         assert hasattr(lib, name), name
     assert declared == set(q.exported_symbols())
-    assert q.qls_abi_version() == 2
+    assert q.qls_abi_version() == 3
 
 
 def test_codebook_bitwise_equals_oracle(q):

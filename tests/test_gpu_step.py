@@ -293,9 +293,116 @@ def test_bad_token_id_is_reported(q, tiny):
     with pytest.raises(q.QlsError) as e:
         _run_sft(q, sess, cfg, ids, synth.lora_init(cfg))
     assert e.value.code == q.QLS_EINVAL
+    sess.stats()                                  # reported once, then cleared
     with pytest.raises(q.QlsError):
         _run_sft(q, sess, cfg, synth.token_ids(cfg, 1, 80), synth.lora_init(cfg))   # S > max_seq
+    # Without a host loss the flag stays raised until qls_session_stats reports it.
+    d_lora = torch.from_numpy(synth.pack_lora(cfg, synth.lora_init(cfg))).cuda()
+    grads = torch.empty_like(d_lora)
+    loss = torch.empty(1, device="cuda")
+    sess.sft_step(torch.from_numpy(ids).cuda(), d_lora, grads, loss)
+    sess.sft_step(torch.from_numpy(synth.token_ids(cfg, 1, 64)).cuda(), d_lora, grads, loss)
+    with pytest.raises(q.QlsError) as e:
+        sess.stats()
+    assert e.value.code == q.QLS_EINVAL
+    sess.stats()
+    hl, _, _ = _run_sft(q, sess, cfg, synth.token_ids(cfg, 1, 64), synth.lora_init(cfg))
+    assert np.isfinite(hl)
     sess.close()
+
+
+def test_stats_exposed_copy_and_peak_workspace(q, deep):
+    cfg, store, _, res = deep
+    sess = q.Session(store, *res, max_tokens=128, max_seq=64, timing=True)
+    lora = torch.from_numpy(synth.pack_lora(cfg, synth.lora_init(cfg))).cuda()
+    grads = torch.empty_like(lora)
+    loss = torch.empty(1, device="cuda")
+    sess.sft_step(torch.from_numpy(synth.token_ids(cfg, 1, 32)).cuda(), lora, grads, loss)
+    st = sess.stats()
+    assert 0 < st["peak_ws_bytes"] < st["ws_bytes"]
+    assert st["copy_ms"] > 0 and abs(st["exposed_copy_ms"] - (st["copy_ms"] - st["overlap_ms"])) < 1e-9
+    small = st["peak_ws_bytes"]
+    sess.sft_step(torch.from_numpy(synth.token_ids(cfg, 2, 64)).cuda(), lora, grads, loss)
+    st = sess.stats()
+    assert small < st["peak_ws_bytes"] <= st["ws_bytes"]
+    run = q.RunCfg(q.QLS_STREAMED, 128, 64, 0, 1)
+    assert st["peak_ws_bytes"] == q.qls_workspace_bytes(store.h, run)
+    sess.reset_stats()
+    assert sess.stats()["peak_ws_bytes"] == 0
+    sess.close()
+
+
+def test_recompute_all_is_bit_identical(q, deep):
+    """The two ends of the backward sweep reuse forward intermediates instead
+    of recomputing them (the last layer's at the turn, layer 0's saved copy);
+    recomputing every layer must give the same bits: loss, checkpoints and
+    every gradient, for SFT and DPO, streamed and resident."""
+    cfg, store, _, res = deep
+    ids = torch.from_numpy(synth.token_ids(cfg, 1, 64, seed=3)).cuda()
+    c, r = synth.dpo_pair(cfg, 64, 16)
+    c, r = torch.from_numpy(c).cuda(), torch.from_numpy(r).cuda()
+    lora = torch.from_numpy(synth.pack_lora(cfg, synth.lora_init(cfg, b_std=0.01))).cuda()
+    out = {}
+    for mode in (q.QLS_STREAMED, q.QLS_RESIDENT):
+        for flags in (0, q.DBG_RECOMPUTE_ALL):
+            sess = q.Session(store, *res, max_tokens=128, max_seq=64, mode=mode)
+            sess.debug(flags)
+            grads = torch.full_like(lora, float("nan"))
+            loss = torch.empty(1, device="cuda")
+            sess.sft_step(ids, lora, grads, loss)
+            sft = (bits(loss), bits(grads), bits(sess.checkpoints(64)))
+            aux = torch.empty(4, device="cuda")
+            sess.dpo_step(c, r, 16, 0.1, lora, grads, loss, aux)
+            out[mode, flags] = sft + (bits(loss), bits(aux), bits(grads))
+            sess.close()
+    want = out[q.QLS_RESIDENT, 0]
+    for key, got in out.items():
+        for a, b in zip(got, want):
+            assert np.array_equal(a, b), key
+    assert np.all(np.isfinite(want[1].view(np.float32)))
+
+
+def test_gradient_capture(q, tiny):
+    """The capture hook adds copies only (gradients, loss and checkpoints equal
+    an uncaptured step bit for bit); entry l holds dL/dx_l: entry 0 against the
+    oracle's dL/dx_0, and every layer of the step against the oracle given that
+    layer's checkpoint and captured incoming gradient."""
+    from tests.layer_oracle import run_layers
+    cfg, store, model, res = tiny
+    ids = synth.token_ids(cfg, 1, 64)
+    lora = synth.lora_init(cfg)
+    d_lora = torch.from_numpy(synth.pack_lora(cfg, lora)).cuda()
+    runs = []
+    for capture in (False, True):
+        sess = q.Session(store, *res, max_tokens=64, max_seq=64)
+        cap = torch.full(((cfg.L + 1) * 64 * cfg.d,), float("nan"), device="cuda")
+        if capture:
+            small = torch.empty((cfg.L + 1) * 64 * cfg.d - 1, device="cuda")
+            sess.capture_grads(small)
+            with pytest.raises(q.QlsError) as e:
+                _run_sft(q, sess, cfg, ids, lora)
+            assert e.value.code == q.QLS_EINVAL
+            sess.capture_grads(cap)
+        hl, loss, grads = _run_sft(q, sess, cfg, ids, lora)
+        runs.append((bits(loss), bits(grads), bits(sess.checkpoints(64)), cap.view(cfg.L + 1, 64, cfg.d).cpu(),
+                     sess.checkpoints(64).float().cpu().numpy(), grads.cpu().numpy()))
+        sess.close()
+    for a, b in zip(runs[0][:3], runs[1][:3]):
+        assert np.array_equal(a, b)
+    cap, ck, grads = runs[1][3].numpy(), runs[1][4], runs[1][5]
+    assert np.all(np.isfinite(cap))
+    _, _, aux = om.sft_step(cfg, PM, model, lora, ids)
+    rr, cc = report("dL/dx_0", cap[0], aux["g0"])
+    assert rr <= 1e-2 and cc >= 0.999
+    jobs = [(cfg, l, ck[l], cap[l + 1], lora[l], 1, 64, "f32", True) for l in range(cfg.L)]
+    res_o = run_layers(jobs, workers=2, threads=2)
+    per = synth.unpack_lora(cfg, grads)
+    for l in range(cfg.L):
+        out, g_in, og = res_o[l]
+        for name, got, want in [("out", ck[l + 1], out), ("dL/dx", cap[l], g_in)] + [
+                (f"{n}.{'AB'[w]}", per[l][n][w], og[n][w]) for n in om.NAMES for w in range(2)]:
+            rr, cc = rel_l2(got, want), cosine(got, want)
+            assert rr <= 1e-2 and cc >= 0.999, (l, name, rr, cc)
 
 
 def test_degenerate_sizes_are_refused(q, tiny):
