@@ -255,6 +255,22 @@ int qls_attention_bwd(const uint16_t* d_qkv, const uint16_t* d_out, const uint16
                       const float* d_lse, int B, int S, int H, int KV, int hd, float* d_dq,
                       float* d_dk, float* d_dv, void* d_ws, void* stream);
 
+/* Attention backward that allocates nothing: for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  Arguments, layouts, results and errors
+ * as qls_attention_bwd, without d_ws: the scratch (qls_attention_ws_bytes(B,
+ * S, H, hd) bytes) lives in a fixed device array of the library,
+ * QLS_NOALLOC_SCRATCH_BYTES per GPU, held until the process ends (at the 8B
+ * shape, H = 32 and hd = 128, up to 1275 tokens).  A larger problem is
+ * refused with QLS_EINVAL before any launch.  All calls on one GPU share its
+ * array, so calls that overlap on one GPU (on different streams, or from
+ * different threads) race; calls ordered on one stream do not.  Calls no
+ * allocating routine. */
+#define QLS_NOALLOC_SCRATCH_BYTES (40 * 1024 * 1024)
+int qls_attention_bwd_noalloc(const uint16_t* d_qkv, const uint16_t* d_out, const uint16_t* d_dout,
+                              const float* d_lse, int B, int S, int H, int KV, int hd, float* d_dq,
+                              float* d_dk, float* d_dv, void* stream);
+
 /* ---------------------------------------------------------------- optimizer
  * AdamW (decoupled weight decay) on n float32 parameters, in place, at step
  * `step` (1-based): the training loop around qls_sft_step / qls_dpo_step.  The

@@ -102,6 +102,7 @@ _SIG = {
     "qls_attention_ws_bytes": (_I64, [_I, _I, _I, _I]),
     "qls_attention_fwd": (_I, [_P, _I, _I, _I, _I, _I, _P, _P, _P]),
     "qls_attention_bwd": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P]),
+    "qls_attention_bwd_noalloc": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _I, _P, _P, _P, _P]),
     "qls_linear_ws_bytes": (_I64, [_I, _I, _I, _I]),
     "qls_linear_fwd": (_I, [_P, _P, _I, _I, _P, _I, _P, _P, _I, _F, _P, _P, _P, _P]),
     "qls_linear_bwd": (_I, [_P, _P, _I, _I, _P, _P, _P, _I, _P, _P, _I, _F, _P, _P, _P, _P, _P]),
@@ -227,6 +228,14 @@ def qls_attention_fwd(qkv, B, S, H, KV, hd, out, lse, stream=None):
 def qls_attention_bwd(qkv, out, dout, lse, B, S, H, KV, hd, dq, dk, dv, ws, stream=None):
     _check(_lib.qls_attention_bwd(_ptr(qkv), _ptr(out), _ptr(dout), _ptr(lse), B, S, H, KV, hd, _ptr(dq),
                                   _ptr(dk), _ptr(dv), _ptr(ws), _stream(stream)))
+
+
+QLS_NOALLOC_SCRATCH_BYTES = 40 * 1024 * 1024
+
+
+def qls_attention_bwd_noalloc(qkv, out, dout, lse, B, S, H, KV, hd, dq, dk, dv, stream=None):
+    _check(_lib.qls_attention_bwd_noalloc(_ptr(qkv), _ptr(out), _ptr(dout), _ptr(lse), B, S, H, KV, hd, _ptr(dq),
+                                          _ptr(dk), _ptr(dv), _stream(stream)))
 
 
 def qls_linear_ws_bytes(T, N, K, r) -> int:

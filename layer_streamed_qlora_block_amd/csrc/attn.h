@@ -32,3 +32,12 @@ int attn_bwd(const AttnBwdArgs& a, int B, hipStream_t st);
 // dK / dV of each kv head from the per-query-head partials of attn_bwd:
 // out [T, KV*hd] = the sum, in head order, of the H/KV partials in part [T, H*hd].
 void attn_group_sum(const float* part, float* out, int T, int H, int KV, int hd, hipStream_t st);
+
+// The whole attention backward of the C ABI (argument checks, D, dQ, the
+// per-query-head dK / dV partials and their group sums) over caller scratch
+// ws: qls_attention_ws_bytes(B, S, H, hd) bytes.  ws_cap >= 0 is ws's size,
+// checked (QLS_EINVAL when too small); -1 skips the check.  Returns a QLS_*
+// code with the message set.
+int attention_bwd_run(const uint16_t* qkv, const uint16_t* out, const uint16_t* dout, const float* lse, int B,
+                      int S, int H, int KV, int hd, float* dq, float* dk, float* dv, void* ws, int64_t ws_cap,
+                      hipStream_t st);

@@ -121,12 +121,25 @@ int qls_attention_fwd(const uint16_t* qkv, int B, int S, int H, int KV, int hd, 
 
 int qls_attention_bwd(const uint16_t* qkv, const uint16_t* out, const uint16_t* dout, const float* lse, int B,
                       int S, int H, int KV, int hd, float* dq, float* dk, float* dv, void* ws, void* stream) {
+  return attention_bwd_run(qkv, out, dout, lse, B, S, H, KV, hd, dq, dk, dv, ws, -1, (hipStream_t)stream);
+}
+
+}  // extern "C"
+
+// Attention backward over caller scratch ws (ws_cap >= 0: its size in bytes,
+// checked; -1: the caller sized it with qls_attention_ws_bytes).
+int attention_bwd_run(const uint16_t* qkv, const uint16_t* out, const uint16_t* dout, const float* lse, int B,
+                      int S, int H, int KV, int hd, float* dq, float* dk, float* dv, void* ws, int64_t ws_cap,
+                      hipStream_t st) {
   if (!qkv || !out || !dout || !lse || !dq || !dk || !dv || !ws) return fail(QLS_EINVAL, "NULL buffer");
   if (!aligned16({qkv, out, dout, lse, dq, dk, dv, ws}))
     return fail(QLS_EINVAL, "attention buffers must be 16-byte aligned");
   int rc = attn_check(B, S, H, KV, hd);
   if (rc) return rc;
-  hipStream_t st = (hipStream_t)stream;
+  if (ws_cap >= 0 && qls_attention_ws_bytes(B, S, H, hd) > ws_cap)
+    return fail(QLS_EINVAL, "attention scratch of " + std::to_string(qls_attention_ws_bytes(B, S, H, hd)) +
+                                " bytes exceeds the " + std::to_string(ws_cap) + " available");
+
   const int64_t T = (int64_t)B * S;
   char* w = reinterpret_cast<char*>(ws);
   float* D = reinterpret_cast<float*>(w);
@@ -143,6 +156,8 @@ int qls_attention_bwd(const uint16_t* qkv, const uint16_t* out, const uint16_t* 
   QLS_HIP(hipGetLastError());
   return QLS_OK;
 }
+
+extern "C" {
 
 int qls_linear_bwd(const uint8_t* codes, const float* absmax, int N, int K, const uint16_t* x,
                    const uint16_t* u, const uint16_t* dy, int T, const uint16_t* A,
