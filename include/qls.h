@@ -72,9 +72,9 @@ enum { QLS_Q = 0, QLS_K, QLS_V, QLS_O, QLS_GATE, QLS_UP, QLS_DOWN, QLS_NMOD };
  * Linears as (out x in): q (H*hd x d), k and v (KV*hd x d), o (d x H*hd),
  * gate and up (I x d), down (d x I).  LoRA scale s = alpha / r.
  * Supported: head_dim in {64, 128}; n_heads % n_kv_heads == 0 with at most 8
- * query heads per kv head; hidden,
- * intermediate and every linear's in/out multiples of 16; lora_r a multiple
- * of 8 in [8, 128]. */
+ * query heads per kv head; hidden at most 8192; hidden, intermediate and
+ * every linear's in/out multiples of 16; lora_r a multiple of 8 in [8, 128];
+ * vocab a multiple of 8. */
 typedef struct qls_model_cfg {
   int32_t n_layers, hidden, n_heads, n_kv_heads, head_dim, intermediate, vocab;
   float rms_eps, rope_theta;
@@ -368,10 +368,11 @@ int qls_workspace_bytes(const qls_store* st, const qls_run_cfg* run, int64_t* ou
 
 /* Bind a store, a device workspace, two streams (compute and copy, both at
  * default priority) and the resident tensors.  Everything is borrowed and must
- * outlive the session; the session owns only its hipEvents.  RESIDENT mode
- * copies the whole store to the workspace before returning.  Errors:
- * QLS_ENOMEM (ws_bytes too small, checked before any launch), QLS_ESTATE (a
- * store layer never set), QLS_EINVAL, QLS_EHIP. */
+ * outlive the session; the session owns only its hipEvents.  d_ws and the
+ * resident tensors must be 256-byte aligned (torch's allocations are).
+ * RESIDENT mode copies the whole store to the workspace before returning.
+ * Errors: QLS_ENOMEM (ws_bytes too small, checked before any launch),
+ * QLS_ESTATE (a store layer never set), QLS_EINVAL, QLS_EHIP. */
 int qls_session_create(const qls_store* st, const qls_run_cfg* run, void* d_ws, int64_t ws_bytes,
                        void* compute_stream, void* copy_stream, const qls_resident* res,
                        qls_session** out);

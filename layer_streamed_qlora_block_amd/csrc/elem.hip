@@ -70,36 +70,10 @@ __global__ void __launch_bounds__(TB) rmsnorm_fwd_k(const uint16_t* __restrict__
   for (int c = threadIdx.x + kKeep * TB; c < nc; c += TB) put(c, xr[c]);
 }
 
-// out = gres + rho (dy*w - xhat * mean(dy*w*xhat)), xhat = rho x.
-__global__ void __launch_bounds__(TB) rmsnorm_bwd_k(const uint16_t* __restrict__ x,
-                                                    const uint16_t* __restrict__ w, float eps,
-                                                    const float* __restrict__ dy,
-                                                    const float* gres, float* out,
-                                                    uint16_t* __restrict__ out_bf16, int d) {
-  __shared__ float red[4];
-  const int64_t row = blockIdx.x;
-  const uint16_t* xr = x + row * d;
-  const float* dr = dy + row * d;
-  float ss = 0.f;
-  for (int i = threadIdx.x; i < d; i += TB) {
-    const float a = bf2f(xr[i]);
-    ss += a * a;
-  }
-  const float rho = 1.f / sqrtf(block_sum(ss, red) / (float)d + eps);
-  float dot = 0.f;
-  for (int i = threadIdx.x; i < d; i += TB) dot += dr[i] * bf2f(w[i]) * (bf2f(xr[i]) * rho);
-  const float mean = block_sum(dot, red) / (float)d;
-  for (int i = threadIdx.x; i < d; i += TB) {
-    const float xh = bf2f(xr[i]) * rho;
-    const float dyw = dr[i] * bf2f(w[i]);
-    const float v = (gres ? gres[row * d + i] : 0.f) + rho * (dyw - xh * mean);
-    out[row * d + i] = v;
-    if (out_bf16) out_bf16[row * d + i] = f2bf(v);
-  }
-}
-
-// Same as rmsnorm_bwd_k for d <= 8 * TB * NC: the thread's (up to NC) 8-wide
-// chunks of x, dy, w (and gres) stay in registers across the three passes.
+// out = gres + rho (dy*w - xhat * mean(dy*w*xhat)), xhat = rho x, one row per
+// workgroup, for d <= 8 * TB * NC (d % 8 == 0): the thread's (up to NC)
+// 8-wide chunks of x, dy, w (and gres) stay in registers across the three
+// passes.
 template <int NC>
 __global__ void __launch_bounds__(TB) rmsnorm_bwd_vec_k(const uint16_t* __restrict__ x,
                                                         const uint16_t* __restrict__ w, float eps,
@@ -164,26 +138,9 @@ __global__ void __launch_bounds__(TB) rmsnorm_bwd_vec_k(const uint16_t* __restri
   }
 }
 
-// cs: [S][hd/2][2] (cos, sin).  One thread per rotated pair.
-__global__ void rope_fwd_k(uint16_t* __restrict__ qkv, int64_t ld, int T, int S, int nh_q,
-                           int nh_k, int hd, const float* __restrict__ cs) {
-  const int h2 = hd / 2;
-  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  const int64_t per_t = (int64_t)(nh_q + nh_k) * h2;
-  if (idx >= (int64_t)T * per_t) return;
-  const int t = (int)(idx / per_t);
-  const int rem = (int)(idx % per_t);
-  const int head = rem / h2, j = rem % h2;
-  const int pos = t % S;
-  const float c = cs[((int64_t)pos * h2 + j) * 2], s = cs[((int64_t)pos * h2 + j) * 2 + 1];
-  uint16_t* p = qkv + (int64_t)t * ld + (int64_t)head * hd;   // k heads follow q heads
-  const float x1 = bf2f(p[j]), x2 = bf2f(p[j + h2]);
-  p[j] = f2bf(x1 * c - x2 * s);
-  p[j + h2] = f2bf(x2 * c + x1 * s);
-}
-
-// As rope_fwd_k, four consecutive pairs per thread (h2 % 4 == 0): 8-byte
-// loads and stores of the bf16 halves and 16-byte loads of (cos, sin).
+// In-place rotate-half RoPE of the q and k heads of qkv; cs: [S][hd/2][2]
+// (cos, sin).  Four consecutive pairs per thread (h2 % 4 == 0): 8-byte loads
+// and stores of the bf16 halves and 16-byte loads of (cos, sin).
 __global__ void rope_fwd4_k(uint16_t* __restrict__ qkv, int64_t ld, int T, int S, int nh_q, int nh_k, int hd,
                             const float* __restrict__ cs) {
   const int h2 = hd / 2, h8 = h2 / 4;
@@ -211,7 +168,9 @@ __global__ void rope_fwd4_k(uint16_t* __restrict__ qkv, int64_t ld, int T, int S
   *reinterpret_cast<u32x2*>(p + j + h2) = u32x2{pack2_bf16(y2[0], y2[1]), pack2_bf16(y2[2], y2[3])};
 }
 
-// As rope_bwd_k, four consecutive pairs (or v elements) per thread.
+// RoPE backward into the bf16 dq | dk | dv rows of out (ld): dq = R^-1 dq',
+// dk = R^-1 (sum of the kv head's query-head partials), dv = that sum for v,
+// four consecutive pairs (or v elements) per thread.
 __global__ void rope_bwd4_k(const float* __restrict__ dq, const float* __restrict__ dk,
                             const float* __restrict__ dv, uint16_t* __restrict__ out, int64_t ld,
                             int T, int S, int nh_q, int nh_k, int hd, const float* __restrict__ cs) {
@@ -260,52 +219,6 @@ __global__ void rope_bwd4_k(const float* __restrict__ dq, const float* __restric
     f32x4 v = f32x4{0.f, 0.f, 0.f, 0.f};
     for (int i = 0; i < grp; ++i) v += *reinterpret_cast<const f32x4*>(src + i * hd);
     *reinterpret_cast<u32x2*>(o + qd + kvd + e) = u32x2{pack2_bf16(v.x, v.y), pack2_bf16(v.z, v.w)};
-  }
-}
-
-__global__ void rope_bwd_k(const float* __restrict__ dq, const float* __restrict__ dk,
-                           const float* __restrict__ dv, uint16_t* __restrict__ out, int64_t ld,
-                           int T, int S, int nh_q, int nh_k, int hd, const float* __restrict__ cs) {
-  const int h2 = hd / 2;
-  const int qd = nh_q * hd, kvd = nh_k * hd;
-  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  const int64_t per_t = (int64_t)(nh_q + nh_k) * h2 + kvd / 2;
-  if (idx >= (int64_t)T * per_t) return;
-  const int t = (int)(idx / per_t);
-  const int rem = (int)(idx % per_t);
-  uint16_t* o = out + (int64_t)t * ld;
-  const int grp = nh_q / nh_k;
-  if (rem < (nh_q + nh_k) * h2) {
-    const int head = rem / h2, j = rem % h2;
-    const int pos = t % S;
-    const float c = cs[((int64_t)pos * h2 + j) * 2], s = cs[((int64_t)pos * h2 + j) * 2 + 1];
-    float x1, x2;
-    if (head < nh_q) {
-      const float* src = dq + (int64_t)t * qd + (int64_t)head * hd;
-      x1 = src[j];
-      x2 = src[j + h2];
-    } else {                      // kv head: sum the query-head partials in order
-      const float* src = dk + (int64_t)t * qd + (int64_t)(head - nh_q) * grp * hd;
-      x1 = 0.f;
-      x2 = 0.f;
-      for (int i = 0; i < grp; ++i) {
-        x1 += src[i * hd + j];
-        x2 += src[i * hd + j + h2];
-      }
-    }
-    o[(int64_t)head * hd + j] = f2bf(x1 * c + x2 * s);
-    o[(int64_t)head * hd + j + h2] = f2bf(x2 * c - x1 * s);
-  } else {
-    const int e = 2 * (rem - (nh_q + nh_k) * h2);      // element of the kv-width v row
-    const int g = e / hd, j = e % hd;
-    const float* src = dv + (int64_t)t * qd + (int64_t)g * grp * hd + j;
-    float v0 = 0.f, v1 = 0.f;
-    for (int i = 0; i < grp; ++i) {
-      v0 += src[i * hd];
-      v1 += src[i * hd + 1];
-    }
-    o[qd + kvd + e] = f2bf(v0);
-    o[qd + kvd + e + 1] = f2bf(v1);
   }
 }
 
@@ -509,44 +422,38 @@ void rmsnorm_fwd(const uint16_t* x, const uint16_t* w, float eps, uint16_t* y, i
   if (T <= 0) return;
   hipLaunchKernelGGL(rmsnorm_fwd_k, dim3(T), dim3(TB), 0, st, x, w, eps, y, d);
 }
-void rmsnorm_bwd(const uint16_t* x, const uint16_t* w, float eps, const float* dy, const float* gres,
-                 float* out, uint16_t* out_bf16, int T, int d, hipStream_t st) {
-  if (T <= 0) return;
+int rmsnorm_bwd(const uint16_t* x, const uint16_t* w, float eps, const float* dy, const float* gres,
+                float* out, uint16_t* out_bf16, int T, int d, hipStream_t st) {
+  if (T <= 0) return 0;
   const auto a16 = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; };
   const bool vec = d % 8 == 0 && a16(x) && a16(w) && a16(dy) && a16(out) && (!gres || a16(gres)) &&
                    (!out_bf16 || a16(out_bf16));
-  if (vec && d <= 8 * TB * 2)
+  if (!vec || d > 8 * TB * 4) return -1;
+  if (d <= 8 * TB * 2)
     hipLaunchKernelGGL(rmsnorm_bwd_vec_k<2>, dim3(T), dim3(TB), 0, st, x, w, eps, dy, gres, out, out_bf16, d);
-  else if (vec && d <= 8 * TB * 4)
-    hipLaunchKernelGGL(rmsnorm_bwd_vec_k<4>, dim3(T), dim3(TB), 0, st, x, w, eps, dy, gres, out, out_bf16, d);
   else
-    hipLaunchKernelGGL(rmsnorm_bwd_k, dim3(T), dim3(TB), 0, st, x, w, eps, dy, gres, out, out_bf16, d);
+    hipLaunchKernelGGL(rmsnorm_bwd_vec_k<4>, dim3(T), dim3(TB), 0, st, x, w, eps, dy, gres, out, out_bf16, d);
+  return 0;
 }
-void rope_fwd(uint16_t* qkv, int64_t ld, int T, int S, int H, int KV, int hd, const float* cs,
-              hipStream_t st) {
+int rope_fwd(uint16_t* qkv, int64_t ld, int T, int S, int H, int KV, int hd, const float* cs, hipStream_t st) {
   const int64_t n = (int64_t)T * (H + KV) * (hd / 2);
-  if (n <= 0) return;
-  if (hd % 8 == 0 && ld % 4 == 0 && (reinterpret_cast<uintptr_t>(qkv) & 7) == 0) {
-    hipLaunchKernelGGL(rope_fwd4_k, dim3((unsigned)ceil_div64(n / 4, 256)), dim3(256), 0, st, qkv, ld, T, S,
-                       H, KV, hd, cs);
-    return;
-  }
-  hipLaunchKernelGGL(rope_fwd_k, dim3((unsigned)ceil_div64(n, 256)), dim3(256), 0, st, qkv, ld, T, S,
-                     H, KV, hd, cs);
+  if (n <= 0) return 0;
+  if (hd % 8 || ld % 4 || (reinterpret_cast<uintptr_t>(qkv) & 7) || (reinterpret_cast<uintptr_t>(cs) & 15))
+    return -1;
+  hipLaunchKernelGGL(rope_fwd4_k, dim3((unsigned)ceil_div64(n / 4, 256)), dim3(256), 0, st, qkv, ld, T, S, H, KV,
+                     hd, cs);
+  return 0;
 }
-void rope_bwd(const float* dq, const float* dk, const float* dv, uint16_t* dqkv, int64_t ld, int T,
-              int S, int H, int KV, int hd, const float* cs, hipStream_t st) {
-  const int64_t n = (int64_t)T * ((H + KV) * (hd / 2) + KV * hd / 2);
-  if (n <= 0) return;
-  if (hd % 8 == 0 && ld % 4 == 0 && (reinterpret_cast<uintptr_t>(dqkv) & 7) == 0 &&
-      ((reinterpret_cast<uintptr_t>(dq) | reinterpret_cast<uintptr_t>(dk) | reinterpret_cast<uintptr_t>(dv)) & 15) == 0) {
-    const int64_t n4 = (int64_t)T * ((H + KV) * (hd / 8) + KV * hd / 4);   // threads: 4 pairs or 4 v elements each
-    hipLaunchKernelGGL(rope_bwd4_k, dim3((unsigned)ceil_div64(n4, 256)), dim3(256), 0, st, dq, dk, dv,
-                       dqkv, ld, T, S, H, KV, hd, cs);
-    return;
-  }
-  hipLaunchKernelGGL(rope_bwd_k, dim3((unsigned)ceil_div64(n, 256)), dim3(256), 0, st, dq, dk, dv,
-                     dqkv, ld, T, S, H, KV, hd, cs);
+int rope_bwd(const float* dq, const float* dk, const float* dv, uint16_t* dqkv, int64_t ld, int T, int S, int H,
+             int KV, int hd, const float* cs, hipStream_t st) {
+  const int64_t n4 = (int64_t)T * ((H + KV) * (hd / 8) + KV * hd / 4);   // threads: 4 pairs or 4 v elements each
+  if (n4 <= 0) return 0;
+  if (hd % 8 || ld % 4 || (reinterpret_cast<uintptr_t>(dqkv) & 7) || (reinterpret_cast<uintptr_t>(cs) & 15) ||
+      ((reinterpret_cast<uintptr_t>(dq) | reinterpret_cast<uintptr_t>(dk) | reinterpret_cast<uintptr_t>(dv)) & 15))
+    return -1;
+  hipLaunchKernelGGL(rope_bwd4_k, dim3((unsigned)ceil_div64(n4, 256)), dim3(256), 0, st, dq, dk, dv, dqkv, ld, T,
+                     S, H, KV, hd, cs);
+  return 0;
 }
 void swiglu_fwd(const uint16_t* gu, uint16_t* a, int T, int I, hipStream_t st) {
   const int64_t n = (int64_t)T * (I / 8);

@@ -76,17 +76,21 @@ int64_t linear_ws_bytes(int T, int N, int K, int r);
 // ---------------------------------------------------------------- layer kernels (elem.hip)
 void rmsnorm_fwd(const uint16_t* x, const uint16_t* w, float eps, uint16_t* y, int T, int d,
                  hipStream_t st);
-// out = gres + dRMSNorm(x, w; dy); optional bf16 copy of out.
-void rmsnorm_bwd(const uint16_t* x, const uint16_t* w, float eps, const float* dy, const float* gres,
-                 float* out, uint16_t* out_bf16, int T, int d, hipStream_t st);
+// out = gres + dRMSNorm(x, w; dy); optional bf16 copy of out.  Needs d % 8 ==
+// 0, d <= 8192 and 16-byte aligned pointers; -1 (nothing launched) otherwise.
+int rmsnorm_bwd(const uint16_t* x, const uint16_t* w, float eps, const float* dy, const float* gres,
+                float* out, uint16_t* out_bf16, int T, int d, hipStream_t st);
 // In-place rotate-half RoPE on the q and k column blocks of qkv [T, ld].
-void rope_fwd(uint16_t* qkv, int64_t ld, int T, int S, int H, int KV, int hd, const float* cs,
-              hipStream_t st);
+// Needs hd % 8 == 0, ld % 4 == 0, qkv 8-byte and cs 16-byte aligned; -1
+// (nothing launched) otherwise.
+int rope_fwd(uint16_t* qkv, int64_t ld, int T, int S, int H, int KV, int hd, const float* cs,
+             hipStream_t st);
 // dq = bf16(R^-1 dq'), dk = bf16(R^-1 dk'), dv = bf16(dv) into dqkv [T, ld] (q | k | v).
 // dq [T, H*hd]; dk and dv [T, H*hd] hold per-query-head partials that are
-// summed over each kv head's group in head order.
-void rope_bwd(const float* dq, const float* dk, const float* dv, uint16_t* dqkv, int64_t ld, int T,
-              int S, int H, int KV, int hd, const float* cs, hipStream_t st);
+// summed over each kv head's group in head order.  Alignment as rope_fwd,
+// dq / dk / dv 16-byte aligned; -1 (nothing launched) otherwise.
+int rope_bwd(const float* dq, const float* dk, const float* dv, uint16_t* dqkv, int64_t ld, int T,
+             int S, int H, int KV, int hd, const float* cs, hipStream_t st);
 void swiglu_fwd(const uint16_t* gu, uint16_t* a, int T, int I, hipStream_t st);
 // x[t] = E[ids[t]]; ids outside [0, V) give a zero row and set *bad (device int) to 1.
 void embed_gather(const int32_t* ids, const uint16_t* E, uint16_t* x, int T, int d, int V, int* bad,

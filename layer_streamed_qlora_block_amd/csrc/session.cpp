@@ -166,6 +166,7 @@ bool check_run(const Shape& sh, const qls_run_cfg* run, std::string* why) {
   if (c.n_heads / c.n_kv_heads > 8) return bad("at most 8 query heads per kv head");
   if (c.hidden % 16 || c.intermediate % 16 || sh.qd % 16 || sh.kvd % 16)
     return bad("hidden, intermediate and head widths must be multiples of 16");
+  if (c.hidden > 8192) return bad("hidden must be at most 8192");
   if (c.lora_r % 8 || c.lora_r > 128) return bad("lora_r must be a multiple of 8 up to 128");
   if (c.vocab % 8) return bad("vocab must be a multiple of 8");
   return true;
@@ -443,7 +444,7 @@ int fwd_layer(qls_session* S, int l, const uint8_t* rec, const uint16_t* x, uint
   f.s = sh.s; f.y = qkv; f.ldy = sh.nqkv; f.u = S->at<uint16_t>(S->p.uqkv); f.ws = part;
   QLS_RC(S->run_fwd(f, lora, st));
   QLS_RC(S->mark(l, PART_QKV));
-  rope_fwd(qkv, sh.nqkv, T, Sq, sh.c.n_heads, sh.c.n_kv_heads, sh.c.head_dim, S->at<float>(S->p.rope), st);
+  QLS_RC(rope_fwd(qkv, sh.nqkv, T, Sq, sh.c.n_heads, sh.c.n_kv_heads, sh.c.head_dim, S->at<float>(S->p.rope), st));
   AttnArgs aa{};
   aa.qkv = qkv; aa.ld = sh.nqkv; aa.q_off = 0; aa.k_off = sh.qd; aa.v_off = sh.qd + sh.kvd;
   aa.S = Sq; aa.H = sh.c.n_heads; aa.KV = sh.c.n_kv_heads; aa.hd = sh.c.head_dim;
@@ -539,7 +540,7 @@ int bwd_layer(qls_session* S, int l, const uint8_t* rec, const uint16_t* x, floa
   x2.out = dn; x2.ldo = d; x2.epi = EPI_F32; x2.ws = part;
   QLS_RC(S->run_dx(x2, st));
   QLS_RC(S->mark(l, PART_GU));
-  rmsnorm_bwd(h, w.nm, sh.c.rms_eps, dn, g, dh, dyb, T, d, st);
+  QLS_RC(rmsnorm_bwd(h, w.nm, sh.c.rms_eps, dn, g, dh, dyb, T, d, st));
 
   // ---- o projection
   QLS_RC(skinny_du(dyb, d, T, d, lw + S->wb[QLS_O], r, s, du, r, part, st));
@@ -564,8 +565,8 @@ int bwd_layer(qls_session* S, int l, const uint8_t* rec, const uint16_t* x, floa
   ab.dk = S->at<float>(S->p.dkf); ab.dv = S->at<float>(S->p.dvf); ab.lddkv = sh.qd;
   QLS_RC(attn_bwd(ab, B, st));
   uint16_t* dqkv = S->at<uint16_t>(S->p.dqkv);
-  rope_bwd(ab.dq, ab.dk, ab.dv, dqkv, sh.nqkv, T, Sq, sh.c.n_heads, sh.c.n_kv_heads, sh.c.head_dim,
-           S->at<float>(S->p.rope), st);
+  QLS_RC(rope_bwd(ab.dq, ab.dk, ab.dv, dqkv, sh.nqkv, T, Sq, sh.c.n_heads, sh.c.n_kv_heads, sh.c.head_dim,
+                  S->at<float>(S->p.rope), st));
 
   // ---- q, k, v
   const int col[3] = {0, sh.qd, sh.qd + sh.kvd};
@@ -584,7 +585,7 @@ int bwd_layer(qls_session* S, int l, const uint8_t* rec, const uint16_t* x, floa
   x4.out = dn; x4.ldo = d; x4.epi = EPI_F32; x4.ws = part;
   QLS_RC(S->run_dx(x4, st));
   QLS_RC(S->mark(l, PART_QKV));
-  rmsnorm_bwd(x, w.na, sh.c.rms_eps, dn, dh, g, dyb, T, d, st);
+  QLS_RC(rmsnorm_bwd(x, w.na, sh.c.rms_eps, dn, dh, g, dyb, T, d, st));
   return QLS_OK;
 }
 
@@ -659,8 +660,8 @@ int head_bwd(qls_session* S, const uint16_t* xL, int T) {
       QLS_RC(gemm_launch(h, A_ROW, B_BF16_NN, epi, kTile, st));
     }
   }
-  rmsnorm_bwd(xL, S->res.d_final_norm, sh.c.rms_eps, dhf, nullptr, S->at<float>(S->p.g), S->at<uint16_t>(S->p.dyb),
-              T, d, st);
+  QLS_RC(rmsnorm_bwd(xL, S->res.d_final_norm, sh.c.rms_eps, dhf, nullptr, S->at<float>(S->p.g),
+                     S->at<uint16_t>(S->p.dyb), T, d, st));
   return QLS_OK;
 }
 
@@ -846,6 +847,8 @@ int qls_session_create(const qls_store* st, const qls_run_cfg* run, void* d_ws, 
   *out = nullptr;
   if (!st || !run || !d_ws || !res || !res->d_embed || !res->d_lm_head || !res->d_final_norm)
     return fail(QLS_EINVAL, "NULL argument");
+  if (((uintptr_t)d_ws | (uintptr_t)res->d_embed | (uintptr_t)res->d_lm_head | (uintptr_t)res->d_final_norm) & 255)
+    return fail(QLS_EINVAL, "workspace and resident tensors must be 256-byte aligned");
   const Shape& sh = store_shape(st);
   std::string why;
   if (!check_run(sh, run, &why)) return fail(QLS_EINVAL, why);

@@ -3,9 +3,10 @@ transposed dX, skinny LoRA products) against the oracle, through the C ABI.
 
 Tolerances: NF4 dequant and every one-hot probe are bit-exact; floating
 outputs are held to relative L2 <= 1e-2 and cosine >= 0.999 (the gradient bar
-of the step), and the forward output additionally to <= 1 bf16 ulp on 99.9% of
+of the step), the forward output additionally to <= 1 bf16 ulp on 99.9% of
 elements (the two sides round the same float32 sum, accumulated in different
-orders)."""
+orders), and dX, dA, dB element by element to 1e-3 rms + 1e-2 |ref| on 99.9%
+of elements and 10 times that on every element."""
 import numpy as np
 import pytest
 import torch
@@ -13,7 +14,7 @@ import torch
 import synth
 from oracle import model as om
 from oracle import nf4
-from tests.gpu_util import bits, dev, f32, report, same_values
+from tests.gpu_util import bits, dev, elementwise, f32, report, same_values
 
 pytestmark = pytest.mark.gpu
 PM = om.Prec("mirror")
@@ -147,3 +148,8 @@ def test_linear_matches_oracle(q, N, K, T, r, seed, alpha):
     # y: within one bf16 ulp on nearly every element
     ulp = np.abs(nf4.bf16_bits_rne(f32(y)).astype(np.int64) - nf4.bf16_bits_rne(yo).astype(np.int64))
     assert np.mean(ulp <= 1) >= 0.999, np.mean(ulp <= 1)
+    # float32 outputs element by element: the two sides differ only in float32
+    # summation order and in the bf16 rounding of du where its float32 sums
+    # straddle a rounding boundary
+    for name, got, want in [("dx", f32(dx), dxo), ("dA", f32(dA), dAo), ("dB", f32(dB), dBo)]:
+        elementwise(name, got, want, 1e-3, 1e-2)

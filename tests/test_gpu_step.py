@@ -488,3 +488,25 @@ def test_dq_streamed_equals_resident_bitwise(q):
     for name in ("streamed", "poison", "no-reuse"):
         for a, b in zip(out[name], out["resident"]):
             assert np.array_equal(a, b), name
+
+
+def test_unsupported_session_configs_are_refused(q, tiny):
+    """A resident tensor off the 256-byte alignment the kernels assume, and a
+    hidden size above the RMSNorm-backward kernel's 8192, are refused before
+    any launch."""
+    cfg, store, _, res = tiny
+    emb, lm, fn = res
+    off = torch.empty(emb.numel() + 64, dtype=torch.bfloat16, device="cuda")[8:8 + emb.numel()].view_as(emb)
+    run = q.RunCfg(q.QLS_STREAMED, 64, 64, 0, 0)
+    need = q.qls_workspace_bytes(store.h, run)
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+    s = torch.cuda.Stream()
+    with pytest.raises(q.QlsError) as e:
+        q.qls_session_create(store.h, run, ws, need, s, s, off, lm, fn)
+    assert e.value.code == q.QLS_EINVAL
+    wide = synth.scaled(cfg, L=1, d=8448, H=66, KV=66, hd=128, I=256)
+    big = q.Store(wide)
+    with pytest.raises(q.QlsError) as e:
+        q.qls_workspace_bytes(big.h, run)
+    assert e.value.code == q.QLS_EINVAL
+    big.close()

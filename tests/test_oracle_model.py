@@ -266,3 +266,40 @@ def test_sft_loss_near_ln_vocab():
     ids = synth.token_ids(cfg, 1, 64)
     loss, _, _ = om.sft_step(cfg, PM, model, synth.lora_init(cfg), ids)
     assert abs(loss - math.log(cfg.V)) < 0.5
+
+
+def test_response_logprob_span_matches_torch_cross_entropy(micro):
+    """The response log-likelihood of a (prompt, response) sequence is the sum,
+    over every response token at position t in [P, S), of log p(ids_t |
+    ids_<t), the next-token distribution read from the logits of position t-1.
+    Written here position by position with torch's F.cross_entropy on logits
+    from the library-op forward, independent of the oracle's row / span
+    bookkeeping; seq_logprobs, dpo_step and pref_step must all agree."""
+    cfg, model, lora, _ = micro
+    S, P, beta = 12, 4, 0.1
+    c, r = synth.dpo_pair(cfg, S, P, seeds=(61, 62, 63))
+    ids2 = np.stack([c, r])
+    tid = torch.as_tensor(ids2, dtype=torch.long)
+
+    def torch_pi(lr, lo=P, hi=S):
+        lt = [{n: (torch.tensor(a, dtype=torch.float64), torch.tensor(b, dtype=torch.float64))
+               for n, (a, b) in mods.items()} for mods in lr]
+        with torch.no_grad():
+            logits = _torch_forward(cfg, model, lt, ids2, 2, S).view(2, S, cfg.V)
+        return [sum(-F.cross_entropy(logits[b, t - 1][None], tid[b, t][None]).item() for t in range(lo, hi))
+                for b in range(2)]
+
+    pol = torch_pi(lora)
+    ref = torch_pi(synth.lora_init(cfg, b_std=0.0))          # adapters disabled: B = 0
+    pol_shift = torch_pi(lora, lo=P - 1, hi=S - 1)           # the span one position early
+    seq, _ = om.seq_logprobs(cfg, P64, model, lora, ids2, P)
+    seq_ref, _ = om.seq_logprobs(cfg, P64, model, None, ids2, P)
+    assert np.allclose(seq, pol, rtol=1e-11, atol=0) and np.allclose(seq_ref, ref, rtol=1e-11, atol=0)
+    loss, _, aux = om.dpo_step(cfg, P64, model, lora, c, r, P, beta)
+    assert np.allclose(aux["pi"], pol, rtol=1e-11) and np.allclose(aux["ref"], ref, rtol=1e-11)
+    z = beta * ((pol[0] - ref[0]) - (pol[1] - ref[1]))
+    assert abs(loss - math.log1p(math.exp(-z))) < 1e-12
+    _, _, paux = om.pref_step(cfg, P64, model, lora, c, r, P, "simpo", beta=2.0, gamma=1.0)
+    assert np.allclose(paux["pi"], pol, rtol=1e-11)
+    # an off-by-one span would be seen: the sums one position early differ
+    assert np.all(np.abs(np.asarray(pol_shift) - seq) > 1e-3)
