@@ -170,6 +170,9 @@ typedef struct qls_stats {
    * and max_seq set to that call's token count and sequence length (ws_bytes
    * is the size for the configured maxima). */
   int64_t peak_ws_bytes;
+  /* The part of dq_fwd_reduce_ms / dq_dx_reduce_ms that followed the
+   * 256 x 256-tile launches (timing on). */
+  double dq_fwd_big_reduce_ms, dq_dx_big_reduce_ms;
 } qls_stats;
 
 typedef struct qls_store qls_store;

@@ -79,7 +79,8 @@ class Stats(C.Structure):
                 ("dq_dx_big_ms", C.c_double), ("dq_dx_big_gflop", C.c_double), ("dq_dx_big_launches", C.c_int64),
                 ("dq_fwd_reduce_ms", C.c_double), ("dq_dx_reduce_ms", C.c_double),
                 ("disk_reads", C.c_int64), ("disk_bytes", C.c_int64), ("disk_read_ms", C.c_double),
-                ("disk_wait_ms", C.c_double), ("exposed_copy_ms", C.c_double), ("peak_ws_bytes", C.c_int64)]
+                ("disk_wait_ms", C.c_double), ("exposed_copy_ms", C.c_double), ("peak_ws_bytes", C.c_int64),
+                ("dq_fwd_big_reduce_ms", C.c_double), ("dq_dx_big_reduce_ms", C.c_double)]
 
     def as_dict(self):
         return {k: getattr(self, k) for k, _ in self._fields_}

@@ -1132,14 +1132,22 @@ int qls_session_stats(qls_session* S, qls_stats* o) {
     for (auto& k : S->kf_ev) {
       const double ms = span(k.a, k.b);
       o->dq_fwd_ms += ms; o->dq_fwd_gflop += k.gflop;
-      if (k.c) o->dq_fwd_reduce_ms += span(k.b, k.c);
-      if (k.big) { o->dq_fwd_big_ms += ms; o->dq_fwd_big_gflop += k.gflop; ++o->dq_fwd_big_launches; }
+      const double red = k.c ? span(k.b, k.c) : 0.0;
+      o->dq_fwd_reduce_ms += red;
+      if (k.big) {
+        o->dq_fwd_big_ms += ms; o->dq_fwd_big_gflop += k.gflop; ++o->dq_fwd_big_launches;
+        o->dq_fwd_big_reduce_ms += red;
+      }
     }
     for (auto& k : S->kd_ev) {
       const double ms = span(k.a, k.b);
       o->dq_dx_ms += ms; o->dq_dx_gflop += k.gflop;
-      if (k.c) o->dq_dx_reduce_ms += span(k.b, k.c);
-      if (k.big) { o->dq_dx_big_ms += ms; o->dq_dx_big_gflop += k.gflop; ++o->dq_dx_big_launches; }
+      const double red = k.c ? span(k.b, k.c) : 0.0;
+      o->dq_dx_reduce_ms += red;
+      if (k.big) {
+        o->dq_dx_big_ms += ms; o->dq_dx_big_gflop += k.gflop; ++o->dq_dx_big_launches;
+        o->dq_dx_big_reduce_ms += red;
+      }
     }
     o->dq_fwd_launches = (int64_t)S->kf_ev.size();
     o->dq_dx_launches = (int64_t)S->kd_ev.size();

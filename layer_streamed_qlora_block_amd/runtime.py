@@ -55,6 +55,10 @@ class Store:
         am = [np.ascontiguousarray(a, dtype=np.float32) for a in absmax]
         qls_store_set_layer_nf4(self.h, layer, cs, am, _np_bf16(norm_attn), _np_bf16(norm_mlp))
 
+    def view(self, layer):
+        """The raw qls_layer_view of one record (host pointers into the store)."""
+        return qls_store_layer_view(self.h, layer)
+
     def layer(self, layer) -> dict:
         """Copies of one record's NF4 codes and absmax data per module and its
         norms ("absmax" for f32 stores; "absmax_q8" and "absmax_scale" for dq8)."""
