@@ -70,3 +70,20 @@ int64_t gemm_partial_elems(int M, int N, int ksplit);
 // Sums the ksplit partials of g (in split order) and applies epilogue epi to g.C
 // (N % 4 == 0).
 void gemm_reduce_epi(const GemmArgs& g, int epi, hipStream_t st);
+
+// Grouped skinny products: up to kMaxGroup products of one loader combination
+// in one launch, each writing split-K float partials (g[i].partial, its
+// g[i].ksplit slices); end[i] = cumulative workgroup count (tiles x slices of
+// 64 x 64) through product i.
+constexpr int kMaxGroup = 6;
+struct GemmGroup { GemmArgs g[kMaxGroup]; int end[kMaxGroup]; int n; };
+int gemm_group_launch(const GemmGroup& gg, int aload, int bload, hipStream_t st);
+// The sums of those partials in split order, one job per product: alpha * sum
+// to C (mode 0 bf16, 1 float) or, with rows > 0, row block m / rows to Cr[m /
+// rows] (float); end[i] = cumulative M * N through job i.
+struct ReduceJob {
+  const float* P; int ks, M, N; float alpha; int mode;
+  void* C; int64_t ldc; int rows; float* Cr[4];
+};
+struct ReduceGroup { ReduceJob j[kMaxGroup]; int64_t end[kMaxGroup]; int n; };
+int reduce_group_launch(const ReduceGroup& rg, hipStream_t st);

@@ -466,18 +466,18 @@ QLS_DEV void b_store(const typename BLoaderOf<BN, BL, F>::T& lb, uint16_t* s, co
 
 QLS_DEV float sigmoidf_(float x) { return 1.f / (1.f + __expf(-x)); }
 
+// One output tile (tile = tm * tiles_n + tn) of contraction slice z of the
+// product g; smem holds two LDS stages of (BM + BN) x PITCH bf16, lut 16 floats.
 template <int BM, int BN, int AL, int BL, int EPI, bool F>
-__global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2)))
-gemm_kernel(GemmArgs g, const float* __restrict__ cb) {
+QLS_DEV void gemm_body(const GemmArgs& g, int tile, int z, const float* __restrict__ cb, uint16_t* smem,
+                       float* lut) {
   constexpr int MI = BM / 64, NI = BN / 64;
   constexpr int STAGE = (BM + BN) * PITCH;
-  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * STAGE];
-  __shared__ float lut[16];
 
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   const int wm = wave >> 1, wn = wave & 1;
   const int tiles_n = (g.N + BN - 1) / BN;
-  const int tm = blockIdx.x / tiles_n, tn = blockIdx.x % tiles_n;
+  const int tm = tile / tiles_n, tn = tile % tiles_n;
   const int m0 = tm * BM, n0 = tn * BN;
   if constexpr (BL == B_NF4_NT || BL == B_NF4_NN) {
     if (t < 16) lut[t] = cb[t];
@@ -485,8 +485,8 @@ gemm_kernel(GemmArgs g, const float* __restrict__ cb) {
 
   const int nk = (g.K + BK - 1) / BK;
   const int ks = g.ksplit > 0 ? g.ksplit : 1;
-  const int kb = (int)((int64_t)nk * blockIdx.z / ks);
-  const int ke = (int)((int64_t)nk * (blockIdx.z + 1) / ks);
+  const int kb = (int)((int64_t)nk * z / ks);
+  const int ke = (int)((int64_t)nk * (z + 1) / ks);
 
   f32x16 acc[MI][NI];
 #pragma unroll
@@ -497,7 +497,7 @@ gemm_kernel(GemmArgs g, const float* __restrict__ cb) {
   // ---- LoRA contraction first (split 0 only), so no second accumulator is
   // needed: FWD starts the accumulator at (s2/alpha) U_g B_g^T, DX at du_cat A_cat;
   // the base product then accumulates on top in fp32.
-  const bool first = blockIdx.z == 0;
+  const bool first = z == 0;
   if constexpr (BL == B_NF4_NT && EPI == EPI_BF16) {
     if (g.lora == LORA_FWD && first) {
       // columns of modules other than g read B as zero
@@ -607,7 +607,7 @@ gemm_kernel(GemmArgs g, const float* __restrict__ cb) {
             const int n = n0 + wn * (BN / 2) + 32 * j + (lane & 31);
             if (m >= g.M || n >= g.N) continue;
             const float v = g.alpha * acc[i][j][q];
-            g.partial[((int64_t)blockIdx.z * g.M + m) * g.N + n] = v;
+            g.partial[((int64_t)z * g.M + m) * g.N + n] = v;
           }
       return;
     }
@@ -670,7 +670,7 @@ gemm_kernel(GemmArgs g, const float* __restrict__ cb) {
           } else if constexpr (EPI == EPI_F32_ACC) {
             reinterpret_cast<float*>(g.C)[(int64_t)m * g.ldc + n] += g.alpha * v;
           } else if constexpr (EPI == EPI_PARTIAL) {
-            g.partial[((int64_t)blockIdx.z * g.M + m) * g.N + n] = v;
+            g.partial[((int64_t)z * g.M + m) * g.N + n] = v;
           } else if constexpr (EPI == EPI_SWIGLU_BWD) {
             const float gg = bf2f(g.gu[(int64_t)m * g.ldgu + n]);
             const float uu = bf2f(g.gu[(int64_t)m * g.ldgu + g.I + n]);
@@ -692,6 +692,52 @@ gemm_kernel(GemmArgs g, const float* __restrict__ cb) {
           }
         }
   }
+}
+
+template <int BM, int BN, int AL, int BL, int EPI, bool F>
+__global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2)))
+gemm_kernel(GemmArgs g, const float* __restrict__ cb) {
+  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * (BM + BN) * PITCH];
+  __shared__ float lut[16];
+  gemm_body<BM, BN, AL, BL, EPI, F>(g, blockIdx.x, blockIdx.z, cb, smem, lut);
+}
+
+// Several products of one loader combination in one launch (split-K float
+// partials, summed by reduce_group_kernel): workgroups [end[p-1], end[p])
+// take the tiles and slices of product p, slice-major.
+template <int BM, int BN, int AL, int BL, bool F>
+__global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2)))
+gemm_group_kernel(GemmGroup gg) {
+  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * (BM + BN) * PITCH];
+  __shared__ float lut[16];
+  int p = 0;
+  while (p + 1 < gg.n && (int)blockIdx.x >= gg.end[p]) ++p;
+  const int local = (int)blockIdx.x - (p ? gg.end[p - 1] : 0);
+  const GemmArgs& g = gg.g[p];
+  const int tiles = ((g.M + BM - 1) / BM) * ((g.N + BN - 1) / BN);
+  gemm_body<BM, BN, AL, BL, EPI_PARTIAL, F>(g, local % tiles, local / tiles, nullptr, smem, lut);
+}
+
+// Split-order sums of the partials of several products, each with its own
+// output: bf16 (mode 0) or float (mode 1) alpha * sum at C (ldc), or, with
+// rows > 0, row block m / rows of the sum to Cr[m / rows] (float).
+__global__ void reduce_group_kernel(ReduceGroup rg) {
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  int p = 0;
+  while (p + 1 < rg.n && idx >= rg.end[p]) ++p;
+  if (idx >= rg.end[p]) return;
+  const ReduceJob& j = rg.j[p];
+  const int64_t local = idx - (p ? rg.end[p - 1] : 0);
+  const int64_t MN = (int64_t)j.M * j.N;
+  const int m = (int)(local / j.N), n = (int)(local % j.N);
+  float s = 0.f;
+  for (int z = 0; z < j.ks; ++z) s += j.P[z * MN + local];
+  if (j.rows > 0)
+    j.Cr[m / j.rows][(int64_t)(m % j.rows) * j.ldc + n] = j.alpha * s;
+  else if (j.mode == 0)
+    reinterpret_cast<uint16_t*>(j.C)[(int64_t)m * j.ldc + n] = f2bf(j.alpha * s);
+  else
+    reinterpret_cast<float*>(j.C)[(int64_t)m * j.ldc + n] = j.alpha * s;
 }
 
 __global__ void reduce_kernel(const float* __restrict__ P, int ks, int M, int N, float alpha,
@@ -840,6 +886,38 @@ int gemm_reduce_rows(const float* partial, int ksplit, int M, int N, float alpha
 }
 
 int64_t gemm_partial_elems(int M, int N, int ksplit) { return (int64_t)M * N * ksplit; }
+
+static_assert(sizeof(GemmGroup) <= 4096, "grouped GEMM arguments must fit the kernel argument segment");
+static_assert(sizeof(ReduceGroup) <= 4096, "grouped reduce arguments must fit the kernel argument segment");
+
+int gemm_group_launch(const GemmGroup& gg, int aload, int bload, hipStream_t st) {
+  if (gg.n < 1 || gg.n > kMaxGroup) return -1;
+  bool fast = true;
+  for (int i = 0; i < gg.n; ++i) {
+    if (!gg.g[i].partial || gg.g[i].ksplit < 1) return -1;
+    fast = fast && fast_ok(gg.g[i], aload, bload, 64);
+  }
+  const dim3 grid((unsigned)gg.end[gg.n - 1]);
+#define QLS_GCASE(AL, BL)                                                                         \
+  if (aload == AL && bload == BL) {                                                               \
+    if (fast) hipLaunchKernelGGL((gemm_group_kernel<64, 64, AL, BL, true>), grid, dim3(NT), 0, st, gg);  \
+    else hipLaunchKernelGGL((gemm_group_kernel<64, 64, AL, BL, false>), grid, dim3(NT), 0, st, gg);      \
+    return 0;                                                                                     \
+  }
+  QLS_GCASE(A_ROW, B_BF16_NN)
+  QLS_GCASE(A_COL, B_BF16_NN)
+  QLS_GCASE(A_ROW, B_BF16_NT)
+#undef QLS_GCASE
+  return -1;
+}
+
+int reduce_group_launch(const ReduceGroup& rg, hipStream_t st) {
+  if (rg.n < 1 || rg.n > kMaxGroup) return -1;
+  const int64_t n = rg.end[rg.n - 1];
+  if (n <= 0) return 0;
+  hipLaunchKernelGGL(reduce_group_kernel, dim3((unsigned)ceil_div64(n, 256)), dim3(256), 0, st, rg);
+  return 0;
+}
 
 void gemm_reduce_epi(const GemmArgs& g, int epi, hipStream_t st) {
   const int64_t n = (int64_t)g.M * (g.N / 4);

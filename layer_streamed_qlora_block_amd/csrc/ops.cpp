@@ -115,6 +115,86 @@ int skinny_dA_multi(const uint16_t* du, int64_t lddu, int T, int r, int nmod, co
   return gemm_reduce_rows(part, g.ksplit, g.M, g.N, 1.f, dA, r, K, st);
 }
 
+SkinnyProd sk_du(const uint16_t* dy, int64_t lddy, int T, int N, const uint16_t* B, int r, float s, uint16_t* du,
+                 int64_t lddu) {
+  SkinnyProd p{};
+  p.aload = A_ROW; p.bload = B_BF16_NN;
+  p.A = dy; p.lda = lddy; p.B = B; p.ldb = r;
+  p.M = T; p.N = r; p.K = N;
+  p.alpha = s; p.mode = 0; p.C = du; p.ldc = lddu;
+  return p;
+}
+
+SkinnyProd sk_dB(const uint16_t* dy, int64_t lddy, int T, int N, const uint16_t* u, int64_t ldu, float s, float* dB,
+                 int r) {
+  SkinnyProd p{};
+  p.aload = A_COL; p.bload = B_BF16_NN;
+  p.A = dy; p.lda = lddy; p.B = u; p.ldb = ldu;
+  p.M = N; p.N = r; p.K = T;
+  p.alpha = s; p.mode = 1; p.C = dB; p.ldc = r;
+  return p;
+}
+
+SkinnyProd sk_dA_multi(const uint16_t* du, int64_t lddu, int T, int r, int nmod, const uint16_t* x, int64_t ldx,
+                       int K, float* const* dA) {
+  SkinnyProd p{};
+  p.aload = A_COL; p.bload = B_BF16_NN;
+  p.A = du; p.lda = lddu; p.B = x; p.ldb = ldx;
+  p.M = nmod * r; p.N = K; p.K = T;
+  p.alpha = 1.f; p.mode = 1; p.ldc = K;
+  p.rows = r;
+  for (int i = 0; i < nmod && i < 4; ++i) p.Crows[i] = dA[i];
+  return p;
+}
+
+int64_t skinny_group_floats(const SkinnyProd* p, int n) {
+  int64_t off = 0;
+  for (int i = 0; i < n; ++i)
+    off += align_up(gemm_partial_elems(p[i].M, p[i].N, pick_split(p[i].M, p[i].N, p[i].K)), 64);
+  return off;
+}
+
+int skinny_group(const SkinnyProd* p, int n, float* part, int64_t part_floats, hipStream_t st) {
+  if (n < 1 || n > kMaxGroup) return -1;
+  static const int kinds[3][2] = {{A_ROW, B_BF16_NN}, {A_COL, B_BF16_NN}, {A_ROW, B_BF16_NT}};
+  GemmArgs args[kMaxGroup];
+  ReduceGroup rg{};
+  int64_t off = 0;
+  for (int i = 0; i < n; ++i) {
+    const SkinnyProd& q = p[i];
+    if (q.rows > 0 && (q.M % q.rows || q.M / q.rows > 4)) return -1;
+    GemmArgs& g = args[i];
+    g = GemmArgs{};
+    g.M = q.M; g.N = q.N; g.K = q.K;
+    g.A = q.A; g.lda = q.lda;
+    g.Bh = q.B; g.ldb = q.ldb;
+    g.ksplit = pick_split(q.M, q.N, q.K);
+    g.partial = part + off;
+    off += align_up(gemm_partial_elems(q.M, q.N, g.ksplit), 64);
+    ReduceJob& j = rg.j[i];
+    j.P = g.partial; j.ks = g.ksplit; j.M = q.M; j.N = q.N; j.alpha = q.alpha; j.mode = q.mode;
+    j.C = q.C; j.ldc = q.ldc; j.rows = q.rows;
+    for (int c = 0; c < 4; ++c) j.Cr[c] = q.Crows[c];
+    rg.end[i] = (i ? rg.end[i - 1] : 0) + (int64_t)q.M * q.N;
+  }
+  rg.n = n;
+  if (off > part_floats) return -1;
+  for (const auto& kd : kinds) {
+    GemmGroup gg{};
+    int wg = 0;
+    for (int i = 0; i < n; ++i) {
+      if (p[i].aload != kd[0] || p[i].bload != kd[1]) continue;
+      const GemmArgs& g = args[i];
+      wg += (int)(cdiv(g.M, 64) * cdiv(g.N, 64)) * g.ksplit;
+      gg.g[gg.n] = g;
+      gg.end[gg.n] = wg;
+      ++gg.n;
+    }
+    if (gg.n && gemm_group_launch(gg, kd[0], kd[1], st)) return -1;
+  }
+  return reduce_group_launch(rg, st);
+}
+
 int linear_fwd(LinearFwd& f, hipStream_t st) {
   const int64_t ldx = f.ldx ? f.ldx : f.K;
   const bool lora = f.A != nullptr && f.r > 0;

@@ -68,6 +68,33 @@ int skinny_dA(const uint16_t* du, int64_t lddu, int T, int r, const uint16_t* x,
 // holds part_floats floats; -1 when they would not fit.
 int skinny_dA_multi(const uint16_t* du, int64_t lddu, int T, int r, int nmod, const uint16_t* x, int64_t ldx,
                     int K, float* const* dA, float* part, int64_t part_floats, hipStream_t st);
+// Several skinny products in as few launches as their loaders allow: one
+// grouped GEMM launch per loader combination (A_ROW / B_BF16_NN: du-like,
+// A_COL / B_BF16_NN: dA- and dB-like, A_ROW / B_BF16_NT: U-like), then one
+// launch that sums every product's split-K partials in split order (the same
+// arithmetic as the one-product calls).  C: bf16 (mode 0) or float (mode 1)
+// alpha * product, or with rows > 0 row block i of the float product to
+// Crows[i] (ldc).  Partials are laid out back to back in part (part_floats
+// floats); -1 when they do not fit or more than kMaxGroup products are given.
+struct SkinnyProd {
+  int aload, bload;
+  const uint16_t* A; int64_t lda;
+  const uint16_t* B; int64_t ldb;
+  int M, N, K;
+  float alpha; int mode;
+  void* C; int64_t ldc;
+  int rows; float* Crows[4];
+};
+int skinny_group(const SkinnyProd* p, int n, float* part, int64_t part_floats, hipStream_t st);
+// Floats of partials skinny_group lays out for these products.
+int64_t skinny_group_floats(const SkinnyProd* p, int n);
+// The product descriptions of the one-product calls above.
+SkinnyProd sk_du(const uint16_t* dy, int64_t lddy, int T, int N, const uint16_t* B, int r, float s, uint16_t* du,
+                 int64_t lddu);
+SkinnyProd sk_dB(const uint16_t* dy, int64_t lddy, int T, int N, const uint16_t* u, int64_t ldu, float s, float* dB,
+                 int r);
+SkinnyProd sk_dA_multi(const uint16_t* du, int64_t lddu, int T, int r, int nmod, const uint16_t* x, int64_t ldx,
+                       int K, float* const* dA);
 // Largest split-K partial buffer (floats) any skinny product of these sizes needs.
 int64_t skinny_partial_floats(int64_t max_mn);
 

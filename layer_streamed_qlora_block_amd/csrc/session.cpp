@@ -89,14 +89,49 @@ Sizes sizes_of(const Shape& sh, const qls_run_cfg& run) {
   return z;
 }
 
-// Floats of the split-K partial buffer: the largest output any skinny LoRA
-// product of a step writes unsplit (the q|k|v dA product writes 3 r x hidden
-// partials even without a split), with the floors of skinny_partial_floats.
+// The skinny LoRA products of one layer's backward, in the groups that run
+// as one launch each (plus one reduce): the du of each linear group, then
+// its dB and dA.  Pointers null: sizes only (dA of a single module: rows =
+// r, one block).
+struct SkGroups { SkinnyProd p[8][4]; int n[8]; };
+SkGroups layer_groups(const Shape& sh, int T) {
+  SkGroups G{};
+  const int d = sh.c.hidden, I = sh.c.intermediate, r = sh.c.lora_r;
+  float* nil[4] = {nullptr, nullptr, nullptr, nullptr};
+  G.p[0][0] = sk_du(nullptr, d, T, d, nullptr, r, 1.f, nullptr, r); G.n[0] = 1;                  // down
+  G.p[1][0] = sk_dB(nullptr, d, T, d, nullptr, r, 1.f, nullptr, r);
+  G.p[1][1] = sk_dA_multi(nullptr, r, T, r, 1, nullptr, I, I, nil); G.n[1] = 2;
+  for (int k = 0; k < 2; ++k) {                                                                   // gate, up
+    G.p[2][k] = sk_du(nullptr, 2 * I, T, I, nullptr, r, 1.f, nullptr, 2 * r);
+    G.p[3][k] = sk_dB(nullptr, 2 * I, T, I, nullptr, 2 * r, 1.f, nullptr, r);
+  }
+  G.n[2] = 2;
+  G.p[3][2] = sk_dA_multi(nullptr, 2 * r, T, r, 2, nullptr, d, d, nil); G.n[3] = 3;
+  G.p[4][0] = sk_du(nullptr, d, T, d, nullptr, r, 1.f, nullptr, r); G.n[4] = 1;                  // o
+  G.p[5][0] = sk_dB(nullptr, d, T, d, nullptr, r, 1.f, nullptr, r);
+  G.p[5][1] = sk_dA_multi(nullptr, r, T, r, 1, nullptr, sh.qd, sh.qd, nil); G.n[5] = 2;
+  const int nout[3] = {sh.qd, sh.kvd, sh.kvd};
+  for (int k = 0; k < 3; ++k) {                                                                   // q, k, v
+    G.p[6][k] = sk_du(nullptr, sh.nqkv, T, nout[k], nullptr, r, 1.f, nullptr, 3 * r);
+    G.p[7][k] = sk_dB(nullptr, sh.nqkv, T, nout[k], nullptr, 3 * r, 1.f, nullptr, r);
+  }
+  G.n[6] = 3;
+  G.p[7][3] = sk_dA_multi(nullptr, 3 * r, T, r, 3, nullptr, d, d, nil); G.n[7] = 4;
+  return G;
+}
+
+// Floats of the split-K partial buffer: the largest any skinny product or
+// group of them lays out at T tokens (their split factors grow with the
+// contraction over T, so the session's largest T bounds every call), with the
+// floors of skinny_partial_floats (which cover the dequant-GEMM splits too).
 int64_t part_floats(const Shape& sh, int64_t T) {
   const int64_t d = sh.c.hidden, I = sh.c.intermediate, r = sh.c.lora_r;
   const int64_t mx = std::max({T * 3 * r, I * r, (int64_t)sh.qd * r, r * std::max<int64_t>(d, I), 3 * r * d,
                                2 * r * d});
-  return skinny_partial_floats(mx);
+  int64_t need = skinny_partial_floats(mx);
+  const SkGroups G = layer_groups(sh, (int)T);
+  for (int i = 0; i < 8; ++i) need = std::max(need, skinny_group_floats(G.p[i], G.n[i]));
+  return need;
 }
 
 Plan make_plan(const Shape& sh, const RecordLayout& lay, const qls_run_cfg& run, int64_t lora_numel) {
@@ -225,6 +260,7 @@ struct qls_session {
   // boundary of a backward sweep, (n_layers + 1) x T x hidden floats.
   float* cap = nullptr;
   int64_t cap_n = 0;
+  int64_t part_n = 0;       // floats of the split-K partial buffer (part_floats at max_tokens)
   int64_t peak_ws = 0;      // largest workspace a call since the last reset needed
   int64_t wall_khz = 100000;
   // stats
@@ -512,10 +548,16 @@ int bwd_layer(qls_session* S, int l, const uint8_t* rec, const uint16_t* x, floa
   const uint16_t* uqkv = S->at<uint16_t>(S->p.uqkv);
   const uint16_t* ugu = S->at<uint16_t>(S->p.ugu);
 
-  // ---- down projection + SwiGLU (dY = dyb)
-  QLS_RC(skinny_du(dyb, d, T, d, lw + S->wb[QLS_DOWN], r, s, du, r, part, st));
-  QLS_RC(skinny_dB(dyb, d, T, d, S->at<uint16_t>(S->p.udown), r, s, dB(QLS_DOWN), part, st, r));
-  QLS_RC(skinny_dA(du, r, T, r, a, I, I, dA(QLS_DOWN), part, st));
+  const int64_t pf = S->part_n;
+  // ---- down projection + SwiGLU (dY = dyb): du, then dB and dA as one group
+  {
+    const SkinnyProd g1[1] = {sk_du(dyb, d, T, d, lw + S->wb[QLS_DOWN], r, s, du, r)};
+    QLS_RC(skinny_group(g1, 1, part, pf, st));
+    float* const dAd[1] = {dA(QLS_DOWN)};
+    const SkinnyProd g2[2] = {sk_dB(dyb, d, T, d, S->at<uint16_t>(S->p.udown), r, s, dB(QLS_DOWN), r),
+                              sk_dA_multi(du, r, T, r, 1, a, I, I, dAd)};
+    QLS_RC(skinny_group(g2, 2, part, pf, st));
+  }
   LinearDx x1{};
   x1.T = T; x1.Kc = d; x1.Nout = I; x1.dy = dyb; x1.lddy = d;
   x1.codes = w.code[QLS_DOWN]; x1.absmax = w.amax[QLS_DOWN]; x1.ldq = I;
@@ -525,14 +567,19 @@ int bwd_layer(qls_session* S, int l, const uint8_t* rec, const uint16_t* x, floa
   QLS_RC(S->run_dx(x1, st));
   QLS_RC(S->mark(l, PART_DOWN));
 
-  // ---- gate / up
-  for (int k = 0; k < 2; ++k) {
-    const int m = k == 0 ? QLS_GATE : QLS_UP;
-    QLS_RC(skinny_du(dgu + k * I, 2 * I, T, I, lw + S->wb[m], r, s, du + k * r, 2 * r, part, st));
-    QLS_RC(skinny_dB(dgu + k * I, 2 * I, T, I, ugu + k * r, 2 * r, s, dB(m), part, st, r));
+  // ---- gate / up: both du, then both dB and the dA of both (they contract n2: one product)
+  {
+    SkinnyProd g1[2], g2[3];
+    for (int k = 0; k < 2; ++k) {
+      const int m = k == 0 ? QLS_GATE : QLS_UP;
+      g1[k] = sk_du(dgu + k * I, 2 * I, T, I, lw + S->wb[m], r, s, du + k * r, 2 * r);
+      g2[k] = sk_dB(dgu + k * I, 2 * I, T, I, ugu + k * r, 2 * r, s, dB(m), r);
+    }
+    float* const dA_gu[2] = {dA(QLS_GATE), dA(QLS_UP)};
+    g2[2] = sk_dA_multi(du, 2 * r, T, r, 2, n2, d, d, dA_gu);
+    QLS_RC(skinny_group(g1, 2, part, pf, st));
+    QLS_RC(skinny_group(g2, 3, part, pf, st));
   }
-  float* const dA_gu[2] = {dA(QLS_GATE), dA(QLS_UP)};   // both contract n2: one product
-  QLS_RC(skinny_dA_multi(du, 2 * r, T, r, 2, n2, d, d, dA_gu, part, part_floats(sh, S->z.Tm), st));
   LinearDx x2{};
   x2.T = T; x2.Kc = 2 * I; x2.Nout = d; x2.dy = dgu; x2.lddy = 2 * I;
   x2.codes = w.code[QLS_GATE]; x2.absmax = w.amax[QLS_GATE]; x2.ldq = d;
@@ -542,10 +589,15 @@ int bwd_layer(qls_session* S, int l, const uint8_t* rec, const uint16_t* x, floa
   QLS_RC(S->mark(l, PART_GU));
   QLS_RC(rmsnorm_bwd(h, w.nm, sh.c.rms_eps, dn, g, dh, dyb, T, d, st));
 
-  // ---- o projection
-  QLS_RC(skinny_du(dyb, d, T, d, lw + S->wb[QLS_O], r, s, du, r, part, st));
-  QLS_RC(skinny_dB(dyb, d, T, d, S->at<uint16_t>(S->p.uo), r, s, dB(QLS_O), part, st, r));
-  QLS_RC(skinny_dA(du, r, T, r, attn, sh.qd, sh.qd, dA(QLS_O), part, st));
+  // ---- o projection: du, then dB and dA
+  {
+    const SkinnyProd g1[1] = {sk_du(dyb, d, T, d, lw + S->wb[QLS_O], r, s, du, r)};
+    QLS_RC(skinny_group(g1, 1, part, pf, st));
+    float* const dAo[1] = {dA(QLS_O)};
+    const SkinnyProd g2[2] = {sk_dB(dyb, d, T, d, S->at<uint16_t>(S->p.uo), r, s, dB(QLS_O), r),
+                              sk_dA_multi(du, r, T, r, 1, attn, sh.qd, sh.qd, dAo)};
+    QLS_RC(skinny_group(g2, 2, part, pf, st));
+  }
   LinearDx x3{};
   x3.T = T; x3.Kc = d; x3.Nout = sh.qd; x3.dy = dyb; x3.lddy = d;
   x3.codes = w.code[QLS_O]; x3.absmax = w.amax[QLS_O]; x3.ldq = sh.qd;
@@ -568,16 +620,21 @@ int bwd_layer(qls_session* S, int l, const uint8_t* rec, const uint16_t* x, floa
   QLS_RC(rope_bwd(ab.dq, ab.dk, ab.dv, dqkv, sh.nqkv, T, Sq, sh.c.n_heads, sh.c.n_kv_heads, sh.c.head_dim,
                   S->at<float>(S->p.rope), st));
 
-  // ---- q, k, v
-  const int col[3] = {0, sh.qd, sh.qd + sh.kvd};
-  const int nout[3] = {sh.qd, sh.kvd, sh.kvd};
-  for (int k = 0; k < 3; ++k) {
-    const int m = QLS_Q + k;
-    QLS_RC(skinny_du(dqkv + col[k], sh.nqkv, T, nout[k], lw + S->wb[m], r, s, du + k * r, 3 * r, part, st));
-    QLS_RC(skinny_dB(dqkv + col[k], sh.nqkv, T, nout[k], uqkv + k * r, 3 * r, s, dB(m), part, st, r));
+  // ---- q, k, v: the three du, then the three dB and the dA of all three (they contract n1: one product)
+  {
+    const int col[3] = {0, sh.qd, sh.qd + sh.kvd};
+    const int nout[3] = {sh.qd, sh.kvd, sh.kvd};
+    SkinnyProd g1[3], g2[4];
+    for (int k = 0; k < 3; ++k) {
+      const int m = QLS_Q + k;
+      g1[k] = sk_du(dqkv + col[k], sh.nqkv, T, nout[k], lw + S->wb[m], r, s, du + k * r, 3 * r);
+      g2[k] = sk_dB(dqkv + col[k], sh.nqkv, T, nout[k], uqkv + k * r, 3 * r, s, dB(m), r);
+    }
+    float* const dA_qkv[3] = {dA(QLS_Q), dA(QLS_K), dA(QLS_V)};
+    g2[3] = sk_dA_multi(du, 3 * r, T, r, 3, n1, d, d, dA_qkv);
+    QLS_RC(skinny_group(g1, 3, part, pf, st));
+    QLS_RC(skinny_group(g2, 4, part, pf, st));
   }
-  float* const dA_qkv[3] = {dA(QLS_Q), dA(QLS_K), dA(QLS_V)};   // all contract n1: one product
-  QLS_RC(skinny_dA_multi(du, 3 * r, T, r, 3, n1, d, d, dA_qkv, part, part_floats(sh, S->z.Tm), st));
   LinearDx x4{};
   x4.T = T; x4.Kc = sh.nqkv; x4.Nout = d; x4.dy = dqkv; x4.lddy = sh.nqkv;
   x4.codes = w.code[QLS_Q]; x4.absmax = w.amax[QLS_Q]; x4.ldq = d;
@@ -865,6 +922,7 @@ int qls_session_create(const qls_store* st, const qls_run_cfg* run, void* d_ws, 
   S->z = sizes_of(sh, *run);
   const int64_t lora_numel = S->ll.per_layer * sh.c.n_layers;
   S->p = make_plan(sh, S->lay, *run, lora_numel);
+  S->part_n = part_floats(sh, S->z.Tm);
   if (ws_bytes < S->p.total) {
     delete S;
     return fail(QLS_ENOMEM, "workspace of " + std::to_string(ws_bytes) + " bytes is smaller than the " +
