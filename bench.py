@@ -231,6 +231,31 @@ def summarize_trace(d, record_bytes, steps):
     return "\n".join(lines)
 
 
+def summarize_counters(d, kernel_regex):
+    """Average of every counter of a rocprofv3 --pmc run (CSV files under d)
+    per dispatch of the kernels whose name matches kernel_regex."""
+    import csv
+    import glob
+    import re
+    rx = re.compile(kernel_regex)
+    per = {}
+    for f in sorted(glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)):
+        with open(f, newline="") as fh:
+            for r in csv.DictReader(fh):
+                name = r.get("Kernel_Name", "")
+                if not rx.search(name):
+                    continue
+                key = (r.get("Dispatch_Id"), r.get("Counter_Name"))
+                per.setdefault(r.get("Counter_Name"), {}).setdefault(r.get("Dispatch_Id"), 0.0)
+                per[r["Counter_Name"]][r["Dispatch_Id"]] += float(r.get("Counter_Value", 0) or 0)
+    lines = [f"Kernels matching `{kernel_regex}` under {os.path.basename(os.path.normpath(d))}:", "",
+             "| counter | dispatches | average per dispatch |", "|---|---:|---:|"]
+    for c, vals in sorted(per.items()):
+        v = list(vals.values())
+        lines.append(f"| {c} | {len(v)} | {sum(v) / len(v):.1f} |")
+    return "\n".join(lines)
+
+
 class _LazyLayers:
     """Oracle model layers that decode their NF4 codes on every access, as the
     method decodes each streamed layer it uses (store build untimed)."""
@@ -387,6 +412,10 @@ def main():
     ap.add_argument("--summarize-trace", default=None, metavar="DIR",
                     help="only print a markdown summary of the rocprofv3 kernel / memory-copy trace CSVs under DIR")
     ap.add_argument("--trace-steps", type=int, default=1, help="steps the summarised trace covers")
+    ap.add_argument("--summarize-counters", default=None, metavar="DIR",
+                    help="only print the per-dispatch average of every rocprofv3 --pmc counter under DIR for the "
+                         "kernels matching --kernel-regex")
+    ap.add_argument("--kernel-regex", default=r"big_kernel<2, 0>", help="kernel name pattern for --summarize-counters")
     ap.add_argument("--record-bytes", type=int, default=112529408,
                     help="bytes of one layer record in the summarised trace (default: the dq8 8B record)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
@@ -395,6 +424,9 @@ def main():
     args = ap.parse_args()
     if args.summarize_trace:
         print(summarize_trace(args.summarize_trace, args.record_bytes, args.trace_steps))
+        return
+    if args.summarize_counters:
+        print(summarize_counters(args.summarize_counters, args.kernel_regex))
         return
     if args.copy_probe_mib:
         import torch
