@@ -48,14 +48,21 @@ QLS_DEV u32x4 pack8(const f32x4& a, const f32x4& b) {
 
 // ---- Unpadded swizzled tiles, filled by LDS-DMA.
 // A tile is 64 rows x HD bf16 with rows of HD*2 bytes; the 16-byte chunk c of
-// row r sits at chunk c ^ tswz(r).  LDS serves 128 bytes (32 banks) per pass:
-// 8 lanes of a 16-byte read, 16 lanes of an 8-byte read, and a chunk's banks
-// are fixed by its index mod 8.  The key permutes the low three chunk bits so
-// that the 16-byte fragment reads of 8 consecutive rows (one chunk index) and
-// the 8-byte transpose reads of 4 consecutive rows (two adjacent chunks each)
-// cover all 32 banks once.
+// row r sits at chunk c ^ tswz(r).  gfx950's LDS has 64 banks: it serves 256
+// bytes per pass, 16 lanes of a 16-byte read or 32 lanes of an 8-byte read,
+// and a chunk's banks are fixed by its 16-byte granule index mod 16.  The key
+// makes the 16-byte fragment reads of 16 consecutive rows (one chunk index)
+// and the 8-byte transpose reads of 8 consecutive rows (two adjacent chunks
+// each) cover all 64 banks once: over 16 rows it is a bijection onto the 16
+// granules, and within each aligned 8 rows it sends the chunk pairs {2p,
+// 2p+1} to 8 different pairs.  HD = 128 (16 chunks per row):
+// 2 (r mod 8) + bit 3 of r; HD = 64 (8 chunks per 128-byte row, two rows
+// per 256 bytes): 2 ((r / 2) mod 4) + bit 3 of r.
 template <int HD>
-QLS_DEV int tswz(int r) { return (2 * (r & 3)) | ((r >> 2) & 1); }
+QLS_DEV int tswz(int r) {
+  static_assert(HD == 64 || HD == 128, "head_dim 64 or 128");
+  return HD == 128 ? (2 * (r & 7)) | ((r >> 3) & 1) : (2 * ((r >> 1) & 3)) | ((r >> 3) & 1);
+}
 template <int HD>
 QLS_DEV int tpos(int r, int col) { return r * HD + 8 * ((col >> 3) ^ tswz<HD>(r)) + (col & 7); }
 

@@ -76,9 +76,18 @@ template <> struct Stage<B_BF16_NT> { static constexpr int kLoads = 0; };
 template <> struct Stage<B_BF16_NN> { static constexpr int kLoads = 0; };
 
 // Row-major bf16 weight tile [64 k][256 n]: 16-byte chunk c of row r sits at
-// chunk c ^ 2 (r mod 4), so the four rows a 16-lane transposing read covers
-// (two adjacent chunks each) land in eight distinct 16-byte bank groups.
-QLS_DEV int t_pos(int r, int n) { return r * BN + 8 * ((n >> 3) ^ (2 * (r & 3))) + (n & 7); }
+// chunk c ^ 4 (r mod 4), so the four rows a 32-lane transposing read covers
+// (four adjacent chunks each) land in sixteen distinct 16-byte granules, all
+// 64 banks of gfx950's LDS.
+QLS_DEV int t_swz(int r) { return 4 * (r & 3); }
+QLS_DEV int t_pos(int r, int n) { return r * BN + 8 * ((n >> 3) ^ t_swz(r)) + (n & 7); }
+
+// NT weight tile: the thread that loads and decodes 32 codes (half `half` of
+// the k-step) of tile row `row`.  Sixteen consecutive lanes take sixteen
+// consecutive rows, so each 16-byte LDS write of the decode covers 16
+// distinct granules of the 144-byte-pitch rows (9 r mod 16 is a bijection).
+QLS_DEV int nt_row(int t) { return (t & 15) | ((t >> 5) << 4); }
+QLS_DEV int nt_half(int t) { return (t >> 4) & 1; }
 
 // Wait until at most n vector-memory operations are outstanding and every LDS
 // operation is done (gfx9 s_waitcnt encoding: vmcnt bits 3:0 and 15:14,
@@ -135,19 +144,19 @@ struct Big {
       // W rows k (ldb elements apart), columns n0 .. n0 + 255 (N % 256 == 0).
       // DMA: wave w, instruction j fills tile rows 2 (4w + j) and +1 (1 KB);
       // lane l lands in row +l/32, chunk slot l%32, which holds chunk
-      // (l%32) ^ 2 (row mod 4).
+      // (l%32) ^ t_swz(row).
       rb = rsrc(g.Bh + n0, ((int64_t)g.K * g.ldb - n0) * 2);
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int r = 2 * (4 * (t >> 6) + j) + (lane >> 5);
-        vdmb[j] = (uint32_t)((r * g.ldb + 8 * ((lane & 31) ^ (2 * (r & 3)))) * 2);
+        vdmb[j] = (uint32_t)((r * g.ldb + 8 * ((lane & 31) ^ t_swz(r))) * 2);
       }
     } else if constexpr (BL == B_NF4_NT) {
       // W rows n0..: codes row n at n * ldq / 2, absmax at n * ldq / 64.
       rq = rsrc(g.Bq + (int64_t)n0 * g.ldq / 2, (int64_t)(g.N - n0) * g.ldq / 2);
       rs = rsrc(g.Bs + (int64_t)n0 * (g.ldq / 64), (int64_t)(g.N - n0) * (g.ldq / 64) * 4);
-      vq = (uint32_t)((t >> 1) * (g.ldq / 2) + 16 * (t & 1));
-      vs = (uint32_t)((t >> 1) * (g.ldq / 64) * 4);
+      vq = (uint32_t)(nt_row(t) * (g.ldq / 2) + 16 * nt_half(t));
+      vs = (uint32_t)(nt_row(t) * (g.ldq / 64) * 4);
     } else {
       // W columns n0..: element (k, n) at k * ldq + n; 32 groups of 8 columns,
       // 16 groups of 4 contraction rows.
@@ -194,7 +203,7 @@ struct Big {
 
   // Dequantise one register stage into weight stage sB.
   QLS_DEV void store(const Stage<BL>& r, uint16_t* sB) const {
-    const int row = t >> 1, half = t & 1;
+    const int row = nt_row(t), half = nt_half(t);
     if constexpr (BL == B_BF16_NT || BL == B_BF16_NN) {
       (void)r;
       (void)sB;
