@@ -186,14 +186,13 @@ __global__ void __launch_bounds__(512) attn_fwd_k(AttnArgs a) {
         sc[1][j] = mfma16(ka, qf[1][s], sc[1][j]);
       }
     }
+    // Running statistics in the log2 domain of the scaled scores: the
+    // maximum is taken on the raw scores (the scale is positive) and each
+    // probability is exp2(fma(score, scale log2 e, -max)).
     u32x4 pf[2][2];
 #pragma unroll
     for (int qg = 0; qg < 2; ++qg) {
       float mloc = -INFINITY;
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) sc[qg][j][i] *= c;
       // Only the block that holds the diagonal (the last one) has keys to mask;
       // every earlier block lies wholly at or below the workgroup's first row.
       if (k0 + 63 > q0) {
@@ -211,7 +210,7 @@ __global__ void __launch_bounds__(512) attn_fwd_k(AttnArgs a) {
         for (int i = 0; i < 4; ++i) mloc = fmaxf(mloc, sc[qg][j][i]);
       mloc = fmaxf(mloc, __shfl_xor(mloc, 16, 64));
       mloc = fmaxf(mloc, __shfl_xor(mloc, 32, 64));
-      const float m_new = fmaxf(m_run[qg], mloc);
+      const float m_new = fmaxf(m_run[qg], mloc * c);
       const float m_use = m_new == -INFINITY ? 0.f : m_new;
       const float alpha = fexp2(m_run[qg] - m_use);
       float ls = 0.f;
@@ -219,14 +218,19 @@ __global__ void __launch_bounds__(512) attn_fwd_k(AttnArgs a) {
       for (int j = 0; j < 4; ++j)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const float p = fexp2(sc[qg][j][i] - m_use);
+          const float p = fexp2(fmaf(sc[qg][j][i], c, -m_use));
           sc[qg][j][i] = p;
           ls += p;
         }
       l_run[qg] = l_run[qg] * alpha + ls;
-      m_run[qg] = m_new;
+      // alpha is exactly 1 on every row whose maximum did not move; the
+      // rescale of the output accumulators is skipped when that holds for
+      // the whole wave (the usual case once a row has seen a few blocks).
+      if (__builtin_amdgcn_ballot_w64(m_new != m_run[qg])) {
 #pragma unroll
-      for (int i = 0; i < HD / 16; ++i) o[qg][i] *= alpha;
+        for (int i = 0; i < HD / 16; ++i) o[qg][i] *= alpha;
+      }
+      m_run[qg] = m_new;
       pf[qg][0] = pack8(sc[qg][0], sc[qg][1]);
       pf[qg][1] = pack8(sc[qg][2], sc[qg][3]);
     }
