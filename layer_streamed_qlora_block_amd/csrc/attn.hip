@@ -77,6 +77,19 @@ QLS_DEV void dma_tile(uint16_t* tile, const uint16_t* base, int64_t ld, int r0, 
   const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint16_t*>(base + (int64_t)r0 * ld), (short)0,
       (int)(rows * ld * 2 > 0x7fffffffLL ? 0x7fffffffLL : rows * ld * 2), 0x00020000);
+  if (nw == 4) {
+    // Four waves (the 8B shape's 32 / 8 heads, and the dK / dV kernel):
+    // unrolled, wave w issues instructions w, w + 4, ...; the swizzle key of
+    // a lane's row is the same in all of them (the rows are 4 RPI apart, a
+    // multiple of 16), so only the scalar row offset changes.
+    const int r = RPI * wave + lane / CH;
+    const uint32_t v = (uint32_t)((r * ld + 8 * ((lane % CH) ^ tswz<HD>(r))) * 2);
+#pragma unroll
+    for (int u = 0; u < NI / 4; ++u)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)(tile + (wave + 4 * u) * 512),
+                                               16, v, (uint32_t)(4 * RPI * u * ld * 2), 0, 0);
+    return;
+  }
   for (int i = wave; i < NI; i += nw) {
     const int r = RPI * i + lane / CH;
     const int c = (lane % CH) ^ tswz<HD>(r);
@@ -143,7 +156,7 @@ __global__ void __launch_bounds__(512) attn_fwd_k(AttnArgs a) {
   rank_major(&rank, &g);
   const int qb = nqb - 1 - rank;                  // long rows first
   const int b = blockIdx.z;
-  const int t = threadIdx.x, lane = t & 63, w = t >> 6, g4 = lane >> 4, c16 = lane & 15;
+  const int t = threadIdx.x, lane = t & 63, w = __builtin_amdgcn_readfirstlane(t >> 6), g4 = lane >> 4, c16 = lane & 15;
   const int h = g * G + w;
   const int q0 = qb * 32;
   const int64_t tb = (int64_t)b * a.S;
@@ -319,7 +332,7 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))
   rank_major(&rank, &g);
   const int qb = nqb - 1 - rank;                  // long rows first
   const int b = blockIdx.z;
-  const int t = threadIdx.x, lane = t & 63, w = t >> 6, g4 = lane >> 4, c16 = lane & 15;
+  const int t = threadIdx.x, lane = t & 63, w = __builtin_amdgcn_readfirstlane(t >> 6), g4 = lane >> 4, c16 = lane & 15;
   const int h = g * G + w;
   const int q0 = qb * 32;
   const int64_t tb = (int64_t)b * a.S;
@@ -444,7 +457,7 @@ __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2)))
   rank_major(&kb, &h);                            // key block 0 walks the most query blocks
   const int b = blockIdx.z;
   const int g = h / (a.H / a.KV);
-  const int t = threadIdx.x, lane = t & 63, w = t >> 6, g4 = lane >> 4, c16 = lane & 15;
+  const int t = threadIdx.x, lane = t & 63, w = __builtin_amdgcn_readfirstlane(t >> 6), g4 = lane >> 4, c16 = lane & 15;
   const int k0 = kb * BQ;
   const int myk = k0 + 16 * w + c16;
   const int64_t tb = (int64_t)b * a.S;
@@ -454,15 +467,31 @@ __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2)))
   const uint16_t* dO = a.dO + tb * a.lddo + (int64_t)h * HD;
   const int64_t rid0 = ((int64_t)b * a.H + h) * a.S;
 
-  auto stage = [&](uint16_t* sq, uint16_t* so, int st, int q0) {
-    dma_tile<HD>(sq, Q, a.ld, q0, a.S, w, NT / 64, lane);
-    dma_tile<HD>(so, dO, a.lddo, q0, a.S, w, NT / 64, lane);
-    if (t < BQ) {
-      const int q = q0 + t;
-      sL[st][t] = q < a.S ? a.lse[rid0 + q] * kLog2e : 0.f;
-      sD[st][t] = q < a.S ? a.D[rid0 + q] : 0.f;
+  // The LSE and D rows of a query block are loaded into registers one block
+  // ahead (wave 0, one row per lane) and written to LDS when the block is
+  // staged, so no wave waits on their latency.
+  float nl = 0.f, nd = 0.f;
+  auto load_ld = [&](int q0) {
+    const int q = q0 + t;
+    if (t < BQ && q < a.S) {
+      nl = a.lse[rid0 + q];
+      nd = a.D[rid0 + q];
+    } else {
+      nl = 0.f;
+      nd = 0.f;
     }
   };
+  auto stage = [&](uint16_t* sq, uint16_t* so, int st, int q0) {
+    if (t < BQ) {
+      sL[st][t] = nl * kLog2e;
+      sD[st][t] = nd;
+    }
+    load_ld(q0 + BQ);
+    asm volatile("" ::: "memory");
+    dma_tile<HD>(sq, Q, a.ld, q0, a.S, w, NT / 64, lane);
+    dma_tile<HD>(so, dO, a.lddo, q0, a.S, w, NT / 64, lane);
+  };
+  load_ld(k0);
   stage(sQ0, sO0, 0, k0);
 
   u32x4 kf[HD / 32], vf[HD / 32];
@@ -489,6 +518,17 @@ __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2)))
         dp[j] = mfma16(frag<HD>(so, 16 * j + c16, 32 * s + 8 * g4), vf[s], dp[j]);
       }
     }
+    // The fragments of row block j+1 are read while the MFMAs of block j
+    // run, and no further ahead: reading all 32 up front would hold 128
+    // registers and spill.
+    constexpr int NRD = HD / 16;                 // fragment reads per row block
+    __builtin_amdgcn_sched_group_barrier(0x100, NRD, 0);
+#pragma unroll
+    for (int j = 0; j < 3; ++j) {
+      __builtin_amdgcn_sched_group_barrier(0x100, NRD, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, NRD, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, NRD, 0);
     // Scheduling barriers between the phases keep the compiler from hoisting
     // the next phase's LDS reads across them, which raises register pressure.
     __builtin_amdgcn_sched_barrier(0);
@@ -515,6 +555,14 @@ __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2)))
         dv[hb] = mfma16(pf, frag_t<HD>(so, 32 * tt, 16 * hb, g4, c16), dv[hb]);
         dk[hb] = mfma16(dsf, frag_t<HD>(sq, 32 * tt, 16 * hb, g4, c16), dk[hb]);
       }
+      // Transposed fragments (4 reads per column block) two blocks ahead.
+      __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+#pragma unroll
+      for (int hb = 0; hb < HD / 16 - 2; ++hb) {
+        __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
       __builtin_amdgcn_sched_barrier(0);
     }
   };
