@@ -41,6 +41,23 @@ constexpr float kLn2 = 0.6931471805599453f;
 // exp2f would wrap each call in a range-scaling sequence for that case.
 QLS_DEV float fexp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Reductions over the four 16-lane rows of a wave (lanes l, l ^ 16, l ^ 32,
+// l ^ 48) with gfx950's row-swap moves, which stay in the VALU: the 16-lane
+// swap pairs rows 0-1 and 2-3, the 32-lane swap the two halves, and every lane
+// ends with the same value, (r0 op r1) op (r2 op r3).
+QLS_DEV float rows_max(float x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+QLS_DEV float rows_sum(float x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
 QLS_DEV u32x4 pack8(const f32x4& a, const f32x4& b) {
   return u32x4{pack2_bf16(a[0], a[1]), pack2_bf16(a[2], a[3]), pack2_bf16(b[0], b[1]),
                pack2_bf16(b[2], b[3])};
@@ -221,8 +238,7 @@ __global__ void __launch_bounds__(512) attn_fwd_k(AttnArgs a) {
       for (int j = 0; j < 4; ++j)
 #pragma unroll
         for (int i = 0; i < 4; ++i) mloc = fmaxf(mloc, sc[qg][j][i]);
-      mloc = fmaxf(mloc, __shfl_xor(mloc, 16, 64));
-      mloc = fmaxf(mloc, __shfl_xor(mloc, 32, 64));
+      mloc = rows_max(mloc);
       const float m_new = fmaxf(m_run[qg], mloc * c);
       const float m_use = m_new == -INFINITY ? 0.f : m_new;
       const float alpha = fexp2(m_run[qg] - m_use);
@@ -274,8 +290,7 @@ __global__ void __launch_bounds__(512) attn_fwd_k(AttnArgs a) {
   }
 #pragma unroll
   for (int qg = 0; qg < 2; ++qg) {
-    float lt = l_run[qg] + __shfl_xor(l_run[qg], 16, 64);
-    lt += __shfl_xor(lt, 32, 64);
+    const float lt = rows_sum(l_run[qg]);
     if (myq[qg] < a.S) {
       const float inv = 1.f / lt;
       uint16_t* O = a.out + (tb + myq[qg]) * a.ldo + (int64_t)h * HD;
