@@ -31,6 +31,10 @@ constexpr int ATILE = BM * BK;      // bf16 elements of an activation tile (unpa
 constexpr int TILE = BN * PITCH;     // bf16 elements of a weight tile
 constexpr int TP = BN + 4;           // fp32 pitch of the staged epilogue rows
 constexpr int EROWS = 32;            // epilogue rows staged at a time (through weight stage 0)
+#ifndef QLS_LORA_STEPS
+#define QLS_LORA_STEPS 2
+#endif
+constexpr int kLoraSteps = QLS_LORA_STEPS;   // split-K weight of one 64-deep LoRA step
 static_assert(EROWS * TP * 4 <= TILE * 2, "epilogue rows must fit a weight stage");
 
 QLS_DEV __amdgpu_buffer_rsrc_t rsrc(const void* p, int64_t bytes) {
@@ -553,14 +557,24 @@ big_kernel(GemmArgs g, const float* __restrict__ cb) {
   // LoRA term goes into slice 0 only, and each slice writes alpha * acc as a
   // float partial that gemm_reduce_epi sums in slice order.
   const int nk = g.K / BK, ks = g.ksplit > 1 ? g.ksplit : 1, z = blockIdx.z;
+  bool lora = false;
   if constexpr (BL == B_NF4_NT || BL == B_NF4_NN)
-    if (z == 0 && ((BL == B_NF4_NT && g.lora == LORA_FWD) || (BL == B_NF4_NN && g.lora == LORA_DX))) k.lora();
+    lora = (BL == B_NF4_NT && g.lora == LORA_FWD) || (BL == B_NF4_NN && g.lora == LORA_DX);
+  if (z == 0 && lora) k.lora();
   if constexpr (EPI == EPI_CE_STATS || EPI == EPI_CE_GRAD) {
     k.mainloop(0, nk);
     k.template epilogue<EPI>(g.C, g.ldc);
     return;
   }
-  k.mainloop(nk * z / ks, nk * (z + 1) / ks);
+  // Slice 0 also runs the LoRA contraction (staged without prefetch; one
+  // 64-deep step of it takes about kLoraSteps base steps), so slice 0 gets
+  // kLoraSteps fewer base steps and the slices end closer together.  The
+  // boundaries depend on the shape and split only, not on whether the LoRA
+  // term runs: with the adapters disabled the base product is summed in the
+  // same order as with B = 0, and the two outputs are identical.
+  const int lu = ks > 1 ? kLoraSteps : 0;
+  const int U = nk + lu;
+  k.mainloop(z == 0 ? 0 : U * z / ks - lu, U * (z + 1) / ks - lu);
   if (ks > 1)
     k.template epilogue<EPI_F32>(g.partial + (int64_t)z * g.M * g.N, g.N);
   else
