@@ -568,11 +568,12 @@ big_kernel(GemmArgs g, const float* __restrict__ cb) {
   }
   // Slice 0 also runs the LoRA contraction (staged without prefetch; one
   // 64-deep step of it takes about kLoraSteps base steps), so slice 0 gets
-  // kLoraSteps fewer base steps and the slices end closer together.  The
-  // boundaries depend on the shape and split only, not on whether the LoRA
-  // term runs: with the adapters disabled the base product is summed in the
-  // same order as with B = 0, and the two outputs are identical.
-  const int lu = ks > 1 ? kLoraSteps : 0;
+  // kLoraSteps fewer base steps and the slices end closer together (when
+  // every slice keeps at least 4 steps).  The boundaries depend on the shape
+  // and split only, not on whether the LoRA term runs: with the adapters
+  // disabled the base product is summed in the same order as with B = 0, and
+  // the two outputs are identical.
+  const int lu = ks > 1 && nk >= 4 * ks ? kLoraSteps : 0;
   const int U = nk + lu;
   k.mainloop(z == 0 ? 0 : U * z / ks - lu, U * (z + 1) / ks - lu);
   if (ks > 1)
