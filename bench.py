@@ -239,20 +239,25 @@ def summarize_counters(d, kernel_regex):
     import re
     rx = re.compile(kernel_regex)
     per = {}
+    dur = {}                                       # dispatch -> ns, from the rows' timestamps
     for f in sorted(glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)):
         with open(f, newline="") as fh:
             for r in csv.DictReader(fh):
                 name = r.get("Kernel_Name", "")
                 if not rx.search(name):
                     continue
-                key = (r.get("Dispatch_Id"), r.get("Counter_Name"))
                 per.setdefault(r.get("Counter_Name"), {}).setdefault(r.get("Dispatch_Id"), 0.0)
                 per[r["Counter_Name"]][r["Dispatch_Id"]] += float(r.get("Counter_Value", 0) or 0)
+                if r.get("Start_Timestamp") and r.get("End_Timestamp"):
+                    dur[r["Dispatch_Id"]] = int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
     lines = [f"Kernels matching `{kernel_regex}` under {os.path.basename(os.path.normpath(d))}:", "",
              "| counter | dispatches | average per dispatch |", "|---|---:|---:|"]
     for c, vals in sorted(per.items()):
         v = list(vals.values())
         lines.append(f"| {c} | {len(v)} | {sum(v) / len(v):.1f} |")
+    if dur:
+        lines.append(f"| duration (us, from the dispatch timestamps) | {len(dur)} | "
+                     f"{sum(dur.values()) / len(dur) / 1e3:.1f} |")
     return "\n".join(lines)
 
 
