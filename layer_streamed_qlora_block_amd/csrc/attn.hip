@@ -203,8 +203,8 @@ __global__ void __launch_bounds__(512) attn_fwd_k(AttnArgs a) {
   float m_run[2] = {-INFINITY, -INFINITY}, l_run[2] = {0.f, 0.f};
   const float c = a.scale * kLog2e;
 
-  // S^T of one key block into sc: 32 MFMAs over the 16 K fragments of the tile.
-  auto scores = [&](const uint16_t* sK, f32x4 (&sc)[2][4]) {
+  auto block = [&](const uint16_t* sK, const uint16_t* sV, int k0) {
+    f32x4 sc[2][4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       sc[0][j] = f32x4{0, 0, 0, 0};
@@ -216,17 +216,10 @@ __global__ void __launch_bounds__(512) attn_fwd_k(AttnArgs a) {
         sc[1][j] = mfma16(ka, qf[1][s], sc[1][j]);
       }
     }
-  };
-  // One key block, software-pipelined: the softmax of this block's scores
-  // (sc, computed one step earlier) runs interleaved with the score MFMAs of
-  // the next block (into sn, from its K tile sKn), then P V accumulates with
-  // this block's V tile.  The last block's "next" scores read a stale tile
-  // and are never used.
-  auto step = [&](const uint16_t* sKn, const uint16_t* sV, f32x4 (&sc)[2][4], f32x4 (&sn)[2][4], int k0) {
     // Running statistics in the log2 domain of the scaled scores: the
     // maximum is taken on the raw scores (the scale is positive) and each
     // probability is exp2(fma(score, scale log2 e, -max)).
-    float m_new[2], m_use[2];
+    u32x4 pf[2][2];
 #pragma unroll
     for (int qg = 0; qg < 2; ++qg) {
       float mloc = -INFINITY;
@@ -246,49 +239,27 @@ __global__ void __launch_bounds__(512) attn_fwd_k(AttnArgs a) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) mloc = fmaxf(mloc, sc[qg][j][i]);
       mloc = rows_max(mloc);
-      m_new[qg] = fmaxf(m_run[qg], mloc * c);
-      m_use[qg] = m_new[qg] == -INFINITY ? 0.f : m_new[qg];
-    }
-    __builtin_amdgcn_sched_barrier(0);
-    scores(sKn, sn);
-    float ls[2] = {0.f, 0.f};
-#pragma unroll
-    for (int qg = 0; qg < 2; ++qg)
+      const float m_new = fmaxf(m_run[qg], mloc * c);
+      const float m_use = m_new == -INFINITY ? 0.f : m_new;
+      const float alpha = fexp2(m_run[qg] - m_use);
+      float ls = 0.f;
 #pragma unroll
       for (int j = 0; j < 4; ++j)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const float p = fexp2(fmaf(sc[qg][j][i], c, -m_use[qg]));
+          const float p = fexp2(fmaf(sc[qg][j][i], c, -m_use));
           sc[qg][j][i] = p;
-          ls[qg] += p;
+          ls += p;
         }
-    // Interleave: the K fragments of a row block one block ahead, each MFMA
-    // followed by three of the exponentials' VALU operations.
-    constexpr int NRD = HD / 32;                 // K fragment reads per row block
-    __builtin_amdgcn_sched_group_barrier(0x100, NRD, 0);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      if (j < 3) __builtin_amdgcn_sched_group_barrier(0x100, NRD, 0);
-#pragma unroll
-      for (int m = 0; m < 2 * NRD; ++m) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
-      }
-    }
-    __builtin_amdgcn_sched_barrier(0);
-    u32x4 pf[2][2];
-#pragma unroll
-    for (int qg = 0; qg < 2; ++qg) {
-      const float alpha = fexp2(m_run[qg] - m_use[qg]);
-      l_run[qg] = l_run[qg] * alpha + ls[qg];
+      l_run[qg] = l_run[qg] * alpha + ls;
       // alpha is exactly 1 on every row whose maximum did not move; the
       // rescale of the output accumulators is skipped when that holds for
       // the whole wave (the usual case once a row has seen a few blocks).
-      if (__builtin_amdgcn_ballot_w64(m_new[qg] != m_run[qg])) {
+      if (__builtin_amdgcn_ballot_w64(m_new != m_run[qg])) {
 #pragma unroll
         for (int i = 0; i < HD / 16; ++i) o[qg][i] *= alpha;
       }
-      m_run[qg] = m_new[qg];
+      m_run[qg] = m_new;
       pf[qg][0] = pack8(sc[qg][0], sc[qg][1]);
       pf[qg][1] = pack8(sc[qg][2], sc[qg][3]);
     }
@@ -302,24 +273,20 @@ __global__ void __launch_bounds__(512) attn_fwd_k(AttnArgs a) {
       }
   };
 
-  // Stage s holds K and V tiles; block kb's V is in stage kb mod 2 and its
-  // scores were formed one step earlier from the K tile there.  After the
-  // barrier of block kb, K of block kb + 2 goes where K of block kb was and V
-  // of block kb + 1 where V of block kb - 1 was (both read before it).
-  if (nkb > 1) dma_tile<HD>(sK1, K, a.ld, 64, a.S, w, G, lane);
-  f32x4 sa[2][4], sb[2][4];
-  wait_dma();
-  scores(sK0, sa);
   for (int kb = 0; kb < nkb; kb += 2) {
-    wait_dma();
-    if (kb + 2 < nkb) dma_tile<HD>(sK0, K, a.ld, 64 * (kb + 2), a.S, w, G, lane);
-    if (kb + 1 < nkb) dma_tile<HD>(sV1, V, a.ld, 64 * (kb + 1), a.S, w, G, lane);
-    step(sK1, sV0, sa, sb, 64 * kb);
+    wait_dma();                                       // block kb in stage 0; stage 1 free
+    if (kb + 1 < nkb) {
+      dma_tile<HD>(sK1, K, a.ld, 64 * (kb + 1), a.S, w, G, lane);
+      dma_tile<HD>(sV1, V, a.ld, 64 * (kb + 1), a.S, w, G, lane);
+    }
+    block(sK0, sV0, 64 * kb);
     if (kb + 1 >= nkb) break;
-    wait_dma();
-    if (kb + 3 < nkb) dma_tile<HD>(sK1, K, a.ld, 64 * (kb + 3), a.S, w, G, lane);
-    if (kb + 2 < nkb) dma_tile<HD>(sV0, V, a.ld, 64 * (kb + 2), a.S, w, G, lane);
-    step(sK0, sV1, sb, sa, 64 * (kb + 1));
+    wait_dma();                                       // block kb+1 in stage 1; stage 0 free
+    if (kb + 2 < nkb) {
+      dma_tile<HD>(sK0, K, a.ld, 64 * (kb + 2), a.S, w, G, lane);
+      dma_tile<HD>(sV0, V, a.ld, 64 * (kb + 2), a.S, w, G, lane);
+    }
+    block(sK1, sV1, 64 * (kb + 1));
   }
 #pragma unroll
   for (int qg = 0; qg < 2; ++qg) {
