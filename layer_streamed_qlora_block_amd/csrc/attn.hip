@@ -65,16 +65,18 @@ QLS_DEV u32x4 pack8(const f32x4& a, const f32x4& b) {
 
 // ---- Unpadded swizzled tiles, filled by LDS-DMA.
 // A tile is 64 rows x HD bf16 with rows of HD*2 bytes; the 16-byte chunk c of
-// row r sits at chunk c ^ tswz(r).  gfx950's LDS has 64 banks: it serves 256
-// bytes per pass, 16 lanes of a 16-byte read or 32 lanes of an 8-byte read,
-// and a chunk's banks are fixed by its 16-byte granule index mod 16.  The key
-// makes the 16-byte fragment reads of 16 consecutive rows (one chunk index)
-// and the 8-byte transpose reads of 8 consecutive rows (two adjacent chunks
-// each) cover all 64 banks once: over 16 rows it is a bijection onto the 16
-// granules, and within each aligned 8 rows it sends the chunk pairs {2p,
-// 2p+1} to 8 different pairs.  HD = 128 (16 chunks per row):
-// 2 (r mod 8) + bit 3 of r; HD = 64 (8 chunks per 128-byte row, two rows
-// per 256 bytes): 2 ((r / 2) mod 4) + bit 3 of r.
+// row r sits at chunk c ^ tswz(r).  gfx950's LDS has 64 banks, and a chunk's
+// banks are fixed by its 16-byte granule index mod 16.  Measured: a 16-byte
+// read runs at full rate when lanes 0-15 (and 32-47) cover 16 distinct
+// granules and lane l + 16 hits the granule of lane l; the MFMA fragment
+// reads here give lanes l and l + 16 adjacent chunks of one row, which no key
+// can align, so they run at half rate whatever the key.  The key makes the 16
+// rows read by each 16-lane group (one chunk index) distinct granules, which
+// removed a further 2-way conflict: over 16 rows it is a bijection onto the
+// 16 granules, and within each aligned 8 rows it sends the chunk pairs {2p,
+// 2p+1} of the transposing reads to 8 different pairs.  HD = 128 (16 chunks
+// per row): 2 (r mod 8) + bit 3 of r; HD = 64 (8 chunks per 128-byte row, two
+// rows per 256 bytes): 2 ((r / 2) mod 4) + bit 3 of r.
 template <int HD>
 QLS_DEV int tswz(int r) {
   static_assert(HD == 64 || HD == 128, "head_dim 64 or 128");
