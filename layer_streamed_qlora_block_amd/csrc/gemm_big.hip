@@ -57,9 +57,13 @@ QLS_DEV int a_pos(int r, int k) { return r * BK + 8 * ((k >> 3) ^ a_swz(r)) + (k
 
 // NN B tile: each thread dequantises 4 contraction rows x 8 columns.  Column
 // group cg (8 columns) and row quad kq of thread t are interleaved so that a
-// half-wave covers 8 column groups x 4 row quads, and the 16-byte chunks of
-// each LDS row are XOR-swizzled by (row / 16) so that both the transposing
-// 8-byte writes and the 16-byte fragment reads are free of bank conflicts.
+// half-wave covers 8 column groups x 4 row quads (so a wave's code loads are
+// 4 rows x 64 bytes), and the 16-byte chunks of each LDS row are XOR-swizzled
+// by (row / 16), which spreads the transposing 8-byte writes.  Measured on
+// gfx950 the writes run at about 3/4 of the conflict-free rate and the 16-byte
+// fragment reads at half rate (lanes l and l + 16 of a read take the two
+// halves of the same four banks, and here they fall on different granules);
+// layouts that fix both need a thread mapping whose code loads cost more.
 QLS_DEV int nn_cg(int t) { return (t & 7) | (((t >> 5) & 3) << 3); }
 QLS_DEV int nn_kq(int t) { return ((t >> 3) & 3) | ((t >> 7) << 2); }
 QLS_DEV int nn_swz(int n) { return 2 * ((n >> 4) & 3); }
